@@ -64,19 +64,27 @@ def indexer_logits(q, k, w, limit=None, q_scale=None, k_scale=None, dtype="bf16"
     """
     B, T, H, D = q.shape
     K = k.shape[1]
-    q_hat = dequant_q(q, q_scale, dtype)
-    k_hat = dequant_k(k, k_scale, dtype)
     w64 = np.asarray(w, dtype=np.float64)
     out = np.full((B, T, K), np.nan, dtype=np.float32)
     todo = rows if rows is not None else [(b, t) for b in range(B) for t in range(T)]
+    by_seq = {}
     for b, t in todo:
-        lim = K - 1 if limit is None else int(limit[b, t])
-        n = max(0, min(lim + 1, K))
-        row = np.full(K, -np.inf, dtype=np.float64)
-        if n:
-            dots = q_hat[b, t] @ k_hat[b, :n].T            # [H, n]
-            row[:n] = np.sum(w64[b, t][:, None] * np.maximum(dots, 0.0), axis=0)
-        out[b, t] = row.astype(np.float32)
+        by_seq.setdefault(int(b), []).append(int(t))
+    for b, ts in by_seq.items():
+        # dequantize only this sequence (and only up to its furthest valid key)
+        lims = [K - 1 if limit is None else int(limit[b, t]) for t in ts]
+        n_max = max(0, min(max(lims) + 1, K))
+        k_hat = dequant_k(k[b: b + 1, :n_max], None if k_scale is None else k_scale[b: b + 1, :n_max],
+                          dtype)[0]
+        for t, lim in zip(ts, lims):
+            n = max(0, min(lim + 1, K))
+            q_hat = dequant_q(q[b: b + 1, t: t + 1],
+                              None if q_scale is None else q_scale[b: b + 1, t: t + 1], dtype)[0, 0]
+            row = np.full(K, -np.inf, dtype=np.float64)
+            if n:
+                dots = q_hat @ k_hat[:n].T                   # [H, n]
+                row[:n] = np.sum(w64[b, t][:, None] * np.maximum(dots, 0.0), axis=0)
+            out[b, t] = row.astype(np.float32)
     return out
 
 
