@@ -1,0 +1,236 @@
+"""Benchmark of the DSA indexer hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+    xk_indexer_logits -> xk_indexer_topk -> xk_mxfp4_paged_gather
+Prints ONE JSON line. `value` is the indexer-logits throughput of the whole
+step (algorithmic logits FLOPs / step wall time), `topk_gather_GBps` the
+algorithmic bytes of top-k + gather over their kernel time; `stages` has every
+kernel's average duration (HIP events on the launch stream over the timed
+steps) against its roof, and `roofline` repeats the dominant kernel.
+
+Inputs are resident in HBM before timing starts. Several identical copies of
+q/k/w are rotated across steps so that a decode-sized working set cannot be
+served from the 256 MB last-level cache instead of HBM.
+
+    python bench.py [--steps K] [--warmup W] [--config flash_decode]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer logits TFLOP/s & top-k+mxfp4 gather GB/s, % of MI355X roofline"
+PEAK = {"hbm": 8000.0, "mfma_bf16": 2500.0, "mfma_fp8": 5000.0}   # GB/s, TFLOP/s (dense)
+FLOP_PER_PAIR = 2 * 64 * 128
+DEFAULT_CONFIG = "flash_decode"
+
+
+def algorithmic_work(x, sel_pos=None):
+    """Per-step algorithmic FLOPs and bytes of each stage (what the method must move)."""
+    cfg = x["cfg"]
+    eb = 2 if cfg.dtype == "bf16" else 1
+    lim = x["limit"].astype(np.int64)
+    n_valid = np.clip(lim + 1, 0, cfg.K)                      # [B,T]
+    pairs = int(n_valid.sum())
+    keys_read = int(n_valid.max(axis=1).sum())                # distinct valid key rows
+    logits_bytes = (keys_read * 128 * eb + cfg.rows * 64 * 128 * eb + cfg.rows * 64 * 4
+                    + pairs * 4)
+    if cfg.dtype == "fp8":
+        logits_bytes += cfg.rows * 64 * 4 + keys_read * 4      # q and k scales
+    topk_bytes = pairs * 4 + cfg.rows * cfg.topk * 4
+    slots = cfg.rows * cfg.topk
+    distinct = slots
+    if sel_pos is not None:
+        seq = np.repeat(x["row_seq"].astype(np.int64), cfg.topk)
+        p = sel_pos.reshape(-1).astype(np.int64)
+        ok = p >= 0
+        distinct = int(np.unique(seq[ok] * (1 << 32) + p[ok]).size)
+    gather_bytes = slots * (256 + 4) + distinct * 68
+    return {"pairs": pairs, "logits_flops": pairs * FLOP_PER_PAIR, "logits_bytes": logits_bytes,
+            "topk_bytes": topk_bytes, "gather_bytes": gather_bytes, "distinct_rows": distinct}
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "sparse_attention_indexer_logits_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config, kernel_stage):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.txt")
+    if not os.path.exists(path):
+        return None
+    src, vals = None, {}
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("kernel_source_sha:"):
+            src = line.split(":", 1)[1].strip()
+        elif line.startswith("traffic_bytes_per_launch"):
+            _, stage, v = line.split()
+            vals[stage] = float(v)
+    if src != source_hash():
+        return None
+    return vals.get(kernel_stage)
+
+
+def cpu_baseline(x, work, budget_s):
+    """The oracle as it stands, on a bounded sample of the step's query rows."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    cfg = x["cfg"]
+    R = cfg.rows
+    order = np.random.default_rng(0).permutation(R)
+
+    def run(n):
+        rows = np.sort(order[:n])
+        pairs = [(int(r) // cfg.T, int(r) % cfg.T) for r in rows]
+        t0 = time.perf_counter()
+        L = oracle.indexer_logits(x["q"], x["k"], x["w"], x["limit"], x["q_scale"],
+                                  x["k_scale"], cfg.dtype, rows=pairs).reshape(R, cfg.K)
+        idx = oracle.indexer_topk(L, x["limit"].reshape(-1), cfg.topk, rows=rows)
+        oracle.mxfp4_paged_gather(x["kv_fp4"], x["kv_scale"], x["block_table"], idx,
+                                  x["row_seq"], x["block_size"], rows=rows)
+        return time.perf_counter() - t0, rows
+
+    t1, _ = run(1)
+    n = int(min(R, max(1, budget_s / max(t1, 1e-6))))
+    tn, rows = run(n)
+    frac = float(np.clip(x["limit"].reshape(-1)[rows] + 1, 0, cfg.K).sum()) / max(work["pairs"], 1)
+    step_s = tn / max(frac, 1e-12)              # scale by the share of the step's pairs done
+    return {"value": work["logits_flops"] / step_s / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{n} of {R} query rows (logits + top-k + gather, float64 numpy), "
+                      f"{tn:.1f} s, scaled by their share of the step's valid pairs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--sets", type=int, default=0, help="input copies rotated across steps (0=auto)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the indexer path here "
+              "is built and timed on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import sparse_attention_indexer_logits_amd as xk
+    from sparse_attention_indexer_logits_amd.pipeline import IndexerStep
+
+    x = workloads.inputs(args.config)
+    cfg = x["cfg"]
+    d = workloads.to_device(x)
+    in_bytes = sum(t.numel() * t.element_size() for key, t in d.items()
+                   if key in ("q", "k", "w") and t is not None)
+    n_sets = args.sets or int(min(16, max(1, -(-512 * 2 ** 20 // in_bytes))))
+    base = IndexerStep(d["q"], d["k"], d["w"], d["limit"], cfg.topk, d["kv_fp4"], d["kv_scale"],
+                       d["block_table"], d["row_seq"], d["q_scale"], d["k_scale"])
+    steps = [base]
+    for _ in range(n_sets - 1):
+        s = IndexerStep(d["q"].clone(), d["k"].clone(), d["w"].clone(), d["limit"], cfg.topk,
+                        d["kv_fp4"], d["kv_scale"], d["block_table"], d["row_seq"],
+                        d["q_scale"], d["k_scale"])
+        s.logits, s.idx, s.gathered = base.logits, base.idx, base.gathered   # shared outputs
+        steps.append(s)
+
+    # one checked pass: top-k indices must be valid positions before the gather reads them
+    base.run_logits()
+    base.run_topk()
+    torch.cuda.synchronize()
+    sel = base.idx.cpu().numpy()
+    lens = x["seq_len"][x["row_seq"]]
+    if not (np.all(sel >= -1) and np.all(sel < lens[:, None])):
+        raise RuntimeError("top-k produced out-of-range indices; not running the gather")
+    base.run_gather()
+    torch.cuda.synchronize()
+    work = algorithmic_work(x, sel)
+
+    for i in range(args.warmup):
+        steps[i % n_sets]()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s = steps[i % n_sets]
+        e = ev[i]
+        e[0].record()
+        s.run_logits()
+        e[1].record()
+        s.run_topk()
+        e[2].record()
+        s.run_gather()
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ms = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+          for j, name in enumerate(("logits", "topk", "gather"))}
+
+    prefill = cfg.T >= 8
+    mfma_peak = PEAK["mfma_fp8" if cfg.dtype == "fp8" else "mfma_bf16"]
+    stages = {}
+    for name in ("logits", "topk", "gather"):
+        sec = ms[name] / 1e3
+        if name == "logits" and prefill:
+            ach = work["logits_flops"] / sec / 1e12
+            stages[name] = {"bound": "mfma", "us": ms[name] * 1e3, "achieved": ach,
+                            "peak": mfma_peak, "unit": "TFLOP/s", "frac": ach / mfma_peak,
+                            "frac_of_bf16_peak": ach / PEAK["mfma_bf16"]}
+        else:
+            nbytes = work[f"{name}_bytes"]
+            ach = nbytes / sec / 1e9
+            stages[name] = {"bound": "hbm", "us": ms[name] * 1e3, "achieved": ach,
+                            "peak": PEAK["hbm"], "unit": "GB/s", "frac": ach / PEAK["hbm"],
+                            "bytes": nbytes}
+    dom = max(stages, key=lambda s: stages[s]["us"])
+    roof = {k: stages[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roof["kernel"] = dom
+    roof["traffic"] = measured_traffic(args.config, dom)
+
+    tg_bytes = work["topk_bytes"] + work["gather_bytes"]
+    tg_gbps = tg_bytes / ((ms["topk"] + ms["gather"]) / 1e3) / 1e9
+    value = work["logits_flops"] / (ms_step / 1e3) / 1e12
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic: seeded numpy PCG64 inputs with the DeepSeek-V4 indexer shapes",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "K": cfg.K, "H": 64, "D": 128,
+                   "topk": cfg.topk, "qk_dtype": cfg.dtype, "limit": "causal"
+                   if cfg.causal_offset is not None else "per-sequence length",
+                   "cache": "mxfp4 E2M1+E8M0, block 64", "input_copies_rotated": n_sets},
+        "topk_gather_GBps": tg_gbps, "topk_gather_frac_hbm": tg_gbps / PEAK["hbm"],
+        "logits_kernel_TFLOPs": work["logits_flops"] / (ms["logits"] / 1e3) / 1e12,
+        "stages": stages, "roofline": roof, "work": work,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x, work, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

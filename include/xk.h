@@ -1,0 +1,155 @@
+/*
+ * xk.h -- C ABI of the MI355X (gfx950) DeepSeek-V4 DSA indexer hot path.
+ *
+ * Three operations, each asynchronous on the caller's HIP stream:
+ *   xk_indexer_logits      weighted-ReLU MQA score over all keys (bf16 or OCP fp8)
+ *   xk_indexer_topk        deterministic per-query top-k of those scores
+ *   xk_mxfp4_paged_gather  mxfp4 paged KV rows of the selected keys, decoded to bf16
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers (hipMalloc / torch CUDA tensors) unless
+ *     stated otherwise; every buffer is dense row-major with the shape given.
+ *     The caller owns all memory; the library allocates nothing and keeps no
+ *     state between calls (apart from a per-device "is this gfx950" cache),
+ *     so calls on different streams or threads are independent.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). A
+ *     call only enqueues kernels: outputs are valid once the stream reaches
+ *     them, and inputs must stay untouched until then. Nothing synchronises.
+ *   - Element offsets are computed in 64 bits (paged-MQA kernels on the pages
+ *     needed 64-bit offsets once a KV buffer passed 4 GiB).
+ *   - Errors: every argument is checked on the host BEFORE any HIP call; a
+ *     bad argument returns XK_ERR_INVALID_ARGUMENT, a shape or device outside
+ *     what the kernels implement returns XK_ERR_UNSUPPORTED, and a failed
+ *     launch returns XK_ERR_HIP. On error nothing is enqueued (except
+ *     XK_ERR_HIP, where the launch was attempted). xk_last_error() gives a
+ *     thread-local one-line reason. No call aborts the process.
+ *   - Preconditions NOT checked on the device (violating them is undefined):
+ *     buffers do not alias, scales are finite and > 0, scores are not NaN,
+ *     sel_pos entries >= 0 index a token the sequence has, and the block-table
+ *     entries they reach lie in [0, NB).
+ */
+#ifndef XK_H_
+#define XK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  XK_OK = 0,
+  XK_ERR_INVALID_ARGUMENT = 1,
+  XK_ERR_UNSUPPORTED = 2,
+  XK_ERR_HIP = 3
+} xk_status;
+
+typedef enum {
+  XK_BF16 = 0,          /* q, k are bfloat16; no scales                        */
+  XK_FP8_E4M3_OCP = 1   /* q, k are OCP e4m3fn bytes with fp32 dequant scales  */
+} xk_qk_dtype;
+
+/*
+ * Indexer logits.
+ *
+ * Defines (page "xkernels #27 -- [AMD/MI300A] DeepSeek-V4 DSA indexer +
+ * attention", comment announcing dsa_indexer_logits):
+ *   logits[b,t,j] = sum_{h<H} w[b,t,h] * relu( q[b,t,h,:] . k[b,j,:] )
+ * for j <= limit[b,t], and exactly -inf for limit[b,t] < j < K; one shared
+ * (MQA) key per position, per-head weights, an optional causal limit,
+ * fp32 logits out. With XK_FP8_E4M3_OCP the operands are the dequantized
+ * values q = e4m3(q8[b,t,h,:]) * q_scale[b,t,h] and
+ * k = e4m3(k8[b,j,:]) * k_scale[b,j] (the fp8 packing of the upstream kernel
+ * is an encoding of the same math). No other constant enters the score.
+ *
+ *   q        [B,T,H,D]  bf16, or e4m3 bytes          (16-byte aligned)
+ *   q_scale  [B,T,H]    fp32, fp8 only; NULL for bf16
+ *   k        [B,K,D]    bf16, or e4m3 bytes          (16-byte aligned)
+ *   k_scale  [B,K]      fp32, fp8 only; NULL for bf16
+ *   w        [B,T,H]    fp32 head weights
+ *   limit    [B,T]      int32 inclusive last valid key of each query, or NULL
+ *                       (every key valid); values < 0 give an all -inf row,
+ *                       values >= K are clamped to K-1
+ *   logits   [B,T,K]    fp32 output; every element is written
+ *   B, T, K >= 1; H must be 64 and D 128 (the DeepSeek-V4 indexer:
+ *   index_n_heads 64, index_head_dim 128), else XK_ERR_UNSUPPORTED.
+ * Accumulation is fp32 (MFMA); results match a float64 evaluation to
+ * ~1e-6 of max|logit|.
+ */
+xk_status xk_indexer_logits(const void* q, const float* q_scale,
+                            const void* k, const float* k_scale,
+                            const float* w, const int32_t* limit, float* logits,
+                            int B, int T, int K, int H, int D,
+                            int dtype, void* stream);
+
+/*
+ * Bytes of device workspace xk_indexer_topk needs for these sizes (may be 0).
+ * Pure host function; returns 0 for sizes xk_indexer_topk would reject.
+ */
+size_t xk_indexer_topk_workspace_size(int R, int K, int k);
+
+/*
+ * Per-row top-k.
+ *
+ * Defines (page "xkernels #28 -- DeepSeek-V4 serving support": the DSA
+ * indexer keeps the top-512 (Flash) / top-1024 (Pro) keys per query; page
+ * "DeepSeek V4 Flash on a single AMD MI300X": a deterministic sparse top-k
+ * with a tie-break and a canonical order of the selected indices):
+ * for row r with n = clamp(limit[r]+1, 0, K) valid keys, idx[r,:] holds the
+ * min(k, n) indices j < n with the largest logits[r,j], ordered by
+ * (score descending, then lower j), -0.0 equal to +0.0, followed by -1 up to
+ * k. The result is unique, so it is bit-reproducible.
+ *
+ *   logits     [R,K] fp32 (e.g. xk_indexer_logits output with R = B*T)
+ *   limit      [R]   int32 inclusive last valid key, or NULL (n = K)
+ *   idx        [R,k] int32 output; every element is written
+ *   1 <= k <= 2048 and 1 <= K <= 98304 (rows are held on chip), else
+ *   XK_ERR_UNSUPPORTED.
+ *   workspace  device buffer of xk_indexer_topk_workspace_size(R,K,k) bytes
+ *              (may be NULL when that size is 0)
+ */
+xk_status xk_indexer_topk(const float* logits, const int32_t* limit, int32_t* idx,
+                          int R, int K, int k,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mxfp4 paged KV gather.
+ *
+ * Defines (page "xkernels #28 -- DeepSeek-V4 serving support", comment
+ * shipping mxfp4_paged_gather): for each row r and top-k slot s with
+ * p = sel_pos[r,s]:
+ *   p < 0  -> out[r,s,:] = 128 x +0.0 (padded slot)
+ *   else   -> blk = block_table[row_seq[r], p / bs], off = p % bs and
+ *             out[r,s,d] = bf16( E2M1(nibble d) * E8M0(scale byte d/32) )
+ * with E8M0(b) = 2^(b-127) and E8M0(0xFF) = 0 (so the product is a signed
+ * zero). Every product is exact in bf16 or overflows to +-inf (only for
+ * scale bytes >= 253), so the output is bit-exact.
+ *
+ *   kv_fp4      [NB,bs,D/2] u8  element 2i in the low nibble, 2i+1 in the high
+ *   kv_scale    [NB,bs,D/32] u8 E8M0 byte of group g = elements [32g, 32g+32)
+ *   block_table [S,MB] int32    physical block of each logical block
+ *   sel_pos     [R,k] int32     token positions (e.g. xk_indexer_topk output)
+ *   row_seq     [R] int32       sequence of each row, or NULL (row r -> seq r,
+ *                               requires R <= S)
+ *   out         [R,k,D] bf16 bits (uint16), every element written
+ *   bs must be a power of two, D must be 128, else XK_ERR_UNSUPPORTED;
+ *   kv_fp4 must be 4-byte aligned and out 16-byte aligned.
+ */
+xk_status xk_mxfp4_paged_gather(const uint8_t* kv_fp4, const uint8_t* kv_scale,
+                                const int32_t* block_table, const int32_t* sel_pos,
+                                const int32_t* row_seq, uint16_t* out,
+                                int R, int k, int S, int MB, int NB, int bs, int D,
+                                void* stream);
+
+/* Static name of a status code. */
+const char* xk_status_string(xk_status status);
+
+/* Thread-local detail of the last non-OK return on this thread ("" if none). */
+const char* xk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XK_H_ */

@@ -1,0 +1,184 @@
+"""Python binding of libxk, the MI355X (gfx950) DeepSeek-V4 DSA indexer path.
+
+Thin ctypes marshalling over the C ABI declared in include/xk.h: each
+function takes torch tensors, checks device/dtype/contiguity/shape, and calls
+the C entry point of the same name on the current HIP stream. Every step of
+the path runs in the HIP kernels of libxk.so; there is no other code path, and
+importing this package fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libxk.so")
+
+XK_OK, XK_ERR_INVALID_ARGUMENT, XK_ERR_UNSUPPORTED, XK_ERR_HIP = 0, 1, 2, 3
+XK_BF16, XK_FP8_E4M3_OCP = 0, 1
+
+EXPORTED = ("xk_indexer_logits", "xk_indexer_topk_workspace_size", "xk_indexer_topk",
+            "xk_mxfp4_paged_gather", "xk_status_string", "xk_last_error")
+
+
+class XKError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_lib.xk_status_string(status).decode()}: {detail}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run "
+                          "`python sparse_attention_indexer_logits_amd/build.py` first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.xk_indexer_logits.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P]
+    lib.xk_indexer_logits.restype = I
+    lib.xk_indexer_topk_workspace_size.argtypes = [I, I, I]
+    lib.xk_indexer_topk_workspace_size.restype = Z
+    lib.xk_indexer_topk.argtypes = [P, P, P, I, I, I, P, Z, P]
+    lib.xk_indexer_topk.restype = I
+    lib.xk_mxfp4_paged_gather.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.xk_mxfp4_paged_gather.restype = I
+    lib.xk_status_string.argtypes = [I]
+    lib.xk_status_string.restype = ctypes.c_char_p
+    lib.xk_last_error.argtypes = []
+    lib.xk_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != XK_OK:
+        raise XKError(status, _lib.xk_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t, name, dtypes, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor, got {tuple(t.shape)}")
+
+
+def xk_indexer_logits(q, k, w, limit=None, q_scale=None, k_scale=None, out=None, stream=None):
+    """logits [B,T,K] fp32 = sum_h w * relu(q . k), -inf past limit (see include/xk.h).
+
+    q [B,T,64,128] and k [B,K,128] are bfloat16, or float8_e4m3fn / uint8
+    bytes with q_scale [B,T,64] and k_scale [B,K] fp32; w [B,T,64] fp32;
+    limit [B,T] int32 or None.
+    """
+    _need(q, "q", (torch.bfloat16, torch.float8_e4m3fn, torch.uint8), 4)
+    B, T, H, D = q.shape
+    fp8 = q.dtype != torch.bfloat16
+    _need(k, "k", (q.dtype,), 3)
+    K = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != D:
+        raise ValueError("k must be [B,K,D]")
+    _need(w, "w", (torch.float32,), 3)
+    if tuple(w.shape) != (B, T, H):
+        raise ValueError("w must be [B,T,H]")
+    if limit is not None:
+        _need(limit, "limit", (torch.int32,), 2)
+        if tuple(limit.shape) != (B, T):
+            raise ValueError("limit must be [B,T]")
+    if fp8:
+        _need(q_scale, "q_scale", (torch.float32,), 3)
+        _need(k_scale, "k_scale", (torch.float32,), 2)
+        if tuple(q_scale.shape) != (B, T, H) or tuple(k_scale.shape) != (B, K):
+            raise ValueError("q_scale must be [B,T,H] and k_scale [B,K]")
+    if out is None:
+        out = torch.empty((B, T, K), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 3)
+    if tuple(out.shape) != (B, T, K):
+        raise ValueError("out must be [B,T,K]")
+    _check(_lib.xk_indexer_logits(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w),
+                                  _ptr(limit), _ptr(out), B, T, K, H, D,
+                                  XK_FP8_E4M3_OCP if fp8 else XK_BF16, _stream(stream)))
+    return out
+
+
+def xk_indexer_topk_workspace_size(R: int, K: int, k: int) -> int:
+    return int(_lib.xk_indexer_topk_workspace_size(R, K, k))
+
+
+def xk_indexer_topk(logits, k: int, limit=None, out=None, workspace=None, stream=None):
+    """idx [R,k] int32: top-k per row by (score desc, j asc), -1 padded (see include/xk.h).
+
+    logits [R,K] fp32 (a [B,T,K] tensor is viewed as [B*T,K]); limit [R] int32 or None.
+    """
+    if logits.dim() == 3:
+        logits = logits.view(-1, logits.shape[-1])
+    _need(logits, "logits", (torch.float32,), 2)
+    R, K = logits.shape
+    if limit is not None:
+        limit = limit.reshape(-1)
+        _need(limit, "limit", (torch.int32,), 1)
+        if limit.shape[0] != R:
+            raise ValueError("limit must have R entries")
+    if out is None:
+        out = torch.empty((R, k), dtype=torch.int32, device=logits.device)
+    _need(out, "out", (torch.int32,), 2)
+    if tuple(out.shape) != (R, k):
+        raise ValueError("out must be [R,k]")
+    need = xk_indexer_topk_workspace_size(R, K, k)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.xk_indexer_topk(_ptr(logits), _ptr(limit), _ptr(out), R, K, k,
+                                _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def xk_mxfp4_paged_gather(kv_fp4, kv_scale, block_table, sel_pos, row_seq=None, out=None,
+                          stream=None):
+    """out [R,k,128] bf16 bits (int16 storage) of the selected mxfp4 rows (see include/xk.h).
+
+    kv_fp4 [NB,bs,64] uint8; kv_scale [NB,bs,4] uint8; block_table [S,MB] int32;
+    sel_pos [R,k] int32; row_seq [R] int32 or None.
+    """
+    _need(kv_fp4, "kv_fp4", (torch.uint8,), 3)
+    NB, bs, half = kv_fp4.shape
+    D = 2 * half
+    _need(kv_scale, "kv_scale", (torch.uint8,), 3)
+    if tuple(kv_scale.shape) != (NB, bs, D // 32):
+        raise ValueError("kv_scale must be [NB,bs,D/32]")
+    _need(block_table, "block_table", (torch.int32,), 2)
+    S, MB = block_table.shape
+    _need(sel_pos, "sel_pos", (torch.int32,), 2)
+    R, k = sel_pos.shape
+    if row_seq is not None:
+        _need(row_seq, "row_seq", (torch.int32,), 1)
+        if row_seq.shape[0] != R:
+            raise ValueError("row_seq must have R entries")
+    if out is None:
+        out = torch.empty((R, k, D), dtype=torch.int16, device=kv_fp4.device)
+    _need(out, "out", (torch.int16, torch.bfloat16), 3)
+    if tuple(out.shape) != (R, k, D):
+        raise ValueError("out must be [R,k,D]")
+    _check(_lib.xk_mxfp4_paged_gather(_ptr(kv_fp4), _ptr(kv_scale), _ptr(block_table),
+                                      _ptr(sel_pos), _ptr(row_seq), _ptr(out),
+                                      R, k, S, MB, NB, bs, D, _stream(stream)))
+    return out

@@ -1,0 +1,140 @@
+// C ABI of libxk: argument validation, device check and kernel dispatch.
+// Every check that needs no device runs before the first HIP call, so a bad
+// argument is reported without touching the GPU.
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+
+#include "../../include/xk.h"
+#include "xk_internal.h"
+
+#define XK_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+xk_status fail(xk_status s, const std::string& why) {
+  g_last_error = why;
+  return s;
+}
+
+xk_status ok() {
+  g_last_error.clear();
+  return XK_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// The code objects in this library are built for gfx950 only.
+xk_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(XK_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  static std::mutex mu;
+  static std::map<int, bool> is_gfx950;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = is_gfx950.find(dev);
+  if (it == is_gfx950.end()) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(XK_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+    it = is_gfx950.emplace(dev, strncmp(prop.gcnArchName, "gfx950", 6) == 0).first;
+  }
+  if (!it->second) return fail(XK_ERR_UNSUPPORTED, "device is not gfx950 (MI355X)");
+  return XK_OK;
+}
+
+xk_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(XK_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+XK_EXPORT const char* xk_status_string(xk_status s) {
+  switch (s) {
+    case XK_OK: return "XK_OK";
+    case XK_ERR_INVALID_ARGUMENT: return "XK_ERR_INVALID_ARGUMENT";
+    case XK_ERR_UNSUPPORTED: return "XK_ERR_UNSUPPORTED";
+    case XK_ERR_HIP: return "XK_ERR_HIP";
+  }
+  return "XK_UNKNOWN_STATUS";
+}
+
+XK_EXPORT const char* xk_last_error(void) { return g_last_error.c_str(); }
+
+XK_EXPORT xk_status xk_indexer_logits(const void* q, const float* q_scale, const void* k,
+                                      const float* k_scale, const float* w, const int32_t* limit,
+                                      float* logits, int B, int T, int K, int H, int D, int dtype,
+                                      void* stream) {
+  if (!q || !k || !w || !logits) return fail(XK_ERR_INVALID_ARGUMENT, "null q, k, w or logits");
+  if (B < 1 || T < 1 || K < 1 || H < 1 || D < 1)
+    return fail(XK_ERR_INVALID_ARGUMENT, "B, T, K, H, D must be >= 1");
+  if (dtype != XK_BF16 && dtype != XK_FP8_E4M3_OCP)
+    return fail(XK_ERR_INVALID_ARGUMENT, "unknown dtype");
+  const bool fp8 = dtype == XK_FP8_E4M3_OCP;
+  if (fp8 && (!q_scale || !k_scale))
+    return fail(XK_ERR_INVALID_ARGUMENT, "fp8 needs q_scale and k_scale");
+  if (!fp8 && (q_scale || k_scale))
+    return fail(XK_ERR_INVALID_ARGUMENT, "bf16 takes no scales");
+  if (H != xk::kHeads || D != xk::kHeadDim)
+    return fail(XK_ERR_UNSUPPORTED, "only H=64, D=128 (DeepSeek-V4 indexer) is implemented");
+  if (!aligned(q, 16) || !aligned(k, 16))
+    return fail(XK_ERR_INVALID_ARGUMENT, "q and k must be 16-byte aligned");
+  if (int64_t(B) * T > (int64_t(1) << 30))
+    return fail(XK_ERR_UNSUPPORTED, "B*T above 2^30");
+  xk_status s = check_device();
+  if (s != XK_OK) return s;
+  return launched(xk::launch_logits(q, q_scale, k, k_scale, w, limit, logits, B, T, K, fp8,
+                                    static_cast<hipStream_t>(stream)),
+                  "xk_indexer_logits launch");
+}
+
+XK_EXPORT size_t xk_indexer_topk_workspace_size(int R, int K, int k) {
+  (void)R;
+  (void)K;
+  (void)k;
+  return 0;  // rows are selected entirely on chip
+}
+
+XK_EXPORT xk_status xk_indexer_topk(const float* logits, const int32_t* limit, int32_t* idx, int R,
+                                    int K, int k, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (!logits || !idx) return fail(XK_ERR_INVALID_ARGUMENT, "null logits or idx");
+  if (R < 1 || K < 1 || k < 1) return fail(XK_ERR_INVALID_ARGUMENT, "R, K, k must be >= 1");
+  if (k > xk::kMaxTopk) return fail(XK_ERR_UNSUPPORTED, "k above 2048");
+  if (K > xk::kMaxTopkRow) return fail(XK_ERR_UNSUPPORTED, "K above 98304");
+  const size_t need = xk_indexer_topk_workspace_size(R, K, k);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(XK_ERR_INVALID_ARGUMENT, "workspace too small");
+  xk_status s = check_device();
+  if (s != XK_OK) return s;
+  return launched(xk::launch_topk(logits, limit, idx, R, K, k, static_cast<hipStream_t>(stream)),
+                  "xk_indexer_topk launch");
+}
+
+XK_EXPORT xk_status xk_mxfp4_paged_gather(const uint8_t* kv_fp4, const uint8_t* kv_scale,
+                                          const int32_t* block_table, const int32_t* sel_pos,
+                                          const int32_t* row_seq, uint16_t* out, int R, int k,
+                                          int S, int MB, int NB, int bs, int D, void* stream) {
+  if (!kv_fp4 || !kv_scale || !block_table || !sel_pos || !out)
+    return fail(XK_ERR_INVALID_ARGUMENT, "null kv_fp4, kv_scale, block_table, sel_pos or out");
+  if (R < 1 || k < 1 || S < 1 || MB < 1 || NB < 1 || bs < 1 || D < 1)
+    return fail(XK_ERR_INVALID_ARGUMENT, "R, k, S, MB, NB, bs, D must be >= 1");
+  if (D != xk::kHeadDim) return fail(XK_ERR_UNSUPPORTED, "only D=128 is implemented");
+  if ((bs & (bs - 1)) != 0) return fail(XK_ERR_UNSUPPORTED, "block size must be a power of two");
+  if (!row_seq && R > S) return fail(XK_ERR_INVALID_ARGUMENT, "row_seq NULL needs R <= S");
+  if (!aligned(kv_fp4, 4) || !aligned(out, 16))
+    return fail(XK_ERR_INVALID_ARGUMENT, "kv_fp4 must be 4-byte and out 16-byte aligned");
+  if (int64_t(R) * k > (int64_t(1) << 31) - 1)
+    return fail(XK_ERR_UNSUPPORTED, "R*k above 2^31-1");
+  xk_status s = check_device();
+  if (s != XK_OK) return s;
+  return launched(xk::launch_gather(kv_fp4, kv_scale, block_table, sel_pos, row_seq, out, R, k,
+                                    MB, bs, static_cast<hipStream_t>(stream)),
+                  "xk_mxfp4_paged_gather launch");
+}

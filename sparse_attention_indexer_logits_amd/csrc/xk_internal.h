@@ -1,0 +1,34 @@
+// Internal declarations shared by the HIP translation units of libxk.
+// (Device code only; the CPU oracle shares nothing with this file.)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xk {
+
+constexpr int kHeads = 64;     // DeepSeek-V4 index_n_heads
+constexpr int kHeadDim = 128;  // DeepSeek-V4 index_head_dim
+constexpr int kMaxTopk = 2048;
+constexpr int kMaxTopkRow = 98304;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+// Host-side launchers (one per translation unit). Arguments are validated by
+// the C ABI layer before these run; they only enqueue work and return the
+// launch status.
+hipError_t launch_logits(const void* q, const float* q_scale, const void* k,
+                         const float* k_scale, const float* w, const int32_t* limit,
+                         float* logits, int B, int T, int K, bool fp8, hipStream_t stream);
+hipError_t launch_topk(const float* logits, const int32_t* limit, int32_t* idx, int R,
+                       int K, int k, hipStream_t stream);
+hipError_t launch_gather(const uint8_t* kv_fp4, const uint8_t* kv_scale,
+                         const int32_t* block_table, const int32_t* sel_pos,
+                         const int32_t* row_seq, uint16_t* out, int R, int k, int MB,
+                         int bs, hipStream_t stream);
+
+}  // namespace xk

@@ -1,0 +1,108 @@
+"""The C ABI: library loads, exports every declared symbol, rejects bad
+arguments on the host before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "xk.h")
+LIB = os.path.join(ROOT, "sparse_attention_indexer_logits_amd", "libxk.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libxk.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(xk_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import sparse_attention_indexer_logits_amd as xk
+    return xk.lib()
+
+
+def test_header_declares_the_three_operations():
+    names = declared_functions()
+    for n in ("xk_indexer_logits", "xk_indexer_topk", "xk_mxfp4_paged_gather",
+              "xk_indexer_topk_workspace_size", "xk_status_string", "xk_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(LIB)
+    for n in declared_functions():
+        assert hasattr(raw, n), n
+    import sparse_attention_indexer_logits_amd as xk
+    assert set(xk.EXPORTED) == set(declared_functions())
+
+
+def test_status_strings(lib):
+    assert lib.xk_status_string(0) == b"XK_OK"
+    assert lib.xk_status_string(1) == b"XK_ERR_INVALID_ARGUMENT"
+    assert lib.xk_status_string(2) == b"XK_ERR_UNSUPPORTED"
+    assert lib.xk_status_string(3) == b"XK_ERR_HIP"
+
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails before any HIP call
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    # (q, q_scale, k, k_scale, w, limit, logits, B, T, K, H, D, dtype)
+    ((None, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 64, 128, 0), 1, "null"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 0, 1, 8, 64, 128, 0), 1, ">= 1"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 1, -3, 64, 128, 0), 1, ">= 1"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 64, 128, 7), 1, "dtype"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 64, 128, 1), 1, "scale"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1, 8, 64, 128, 0), 1, "no scales"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 32, 128, 0), 2, "H=64"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 64, 64, 0), 2, "H=64"),
+    ((FAKE + 2, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 64, 128, 0), 1, "aligned"),
+])
+def test_logits_validation(lib, args, status, needle):
+    assert lib.xk_indexer_logits(*args, None) == status
+    assert needle in lib.xk_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    # (logits, limit, idx, R, K, k, workspace, workspace_bytes)
+    ((None, None, FAKE, 1, 8, 4, None, 0), 1, "null"),
+    ((FAKE, None, FAKE, 0, 8, 4, None, 0), 1, ">= 1"),
+    ((FAKE, None, FAKE, 1, 8, 0, None, 0), 1, ">= 1"),
+    ((FAKE, None, FAKE, 1, 8, 4096, None, 0), 2, "2048"),
+    ((FAKE, None, FAKE, 1, 200000, 512, None, 0), 2, "98304"),
+])
+def test_topk_validation(lib, args, status, needle):
+    assert lib.xk_indexer_topk(*args, None) == status
+    assert needle in lib.xk_last_error().decode()
+
+
+def test_topk_workspace_is_host_only(lib):
+    assert lib.xk_indexer_topk_workspace_size(4096, 4096, 512) == 0
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    # (kv_fp4, kv_scale, block_table, sel_pos, row_seq, out, R, k, S, MB, NB, bs, D)
+    ((None, FAKE, FAKE, FAKE, None, FAKE, 1, 4, 1, 1, 1, 64, 128), 1, "null"),
+    ((FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 0, 1, 1, 1, 64, 128), 1, ">= 1"),
+    ((FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 4, 1, 1, 1, 64, 64), 2, "D=128"),
+    ((FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 4, 1, 1, 1, 48, 128), 2, "power of two"),
+    ((FAKE, FAKE, FAKE, FAKE, None, FAKE, 3, 4, 2, 1, 1, 64, 128), 1, "R <= S"),
+    ((FAKE + 1, FAKE, FAKE, FAKE, None, FAKE, 1, 4, 1, 1, 1, 64, 128), 1, "aligned"),
+    ((FAKE, FAKE, FAKE, FAKE, None, FAKE + 4, 1, 4, 1, 1, 1, 64, 128), 1, "aligned"),
+])
+def test_gather_validation(lib, args, status, needle):
+    assert lib.xk_mxfp4_paged_gather(*args, None) == status
+    assert needle in lib.xk_last_error().decode()
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    import sparse_attention_indexer_logits_amd as xk
+    q = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        xk.xk_indexer_logits(q, torch.zeros((1, 8, 128), dtype=torch.bfloat16),
+                             torch.zeros((1, 1, 64)))

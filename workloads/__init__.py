@@ -208,3 +208,31 @@ def apply_forced_negatives(idx: np.ndarray, neg_slots) -> np.ndarray:
         for r in range(sel.shape[0]):
             sel[r, neg_slots[r]] = -1
     return sel
+
+
+def to_device(x: dict, device="cuda") -> dict:
+    """Device copies of a config's arrays, typed for the binding (bf16 / fp8 / int)."""
+    import torch
+
+    def dev(a, dtype=None):
+        t = torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        return t.view(dtype) if dtype is not None else t
+
+    cfg = x["cfg"]
+    out = {}
+    if cfg.dtype == "bf16":
+        out["q"] = dev(x["q"].view(np.int16), torch.bfloat16)
+        out["k"] = dev(x["k"].view(np.int16), torch.bfloat16)
+        out["q_scale"] = out["k_scale"] = None
+    else:
+        out["q"] = dev(x["q"], torch.float8_e4m3fn)
+        out["k"] = dev(x["k"], torch.float8_e4m3fn)
+        out["q_scale"] = dev(x["q_scale"])
+        out["k_scale"] = dev(x["k_scale"])
+    out["w"] = dev(x["w"])
+    out["limit"] = dev(x["limit"])
+    out["kv_fp4"] = dev(x["kv_fp4"])
+    out["kv_scale"] = dev(x["kv_scale"])
+    out["block_table"] = dev(x["block_table"])
+    out["row_seq"] = dev(x["row_seq"])
+    return out
