@@ -111,13 +111,34 @@ def cpu_baseline(x, work, budget_s):
 
     t1, _ = run(1)
     n = int(min(R, max(1, budget_s / max(t1, 1e-6))))
-    tn, rows = run(n)
-    frac = float(np.clip(x["limit"].reshape(-1)[rows] + 1, 0, cfg.K).sum()) / max(work["pairs"], 1)
-    step_s = tn / max(frac, 1e-12)              # scale by the share of the step's pairs done
+    if n < R:
+        tn, rows = run(n)
+        frac = float(np.clip(x["limit"].reshape(-1)[rows] + 1, 0, cfg.K).sum()) / max(work["pairs"], 1)
+        step_s = tn / max(frac, 1e-12)          # scale by the share of the step's pairs done
+        sample = (f"{n} of {R} query rows (logits + top-k + gather, float64 numpy), {tn:.1f} s, "
+                  "scaled by their share of the step's valid pairs")
+    else:
+        total, reps = 0.0, 0
+        while total < budget_s or reps == 0:    # whole steps, repeated to fill the budget
+            t, _ = run(R)
+            total, reps = total + t, reps + 1
+        step_s = total / reps
+        sample = (f"{reps} whole steps ({R} query rows each: logits + top-k + gather, float64 "
+                  f"numpy), {total:.1f} s")
     return {"value": work["logits_flops"] / step_s / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{n} of {R} query rows (logits + top-k + gather, float64 numpy), "
-                      f"{tn:.1f} s, scaled by their share of the step's valid pairs"}
+            "kind": "oracle", "sample": sample, "ms_per_step": step_s * 1e3}
+
+
+def copy_calibration(nbytes=1 << 30, reps=4):
+    """A plain device copy of known size, to scale rocprofv3 FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def main():
@@ -129,7 +150,12 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="input copies rotated across steps (0=auto)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (PMC byte-counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the indexer path here "
               "is built and timed on a single MI355X.", file=sys.stderr)
