@@ -104,8 +104,8 @@ size_t xk_indexer_topk_workspace_size(int R, int K, int k);
  *   logits     [R,K] fp32 (e.g. xk_indexer_logits output with R = B*T)
  *   limit      [R]   int32 inclusive last valid key, or NULL (n = K)
  *   idx        [R,k] int32 output; every element is written
- *   1 <= k <= 2048 and 1 <= K <= 98304 (rows are held on chip), else
- *   XK_ERR_UNSUPPORTED.
+ *   1 <= k <= 2048, else XK_ERR_UNSUPPORTED; K >= 1 (rows up to 16384 keys
+ *   are held in registers, longer rows are re-read for each selection pass).
  *   workspace  device buffer of xk_indexer_topk_workspace_size(R,K,k) bytes
  *              (may be NULL when that size is 0)
  */

@@ -7,25 +7,28 @@
 // with H = 64 heads, D = 128, one shared key per position (MQA).
 //
 // Mapping onto the matrix cores: for one query the 64 heads are the M
-// dimension (two 32-row MFMA tiles), 32 keys are the N dimension and D the
-// contraction. With a 32x32 fp32 accumulator a lane holds 16 rows (heads) of
-// ONE column (key), so the ReLU, the head weight and most of the head sum run
-// in registers of that lane; one cross-lane add (lane l with l^32) finishes
-// the 64-head sum. The score never leaves registers until it is final.
+// dimension, keys the N dimension and D the contraction. Because the
+// accumulator layout puts several rows (heads) of ONE column (key) in each
+// lane, the ReLU, the head weight and most of the head sum run in registers
+// of that lane and only a few cross-lane adds finish the 64-head sum; the
+// score never leaves registers until it is final.
 //
-// bf16: v_mfma_f32_32x32x16_bf16, 8 steps over D.
-// fp8 : v_mfma_scale_f32_32x32x64_f8f6f4 with both operands OCP e4m3 and unit
-//       block scales, 2 steps over D. The dequant scales are positive, so
-//       relu(sq*sk*x) = sq*sk*relu(x): sq folds into the head weight and sk
-//       multiplies the finished score.
+// The dequant scales of fp8 inputs are positive, so relu(sq*sk*x) =
+// sq*sk*relu(x): sq folds into the head weight and sk multiplies the
+// finished score. fp8 operands use the f8f6f4 MFMAs with OCP e4m3 on both
+// sides and unit block scales.
 //
-// Two kernels share that core:
-//  * decode  (few queries, long rows; HBM bound): a workgroup owns one query
-//    and a key chunk; each wave streams its own 32-key tiles straight from
-//    HBM into MFMA B registers, prefetching one tile ahead.
-//  * prefill (many queries; MFMA bound): a workgroup owns 8 queries (one per
-//    wave) and a key chunk; 64-key tiles are staged once in LDS and read by
-//    all 8 waves, so each key byte fetched from L2 feeds 8 queries.
+// Two kernels:
+//  * decode  (few queries, long rows; HBM bound): 32x32 tiles
+//    (v_mfma_f32_32x32x16_bf16 / v_mfma_scale_f32_32x32x64_f8f6f4; a lane
+//    holds 32 heads of one key). A workgroup owns one query and a key chunk;
+//    each wave streams its own 32-key tiles with coalesced loads, two tiles
+//    in flight, through a private LDS slab.
+//  * prefill (many queries; MFMA bound): 16x16 tiles
+//    (v_mfma_f32_16x16x32_bf16 / v_mfma_scale_f32_16x16x128_f8f6f4; a lane
+//    holds 16 heads of one key, so per-query state is small). A workgroup
+//    owns 4 (bf16) or 8 (fp8) queries, one per wave, and a key chunk;
+//    double-buffered 64-key LDS tiles are shared by all its waves.
 // Causal tiles that lie wholly past a query's limit are skipped and filled
 // with -inf.
 #include <math.h>
@@ -76,69 +79,19 @@ struct Mma<true> {  // OCP e4m3 operands
   }
 };
 
-// Everything one wave keeps for its query: the 64x128 q block as MFMA A
-// fragments and the head weights laid out like the accumulator rows.
-template <bool FP8>
-struct QueryRegs {
-  using M = Mma<FP8>;
-  typename M::Frag a[2][M::kSteps];
-  float wr[2][16];
-
-  __device__ void load(const uint8_t* qrow, const float* wrow, const float* sqrow, int lane) {
-    const int hf = lane >> 5, col = lane & 31;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int s = 0; s < M::kSteps; ++s)
-        a[mt][s] = M::load(qrow + ((32 * mt + col) * kHeadDim + M::dofs(s, hf)) * M::kElemBytes);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int h = 32 * mt + acc_row(i, lane);
-        wr[mt][i] = FP8 ? wrow[h] * sqrow[h] : wrow[h];
-      }
-  }
-
-  __device__ void zero() {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int s = 0; s < M::kSteps; ++s) a[mt][s] = typename M::Frag{};
-#pragma unroll
-      for (int i = 0; i < 16; ++i) wr[mt][i] = 0.f;
-    }
-  }
-
-  // Score of key (lane % 32) of a 32-key tile whose B fragments are `b`.
-  // Returned in both lane halves.
-  __device__ float score(const typename M::Frag (&b)[M::kSteps]) const {
-    f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-    for (int s = 0; s < M::kSteps; ++s) {
-      acc0 = M::mma(a[0][s], b[s], acc0);
-      acc1 = M::mma(a[1][s], b[s], acc1);
-    }
-    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      p0 = fmaf(wr[0][i], fmaxf(acc0[i], 0.f), p0);
-      p1 = fmaf(wr[0][i + 1], fmaxf(acc0[i + 1], 0.f), p1);
-      p2 = fmaf(wr[1][i], fmaxf(acc1[i], 0.f), p2);
-      p3 = fmaf(wr[1][i + 1], fmaxf(acc1[i + 1], 0.f), p3);
-    }
-    float p = (p0 + p1) + (p2 + p3);
-    p += __shfl_xor(p, 32);  // the other 32 heads of this key live in lane ^ 32
-    return p;
-  }
-};
-
 __device__ __forceinline__ int clamp_limit(const int32_t* limit, int64_t bt, int K) {
   return limit ? min(limit[bt], K - 1) : K - 1;
 }
 
 // ---------------------------------------------------------------------------
-// decode: 1-D grid over (B*T rows) x (key chunks); 4 waves, each streaming its own 32-key tiles.
+// decode: 1-D grid over (B*T rows) x (key chunks); 4 waves share one query.
+// q (and its head weights) is staged once per workgroup in LDS. Each wave
+// streams its own 32-key tiles with fully coalesced 1 KB loads, two tiles in
+// flight, and turns rows into MFMA B fragments through a private LDS slab;
+// A fragments are read from the staged q. No barrier inside the key loop.
+constexpr int kDecWaves = 4;
+constexpr int kDecTile = 32;
+
 template <bool FP8>
 __global__ __launch_bounds__(256, 2) void logits_decode_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
@@ -146,7 +99,14 @@ __global__ __launch_bounds__(256, 2) void logits_decode_kernel(
     const float* __restrict__ w, const int32_t* __restrict__ limit,
     float* __restrict__ out, int T, int K, int keys_per_wg, int n_chunks) {
   using M = Mma<FP8>;
-  constexpr int kRowBytes = kHeadDim * M::kElemBytes;
+  constexpr int kRowBytes = kHeadDim * M::kElemBytes;     // 256 or 128
+  constexpr int kPitch = kRowBytes + 16;                  // padded LDS row
+  constexpr int kLoads = kDecTile * kRowBytes / 1024;     // 1 KB per wave load
+  constexpr int kLanesPerRow = kRowBytes / 16;            // 16 or 8
+  constexpr int kRowsPerLoad = 64 / kLanesPerRow;         // 4 or 8
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kHeads * kPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t slab[kDecWaves][kDecTile * kPitch];
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hf = lane >> 5, col = lane & 31;
   const int64_t bt = blockIdx.x / n_chunks;  // all chunks of a row are adjacent
@@ -159,113 +119,315 @@ __global__ __launch_bounds__(256, 2) void logits_decode_kernel(
 
   for (int j = max(j_begin, lim + 1) + int(threadIdx.x); j < j_end; j += 256) orow[j] = -INFINITY;
   const int c_end = min(j_end, lim + 1);  // keys [j_begin, c_end) are scored
-  if (c_end <= j_begin) return;
+  if (c_end <= j_begin) return;           // uniform over the workgroup
 
-  QueryRegs<FP8> qr;
-  qr.load(q + bt * (kHeads * kRowBytes), w + bt * kHeads, FP8 ? q_scale + bt * kHeads : nullptr,
-          lane);
   const uint8_t* kseq = k + b * int64_t(K) * kRowBytes;
   const float* skseq = FP8 ? k_scale + b * int64_t(K) : nullptr;
-
-  typename M::Frag nxt[M::kSteps];
-  auto load_tile = [&](int j0) {
-    const int row = min(j0 + col, K - 1);  // ragged tail: clamp, result discarded
-    const uint8_t* krow = kseq + int64_t(row) * kRowBytes;
+  uint8_t* my = slab[wave];
+  // coalesced tile load: load i covers rows [i*kRowsPerLoad, ...); lane l
+  // takes 16 bytes at offset 16*l of that 1 KB
+  auto gload = [&](int j0, u32x4 (&r)[kLoads]) {
 #pragma unroll
-    for (int s = 0; s < M::kSteps; ++s) nxt[s] = M::load(krow + M::dofs(s, hf) * M::kElemBytes);
-  };
-  int j0 = j_begin + 32 * wave;
-  if (j0 < c_end) load_tile(j0);
-  for (; j0 < c_end; j0 += 128) {
-    typename M::Frag cur[M::kSteps];
-#pragma unroll
-    for (int s = 0; s < M::kSteps; ++s) cur[s] = nxt[s];
-    if (j0 + 128 < c_end) load_tile(j0 + 128);
-    float p = qr.score(cur);
-    const int j = j0 + col;
-    if (hf == 0 && j < c_end) {
-      if (FP8) p *= skseq[j];
-      orow[j] = p;
+    for (int i = 0; i < kLoads; ++i) {
+      const int row = min(j0 + i * kRowsPerLoad + lane / kLanesPerRow, K - 1);
+      r[i] = *reinterpret_cast<const u32x4*>(kseq + int64_t(row) * kRowBytes +
+                                             (lane % kLanesPerRow) * 16);
     }
+  };
+  auto lds_put = [&](const u32x4 (&r)[kLoads]) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int row = i * kRowsPerLoad + lane / kLanesPerRow;
+      *reinterpret_cast<u32x4*>(my + row * kPitch + (lane % kLanesPerRow) * 16) = r[i];
+    }
+  };
+
+  constexpr int kStride = kDecWaves * kDecTile;
+  u32x4 buf0[kLoads], buf1[kLoads];
+  int j0 = j_begin + wave * kDecTile;
+  if (j0 < c_end) gload(j0, buf0);
+  if (j0 + kStride < c_end) gload(j0 + kStride, buf1);
+
+  // stage q while the first tiles are in flight
+  const uint8_t* qsrc = q + bt * (kHeads * kRowBytes);
+  for (int c = threadIdx.x; c < kHeads * kLanesPerRow; c += 256) {
+    const int r = c / kLanesPerRow, cc = c % kLanesPerRow;
+    *reinterpret_cast<u32x4*>(q_lds + r * kPitch + cc * 16) =
+        *reinterpret_cast<const u32x4*>(qsrc + r * kRowBytes + cc * 16);
+  }
+  float wr[2][16];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int h = 32 * mt + acc_row(i, lane);
+      wr[mt][i] = FP8 ? w[bt * kHeads + h] * q_scale[bt * kHeads + h] : w[bt * kHeads + h];
+    }
+  __syncthreads();
+
+  auto score = [&](int jt) {
+    f32x16 acc0 = {}, acc1 = {};
+    const uint8_t* brow = my + col * kPitch;
+    const uint8_t* arow0 = q_lds + col * kPitch;
+    const uint8_t* arow1 = q_lds + (32 + col) * kPitch;
+#pragma unroll
+    for (int s = 0; s < M::kSteps; ++s) {
+      const int off = M::dofs(s, hf) * M::kElemBytes;
+      const typename M::Frag bfr = M::load(brow + off);
+      acc0 = M::mma(M::load(arow0 + off), bfr, acc0);
+      acc1 = M::mma(M::load(arow1 + off), bfr, acc1);
+    }
+    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      p0 = fmaf(wr[0][i], fmaxf(acc0[i], 0.f), p0);
+      p1 = fmaf(wr[0][i + 1], fmaxf(acc0[i + 1], 0.f), p1);
+      p2 = fmaf(wr[1][i], fmaxf(acc1[i], 0.f), p2);
+      p3 = fmaf(wr[1][i + 1], fmaxf(acc1[i + 1], 0.f), p3);
+    }
+    float tot = (p0 + p1) + (p2 + p3);
+    tot += __shfl_xor(tot, 32);
+    const int j = jt + col;
+    if (hf == 0 && j < c_end) {
+      if (FP8) tot *= skseq[j];
+      orow[j] = tot;
+    }
+  };
+
+  // two tiles in flight; the loop body handles them alternately
+  while (j0 < c_end) {
+    lds_put(buf0);
+    if (j0 + 2 * kStride < c_end) gload(j0 + 2 * kStride, buf0);
+    score(j0);
+    j0 += kStride;
+    if (j0 >= c_end) break;
+    lds_put(buf1);
+    if (j0 + 2 * kStride < c_end) gload(j0 + 2 * kStride, buf1);
+    score(j0);
+    j0 += kStride;
   }
 }
 
 // ---------------------------------------------------------------------------
-// prefill: 1-D grid over (query blocks of 8, longest causal rows first) x B x
-// (key chunks); 8 waves = 8 queries.
-constexpr int kPrefillQ = 8;
-constexpr int kPrefillTile = 64;
+// prefill: 16x16 MFMA tiles. For one query the 64 heads are four 16-row
+// M-tiles and 16 keys the N dimension; a 16x16 fp32 accumulator gives lane l
+// rows 4*(l/16)+i (i < 4) of column l%16, i.e. 16 heads of one key per lane
+// across the four M-tiles. That keeps the per-query state small (16 head
+// weights + 16 accumulators per lane) so a wave can own QW queries and each
+// B fragment read from LDS feeds 4*QW MFMAs. After the four 16-key subtiles
+// of a 64-key tile, a 3-shuffle butterfly leaves lane l with the full score
+// of key l, so stores are 64 consecutive floats.
+template <bool FP8>
+struct Mma16;
+
+template <>
+struct Mma16<false> {  // bf16: v_mfma_f32_16x16x32_bf16, 4 steps over D = 128
+  using Frag = bf16x8;
+  static constexpr int kSteps = 4;
+  static constexpr int kElemBytes = 2;
+  __device__ static int dofs(int s, int g) { return 32 * s + 8 * g; }  // g = lane / 16
+  __device__ static Frag load(const uint8_t* p) { return *reinterpret_cast<const Frag*>(p); }
+  __device__ static f32x4 mma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma16<true> {  // OCP e4m3: v_mfma_scale_f32_16x16x128_f8f6f4, 1 step
+  using Frag = i32x8;
+  static constexpr int kSteps = 1;
+  static constexpr int kElemBytes = 1;
+  __device__ static int dofs(int, int g) { return 32 * g; }
+  __device__ static Frag load(const uint8_t* p) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 16);
+    return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  __device__ static f32x4 mma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
 
 template <bool FP8>
-__global__ __launch_bounds__(512, 2) void logits_prefill_kernel(
+struct Query16 {
+  using M = Mma16<FP8>;
+  typename M::Frag a[4][M::kSteps];  // [M-tile][step]
+  float wr[4][4];                    // head 16*mt + 4*(lane/16) + i
+
+  __device__ void load(const uint8_t* qrow, const float* wrow, const float* sqrow, int lane) {
+    const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int s = 0; s < M::kSteps; ++s)
+        a[mt][s] = M::load(qrow + ((16 * mt + r) * kHeadDim + M::dofs(s, g)) * M::kElemBytes);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 16 * mt + 4 * g + i;
+        wr[mt][i] = FP8 ? wrow[h] * sqrow[h] : wrow[h];
+      }
+  }
+  __device__ void zero() {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int s = 0; s < M::kSteps; ++s) a[mt][s] = typename M::Frag{};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wr[mt][i] = 0.f;
+    }
+  }
+  // this lane's 16-head partial score of key (lane % 16) of a 16-key subtile
+  __device__ float partial(const typename M::Frag (&b)[M::kSteps]) const {
+    f32x4 acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < M::kSteps; ++s) acc[mt] = M::mma(a[mt][s], b[s], acc[mt]);
+    }
+    float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      p0 = fmaf(wr[mt][0], fmaxf(acc[mt][0], 0.f), p0);
+      p1 = fmaf(wr[mt][1], fmaxf(acc[mt][1], 0.f), p1);
+      p0 = fmaf(wr[mt][2], fmaxf(acc[mt][2], 0.f), p0);
+      p1 = fmaf(wr[mt][3], fmaxf(acc[mt][3], 0.f), p1);
+    }
+    return p0 + p1;
+  }
+};
+
+// p[st] = this lane's partial for key 16*st + lane%16; returns the full score
+// of key `lane` (sum over the four lane groups, routed by a butterfly).
+__device__ __forceinline__ float subtile_total(const float (&p)[4], int lane) {
+  const bool up32 = lane >= 32, up16 = (lane & 16) != 0;
+  // xor 32: lower half keeps subtiles 0,1; upper half keeps 2,3
+  const float k0 = up32 ? p[2] : p[0], k1 = up32 ? p[3] : p[1];
+  const float s0 = up32 ? p[0] : p[2], s1 = up32 ? p[1] : p[3];
+  const float a0 = k0 + __shfl_xor(s0, 32);
+  const float a1 = k1 + __shfl_xor(s1, 32);
+  // xor 16: even groups keep the first, odd groups the second
+  const float keep = up16 ? a1 : a0, send = up16 ? a0 : a1;
+  return keep + __shfl_xor(send, 16);
+}
+
+// prefill grid: 1-D over (query blocks, longest causal rows first) x B x
+// (key chunks). NW waves x QW queries per workgroup share double-buffered
+// 64-key LDS tiles; the next tile's global loads are issued before this
+// tile's MFMAs and stored to LDS after them, one barrier per tile.
+constexpr int kPrefillTile = 64;
+
+template <bool FP8, int QW, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ k, const float* __restrict__ k_scale,
     const float* __restrict__ w, const int32_t* __restrict__ limit,
     float* __restrict__ out, int B, int T, int K, int keys_per_wg, int n_chunks, int n_qblocks) {
-  using M = Mma<FP8>;
+  using M = Mma16<FP8>;
+  constexpr int QB = QW * NW;  // queries per workgroup
   constexpr int kRowBytes = kHeadDim * M::kElemBytes;
   constexpr int kPitch = kRowBytes + 16;  // 16-byte pad: conflict-free fragment reads
   constexpr int kChunks = kRowBytes / 16;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kPrefillTile * kPitch];
+  constexpr int kThreads = NW * 64;
+  constexpr int kPer = kPrefillTile * kChunks / kThreads;  // 16-byte pieces per thread per tile
+  static_assert(kPer >= 1 && kPrefillTile * kChunks % kThreads == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kPrefillTile * kPitch];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hf = lane >> 5, col = lane & 31;
+  const int g = lane >> 4, r = lane & 15;
   const int chunk = int(blockIdx.x % n_chunks);
   const int rest = int(blockIdx.x / n_chunks);
   const int64_t b = rest % B;
   const int qb = n_qblocks - 1 - rest / B;  // longest causal rows first
-  const int t = qb * kPrefillQ + wave;
-  const bool qvalid = t < T;
-  const int64_t bt = b * T + t;
-  const int lim = qvalid ? clamp_limit(limit, bt, K) : -1;
   int blk_lim = -1;
 #pragma unroll
-  for (int i = 0; i < kPrefillQ; ++i) {
-    const int ti = qb * kPrefillQ + i;
+  for (int i = 0; i < QB; ++i) {
+    const int ti = qb * QB + i;
     if (ti < T) blk_lim = max(blk_lim, clamp_limit(limit, b * T + ti, K));
   }
   const int j_begin = chunk * keys_per_wg;
   const int j_end = min(j_begin + keys_per_wg, K);
-  float* orow = out + bt * K;
-  if (qvalid)
-    for (int j = max(j_begin, lim + 1) + lane; j < j_end; j += 64) orow[j] = -INFINITY;
   const int c_end = min(j_end, blk_lim + 1);
-  if (c_end <= j_begin) return;  // uniform over the workgroup
 
-  QueryRegs<FP8> qr;
-  if (qvalid)
-    qr.load(q + bt * (kHeads * kRowBytes), w + bt * kHeads,
-            FP8 ? q_scale + bt * kHeads : nullptr, lane);
-  else
-    qr.zero();
+  int q_end[QW];
+  int64_t bt[QW];
+  bool qvalid[QW];
+#pragma unroll
+  for (int qi = 0; qi < QW; ++qi) {
+    const int t = qb * QB + QW * wave + qi;
+    qvalid[qi] = t < T;
+    bt[qi] = b * T + (qvalid[qi] ? t : 0);
+    const int lim = qvalid[qi] ? clamp_limit(limit, bt[qi], K) : -1;
+    q_end[qi] = min(j_end, lim + 1);
+    if (qvalid[qi]) {
+      float* orow = out + bt[qi] * K;
+      for (int j = max(j_begin, lim + 1) + lane; j < j_end; j += 64) orow[j] = -INFINITY;
+    }
+  }
+  if (c_end <= j_begin) return;  // uniform over the workgroup
+  int w_end = q_end[0];
+#pragma unroll
+  for (int qi = 1; qi < QW; ++qi) w_end = max(w_end, q_end[qi]);
+
   const uint8_t* kseq = k + b * int64_t(K) * kRowBytes;
   const float* skseq = FP8 ? k_scale + b * int64_t(K) : nullptr;
-  const int q_end = min(j_end, lim + 1);  // this wave's scored keys end
-
-  for (int j0 = j_begin; j0 < c_end; j0 += kPrefillTile) {
-    __syncthreads();  // previous tile fully consumed
-    for (int c = threadIdx.x; c < kPrefillTile * kChunks; c += 512) {
-      const int r = c / kChunks, cc = c % kChunks;
-      const int row = min(j0 + r, K - 1);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(kseq + int64_t(row) * kRowBytes + cc * 16);
-      *reinterpret_cast<u32x4*>(tile + r * kPitch + cc * 16) = v;
+  u32x4 pre[kPer];
+  auto gload = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = int(threadIdx.x) + kThreads * i;
+      const int row = min(j0 + c / kChunks, K - 1);
+      pre[i] = *reinterpret_cast<const u32x4*>(kseq + int64_t(row) * kRowBytes + (c % kChunks) * 16);
     }
-    __syncthreads();
+  };
+  auto lds_put = [&](uint8_t* dst) {
 #pragma unroll
-    for (int nt = 0; nt < kPrefillTile / 32; ++nt) {
-      const int jt = j0 + 32 * nt;
-      if (jt >= q_end) break;  // uniform per wave
-      typename M::Frag bf[M::kSteps];
-      const uint8_t* lrow = tile + (32 * nt + col) * kPitch;
+    for (int i = 0; i < kPer; ++i) {
+      const int c = int(threadIdx.x) + kThreads * i;
+      *reinterpret_cast<u32x4*>(dst + (c / kChunks) * kPitch + (c % kChunks) * 16) = pre[i];
+    }
+  };
+
+  gload(j_begin);
+  Query16<FP8> qr[QW];
 #pragma unroll
-      for (int s = 0; s < M::kSteps; ++s) bf[s] = M::load(lrow + M::dofs(s, hf) * M::kElemBytes);
-      float p = qr.score(bf);
-      const int j = jt + col;
-      if (hf == 0 && j < q_end) {
-        if (FP8) p *= skseq[j];
-        orow[j] = p;
+  for (int qi = 0; qi < QW; ++qi) {
+    if (qvalid[qi])
+      qr[qi].load(q + bt[qi] * (kHeads * kRowBytes), w + bt[qi] * kHeads,
+                  FP8 ? q_scale + bt[qi] * kHeads : nullptr, lane);
+    else
+      qr[qi].zero();
+  }
+  lds_put(tile[0]);
+  __syncthreads();
+
+  int cur = 0;
+  for (int j0 = j_begin; j0 < c_end; j0 += kPrefillTile, cur ^= 1) {
+    const bool more = j0 + kPrefillTile < c_end;  // uniform
+    if (more) gload(j0 + kPrefillTile);
+    if (j0 < w_end) {
+      float p[QW][4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        typename M::Frag bf[M::kSteps];
+        const uint8_t* lrow = tile[cur] + (16 * st + r) * kPitch;
+#pragma unroll
+        for (int s = 0; s < M::kSteps; ++s) bf[s] = M::load(lrow + M::dofs(s, g) * M::kElemBytes);
+#pragma unroll
+        for (int qi = 0; qi < QW; ++qi) p[qi][st] = qr[qi].partial(bf);
+      }
+      const int j = j0 + lane;
+      const float sk = FP8 && j < w_end ? skseq[j] : 1.f;
+#pragma unroll
+      for (int qi = 0; qi < QW; ++qi) {
+        const float tot = subtile_total(p[qi], lane);
+        if (j < q_end[qi]) out[bt[qi] * K + j] = FP8 ? tot * sk : tot;
       }
     }
+    if (more) lds_put(tile[cur ^ 1]);
+    __syncthreads();
   }
 }
 
@@ -278,12 +440,12 @@ hipError_t launch_logits(const void* q, const float* q_scale, const void* k,
                          float* logits, int B, int T, int K, bool fp8, hipStream_t stream) {
   const auto* q8 = static_cast<const uint8_t*>(q);
   const auto* k8 = static_cast<const uint8_t*>(k);
-  if (T < kPrefillQ) {
-    // one query per workgroup; ~1024 workgroups, chunks a multiple of 4 waves x 32 keys
+  if (T < 8) {
+    // one query per workgroup; ~512 workgroups, chunks a multiple of 4 waves x 64 keys
     const int64_t rows = int64_t(B) * T;
-    int64_t per = (int64_t(K) * rows + 1023) / 1024;
-    int kpw = int(std::min<int64_t>(std::max<int64_t>(per, 256), K));
-    kpw = round_up(kpw, 128);
+    int64_t per = (int64_t(K) * rows + 511) / 512;
+    int kpw = int(std::min<int64_t>(std::max<int64_t>(per, 512), K));
+    kpw = round_up(kpw, kDecWaves * kDecTile);
     const int nch = (K + kpw - 1) / kpw;
     const dim3 grid(unsigned(rows * nch));
     if (fp8)
@@ -293,18 +455,25 @@ hipError_t launch_logits(const void* q, const float* q_scale, const void* k,
       hipLaunchKernelGGL(logits_decode_kernel<false>, grid, dim3(256), 0, stream, q8, q_scale, k8,
                          k_scale, w, limit, logits, T, K, kpw, nch);
   } else {
-    const int nqb = (T + kPrefillQ - 1) / kPrefillQ;
+    // One query per wave (64 VGPRs of A fragments): 4 waves for bf16 (three
+    // workgroups per CU), 8 for fp8 (half the A bytes, so a workgroup's LDS
+    // tile is shared by more queries). Shapes measured on the flash-prefill
+    // and long-context configs.
+    const int QB = fp8 ? 8 : 4;
+    const int nqb = (T + QB - 1) / QB;
     const int64_t qblocks = int64_t(nqb) * B;
-    const int nkc = int(std::max<int64_t>(1, (2048 + qblocks - 1) / qblocks));
+    // key chunks re-read the block's q, so split keys only when there are
+    // fewer than ~1024 query blocks
+    const int nkc = int(std::max<int64_t>(1, (1024 + qblocks - 1) / qblocks));
     const int kpw = round_up((K + nkc - 1) / nkc, kPrefillTile);
     const int nch = (K + kpw - 1) / kpw;
     const dim3 grid(unsigned(int64_t(nch) * qblocks));
     if (fp8)
-      hipLaunchKernelGGL(logits_prefill_kernel<true>, grid, dim3(512), 0, stream, q8, q_scale, k8,
-                         k_scale, w, limit, logits, B, T, K, kpw, nch, nqb);
+      hipLaunchKernelGGL((logits_prefill_kernel<true, 1, 8>), grid, dim3(8 * 64), 0, stream, q8,
+                         q_scale, k8, k_scale, w, limit, logits, B, T, K, kpw, nch, nqb);
     else
-      hipLaunchKernelGGL(logits_prefill_kernel<false>, grid, dim3(512), 0, stream, q8, q_scale, k8,
-                         k_scale, w, limit, logits, B, T, K, kpw, nch, nqb);
+      hipLaunchKernelGGL((logits_prefill_kernel<false, 1, 4>), grid, dim3(4 * 64), 0, stream, q8,
+                         q_scale, k8, k_scale, w, limit, logits, B, T, K, kpw, nch, nqb);
   }
   return hipGetLastError();
 }

@@ -6,20 +6,26 @@
 // selection): among the n = clamp(limit+1, 0, K) valid keys of a row, the
 // min(k, n) largest scores ordered by (score desc, j asc), then -1 padding.
 //
-// One workgroup per row; the row is read from HBM once and stays in VGPRs
-// (V values per thread, j = tid + BLOCK*v).
-//  1. Scores become order-preserving u32 keys (-0.0 first folded to +0.0);
-//     key 0 marks an invalid slot (every valid float maps above it).
-//  2. Radix select, 8 bits per pass from the top: an LDS histogram of the
-//     next digit over the keys still matching the prefix, then one wave finds
-//     the digit holding the k-th largest key with a suffix scan. A pass stops
-//     early when that digit's bucket is exactly what is still needed.
-//  3. If the threshold bucket holds more keys than needed, the lowest j win:
-//     a second radix select over j (ascending) inside that bucket gives the
-//     cut. Histogram counts are order independent, so the selected SET is
-//     fixed regardless of atomic ordering.
-//  4. The k winners go to LDS as 64-bit (key << 32 | ~j) and a bitonic sort
-//     (descending) puts them in the canonical order, which is unique.
+// One workgroup per row. Rows up to 16384 keys are read from HBM once and
+// stay in VGPRs (V values per thread, j = tid + BLOCK*v); longer rows are
+// streamed again for each pass. Scores become order-preserving u32 keys
+// (-0.0 folded to +0.0); key 0 marks a slot past the row's end.
+//
+//  A. An LDS histogram of the top 11 key bits (sign, exponent, 2 mantissa
+//     bits) and one wave's scan give the bucket b* that holds the k-th
+//     largest key, the count above it and the count in it.
+//  B. One sweep appends every key above b* to the selection and every key
+//     in b* to an LDS candidate list; slots come from wave ballots and one
+//     block-wide scan of the wave totals (no per-element atomics).
+//  C. The rest of the threshold is found on the short candidate list only:
+//     radix passes over key bits 20..10 and 9..0, then, for ties on the full
+//     key, over j ascending (lower j wins). Histogram counts do not depend on
+//     atomic order, so the selected SET is fixed.
+//     If b* holds more keys than the list can take (heavy ties), the same
+//     passes run over the registers instead.
+//  D. The selection is sorted by (key << 32 | ~j), descending: 64-entry runs
+//     by a bitonic network across the lanes of a wave, then pairwise merges
+//     in which each entry's slot comes from a binary search in the other run.
 #include <algorithm>
 
 #include "xk_internal.h"
@@ -27,34 +33,59 @@
 namespace xk {
 namespace {
 
+constexpr int kBins = 2048;  // 11-bit digits
+
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;                     // -0.0 ties with +0.0
+  if (u == 0x80000000u) u = 0u;  // -0.0 ties with +0.0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+__device__ __forceinline__ int lane_id() { return int(threadIdx.x & 63); }
+
+__device__ __forceinline__ int prefix_in_wave(uint64_t mask) {
+  return __popcll(mask & ((uint64_t(1) << lane_id()) - 1));
+}
+
+template <int BLOCK, int CAP>
 struct TopkShared {
-  uint32_t hist[256];
-  uint64_t cand[kMaxTopk];
-  int digit;       // digit found by the scan
-  int above;       // count of matching keys in digits past `digit`
-  int at;          // count of matching keys in `digit`
-  int cnt;         // compaction cursor
+  __attribute__((aligned(16))) uint32_t hist[kBins];
+  uint64_t sel[kMaxTopk];
+  union {
+    struct {
+      uint32_t ckey[CAP];  // candidate list: keys in the threshold bucket
+      uint32_t cj[CAP];    // ... and their positions
+    };
+    uint64_t sel2[kMaxTopk];  // merge-round buffer (the list is dead by then)
+  };
+  int wsel[BLOCK / 64], wcand[BLOCK / 64];
+  int digit, above, at;
 };
 
-// Wave 0 scans hist[] for the bucket holding the `need`-th element, counting
-// from the top digit down (descending) or from digit 0 up (ascending).
-__device__ void find_digit(TopkShared& sh, int need, bool descending) {
-  const int lane = threadIdx.x;  // only wave 0 calls this
-  int c[4];
+// Wave 0: find the bin that holds the `need`-th element of hist[0..NBINS),
+// counted from the top bin down (descending) or from bin 0 up. Each lane
+// loads its NBINS/64 consecutive bins with 128-bit LDS reads, so the scan
+// costs a few LDS round trips.
+template <int NBINS, int BLOCK, int CAP>
+__device__ __forceinline__ void find_bin(TopkShared<BLOCK, CAP>& sh, int need, bool descending) {
+  constexpr int PER = NBINS / 64;
+  static_assert(PER % 4 == 0, "bins per lane");
+  const int lane = lane_id();
+  // lane L covers scan positions [L*PER, L*PER+PER); descending scan position
+  // p is bin NBINS-1-p, so lane L's bins are the block ending at NBINS-L*PER
+  const int base = descending ? NBINS - (lane + 1) * PER : lane * PER;
+  uint32_t c[PER];
+#pragma unroll
+  for (int i = 0; i < PER / 4; ++i) {
+    const u32x4 q4 = *reinterpret_cast<const u32x4*>(&sh.hist[base + 4 * i]);
+    c[4 * i] = q4[0];
+    c[4 * i + 1] = q4[1];
+    c[4 * i + 2] = q4[2];
+    c[4 * i + 3] = q4[3];
+  }
   int s = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int bin = descending ? 255 - (4 * lane + i) : 4 * lane + i;
-    c[i] = int(sh.hist[bin]);
-    s += c[i];
-  }
-  // exclusive prefix over lanes in scan order
+  for (int i = 0; i < PER; ++i) s += int(c[i]);
   int incl = s;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -62,130 +93,376 @@ __device__ void find_digit(TopkShared& sh, int need, bool descending) {
     if (lane >= d) incl += t;
   }
   int before = incl - s;
+  if (before < need && incl >= need) {
+    int found = -1, f_above = 0, f_at = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (before < need && before + c[i] >= need) {
-      sh.digit = descending ? 255 - (4 * lane + i) : 4 * lane + i;
-      sh.above = before;
-      sh.at = c[i];
+    for (int o = 0; o < PER; ++o) {  // scan order within the lane's block
+      const int i = descending ? PER - 1 - o : o;
+      const int cnt = int(c[i]);
+      if (found < 0 && before + cnt >= need) {
+        found = base + i;
+        f_above = before;
+        f_at = cnt;
+      }
+      before += cnt;
     }
-    before += c[i];
+    sh.digit = found;
+    sh.above = f_above;
+    sh.at = f_at;
   }
 }
 
-template <int BLOCK, int V>
+template <int BLOCK, int CAP>
+__device__ __forceinline__ void clear_hist(TopkShared<BLOCK, CAP>& sh, int nbins) {
+  for (int i = threadIdx.x; i < nbins; i += BLOCK) sh.hist[i] = 0u;
+}
+
+// Append the flagged entries of a chunk (U per thread) to the selection and
+// to the candidate list with one block-wide scan: per-wave ballots give each
+// lane its slot, per-wave totals in LDS give each wave its base. The running
+// totals nsel / ncand stay in registers (uniform across the block).
+template <int BLOCK, int CAP, int U>
+__device__ __forceinline__ void compact(TopkShared<BLOCK, CAP>& sh, const uint32_t (&kv)[U],
+                                        const uint32_t (&jv)[U], const bool (&to_sel)[U],
+                                        const bool (&to_cand)[U], int& nsel, int& ncand) {
+  constexpr int NW = BLOCK / 64;
+  const int lane = lane_id(), wave = int(threadIdx.x) >> 6;
+  int ts = 0, tc = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    ts += __popcll(__ballot(to_sel[u]));
+    tc += __popcll(__ballot(to_cand[u]));
+  }
+  if (lane == 0) {
+    sh.wsel[wave] = ts;
+    sh.wcand[wave] = tc;
+  }
+  __syncthreads();
+  int bs = nsel, bc = ncand;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int a = sh.wsel[w], c = sh.wcand[w];
+    if (w < wave) {
+      bs += a;
+      bc += c;
+    }
+    nsel += a;
+    ncand += c;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t ms = __ballot(to_sel[u]), mc = __ballot(to_cand[u]);
+    if (to_sel[u]) {
+      const int pos = bs + prefix_in_wave(ms);
+      if (pos < kMaxTopk) sh.sel[pos] = (uint64_t(kv[u]) << 32) | uint64_t(~jv[u]);
+    }
+    if (to_cand[u]) {
+      const int pos = bc + prefix_in_wave(mc);
+      if (pos < CAP) {
+        sh.ckey[pos] = kv[u];
+        sh.cj[pos] = jv[u];
+      }
+    }
+    bs += __popcll(ms);
+    bc += __popcll(mc);
+  }
+  __syncthreads();  // wsel / wcand are rewritten by the next call
+}
+
+// Running threshold: a key is taken when (key >> shift) > thr, or equals thr
+// with j <= jcut. `need` is how many of the keys equal to thr (at this
+// resolution) are still to be taken.
+struct Cut {
+  int shift;
+  uint32_t thr;
+  uint32_t jcut;
+  int need;
+  bool settled;
+};
+
+// One radix pass over a source of (key, j): histogram of key bits
+// [sft, sft+width) among keys whose bits above sft+width equal cut.thr,
+// then refine the cut. `each(f)` calls f(key, j) for every element.
+template <int BLOCK, int CAP, typename Each>
+__device__ __forceinline__ void key_pass(TopkShared<BLOCK, CAP>& sh, Cut& cut, int sft, int width, Each each) {
+  const uint32_t hi_thr = cut.thr;
+  const int hi_shift = sft + width;
+  const uint32_t mask = (1u << width) - 1u;
+  clear_hist(sh, kBins);
+  __syncthreads();
+  each([&](uint32_t key, uint32_t) {
+    if (key != 0u && (hi_shift >= 32 || (key >> hi_shift) == hi_thr))
+      atomicAdd(&sh.hist[(key >> sft) & mask], 1u);
+  });
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    if (width == 11)
+      find_bin<2048>(sh, cut.need, true);
+    else
+      find_bin<1024>(sh, cut.need, true);
+  }
+  __syncthreads();
+  cut.thr = (hi_shift >= 32 ? 0u : (hi_thr << width)) | uint32_t(sh.digit);
+  cut.shift = sft;
+  cut.need -= sh.above;
+  cut.settled = sh.at == cut.need;
+  __syncthreads();
+}
+
+// Radix pass over j (ascending) among keys equal to `full` (shift 0).
+template <int BLOCK, int CAP, typename Each>
+__device__ __forceinline__ void j_pass(TopkShared<BLOCK, CAP>& sh, uint32_t full, uint32_t& jpre, int& need,
+                       int sft, int width, Each each) {
+  const int hi_shift = sft + width;
+  const uint32_t mask = (1u << width) - 1u;
+  clear_hist(sh, kBins);
+  __syncthreads();
+  each([&](uint32_t key, uint32_t j) {
+    if (key == full && (hi_shift >= 32 || (j >> hi_shift) == jpre))
+      atomicAdd(&sh.hist[(j >> sft) & mask], 1u);
+  });
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    if (width == 11)
+      find_bin<2048>(sh, need, false);
+    else
+      find_bin<1024>(sh, need, false);
+  }
+  __syncthreads();
+  jpre = (hi_shift >= 32 ? 0u : (jpre << width)) | uint32_t(sh.digit);
+  need -= sh.above;
+  __syncthreads();
+}
+
+// Finish a cut over a source: remaining key bits below cut.shift, then j.
+template <int BLOCK, int CAP, typename Each>
+__device__ __forceinline__ void finish_cut(TopkShared<BLOCK, CAP>& sh, Cut& cut, Each each) {
+  if (!cut.settled && cut.shift == 21) key_pass(sh, cut, 10, 11, each);
+  if (!cut.settled && cut.shift == 10) key_pass(sh, cut, 0, 10, each);
+  if (!cut.settled) {  // ties on the full key: the `need` lowest j
+    uint32_t jpre = 0u;
+    int need = cut.need;
+    j_pass(sh, cut.thr, jpre, need, 21, 11, each);
+    j_pass(sh, cut.thr, jpre, need, 10, 11, each);
+    j_pass(sh, cut.thr, jpre, need, 0, 10, each);
+    cut.jcut = jpre;
+  }
+}
+
+__device__ __forceinline__ bool taken(const Cut& c, uint32_t key, uint32_t j) {
+  const uint32_t h = key >> c.shift;
+  return key != 0u && (h > c.thr || (h == c.thr && j <= c.jcut));
+}
+
+// Sorts one 64-entry run held one per lane, descending (bitonic network
+// across the lanes of a wave).
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int sz = 2; sz <= 64; sz <<= 1) {
+#pragma unroll
+    for (int s = sz >> 1; s > 0; s >>= 1) {
+      const uint64_t o = __shfl_xor(x, s);
+      const bool desc = (lane & sz) == 0;
+      const bool lower = (lane & s) == 0;
+      const uint64_t hi = x > o ? x : o, lo = x > o ? o : x;
+      x = (lower == desc) ? hi : lo;
+    }
+  }
+  return x;
+}
+
+// Number of entries of the descending run a[0..L) that are > x (or >= x).
+template <bool OR_EQUAL>
+__device__ __forceinline__ int count_before(const uint64_t* a, int L, uint64_t x) {
+  int pos = 0;
+  for (int step = L >> 1; step > 0; step >>= 1) {
+    const uint64_t y = a[pos + step - 1];
+    if (OR_EQUAL ? y >= x : y > x) pos += step;
+  }
+  const uint64_t last = a[L - 1];
+  if (pos == L - 1 && (OR_EQUAL ? last >= x : last > x)) pos = L;
+  return pos;
+}
+
+// Sort sh.sel[0..m) descending (m <= kMaxTopk) and write the row:
+// 64-entry runs are sorted inside waves, then runs are merged pairwise; in a
+// merge every entry finds its slot as (its index in its run) + (entries of
+// the partner run that precede it), by binary search. Entries are distinct
+// except the zero padding, which the left run places first.
+template <int BLOCK, int CAP>
+__device__ __forceinline__ void sort_and_store(TopkShared<BLOCK, CAP>& sh, int m, int32_t* orow,
+                                               int k) {
+  constexpr int NW = BLOCK / 64;
+  const int lane = lane_id(), wave = int(threadIdx.x) >> 6;
+  int runs = (m + 63) >> 6;
+  int P = 1;
+  while (P < runs) P <<= 1;  // runs padded to a power of two
+  const int N = P * 64;
+  for (int r = wave; r < P; r += NW) {
+    const int i = r * 64 + lane;
+    const uint64_t x = i < m ? sh.sel[i] : 0ull;
+    sh.sel[i] = wave_sort_desc(x);
+  }
+  __syncthreads();
+  uint64_t* src = sh.sel;
+  uint64_t* dst = sh.sel2;
+  for (int L = 64; L < N; L <<= 1) {
+    for (int i = threadIdx.x; i < N; i += BLOCK) {
+      const uint64_t x = src[i];
+      const int run = i / L, own = i % L;
+      const int base = (run & ~1) * L;
+      const uint64_t* partner = src + (run ^ 1) * L;
+      const int c = (run & 1) ? count_before<true>(partner, L, x)
+                              : count_before<false>(partner, L, x);
+      dst[base + own + c] = x;
+    }
+    __syncthreads();
+    uint64_t* t = src;
+    src = dst;
+    dst = t;
+  }
+  for (int p = threadIdx.x; p < k; p += BLOCK)
+    orow[p] = p < m ? int32_t(~uint32_t(src[p] & 0xFFFFFFFFull)) : -1;
+}
+
+// V > 0: the row lives in V registers per thread (j = tid + BLOCK*v).
+// V == 0: long rows; every pass streams the row from memory again (the first
+// read comes from HBM, later ones mostly from L2 / the last-level cache).
+template <int BLOCK, int V, int CAP>
 __global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ logits,
                                                      const int32_t* __restrict__ limit,
                                                      int32_t* __restrict__ idx, int K, int k) {
-  __shared__ TopkShared sh;
+  __shared__ TopkShared<BLOCK, CAP> sh;
+  constexpr int U = V > 0 ? V : 8;  // entries per thread per chunk
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int n = limit ? max(0, min(limit[row], K - 1) + 1) : K;
   const float* x = logits + row * K;
 
-  uint32_t key[V];
+  uint32_t key[V > 0 ? V : 1];
+  if constexpr (V > 0) {
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int j = tid + BLOCK * v;
-    key[v] = j < n ? order_key(x[j]) : 0u;
+    for (int v = 0; v < V; ++v) {
+      const int j = tid + BLOCK * v;
+      key[v] = j < n ? order_key(x[j]) : 0u;
+    }
   }
+  // g(kv[U], jv[U]) over the row in chunks of BLOCK*U; every thread runs the
+  // same number of chunks (slots past n carry key 0)
+  auto chunks = [&](auto g) {
+    uint32_t kv[U], jv[U];
+    if constexpr (V > 0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kv[u] = key[u];
+        jv[u] = uint32_t(tid + BLOCK * u);
+      }
+      g(kv, jv);
+    } else {
+      // the next chunk's loads are in flight while this chunk is processed
+      float cur[U], nxt[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = BLOCK * u + tid;
+        cur[u] = j < n ? x[j] : 0.f;
+      }
+      for (int base = 0; base < n; base += BLOCK * U) {
+        const int nb = base + BLOCK * U;
+        if (nb < n) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int j = nb + BLOCK * u + tid;
+            nxt[u] = j < n ? x[j] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = base + BLOCK * u + tid;
+          kv[u] = j < n ? order_key(cur[u]) : 0u;
+          jv[u] = uint32_t(j);
+        }
+        g(kv, jv);
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+      }
+    }
+  };
+  auto each_src = [&](auto f) {
+    chunks([&](const uint32_t (&kv)[U], const uint32_t (&jv)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) f(kv[u], jv[u]);
+    });
+  };
 
+  int nsel = 0, ncand = 0;
   const int m = min(k, n);
-  // selection rule: (key >> shift) > thr, or == thr with j <= jcut
-  int shift = 0;
-  uint32_t thr = 0u;  // with shift 0 and jcut max: take every valid key (n <= k)
-  int jcut = 0x7FFFFFFF;
   if (n > k) {
-    uint32_t prefix = 0u;
-    int need = k;
-    bool settled = false;
-    for (int pass = 0; pass < 4 && !settled; ++pass) {
-      const int sft = 24 - 8 * pass;
-      const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (sft + 8));
-      for (int i = tid; i < 256; i += BLOCK) sh.hist[i] = 0u;
-      __syncthreads();
+    // A: top 11 bits over the whole row
+    Cut cut{32, 0u, 0xFFFFFFFFu, k, false};
+    key_pass(sh, cut, 21, 11, each_src);
+    if (cut.settled || sh.at <= CAP) {
+      // B: above b* -> selection, in b* -> candidate list
+      const Cut bucket = cut;
+      chunks([&](const uint32_t (&kv)[U], const uint32_t (&jv)[U]) {
+        bool ts[U], tc[U];
 #pragma unroll
-      for (int v = 0; v < V; ++v)
-        if (key[v] != 0u && (key[v] & hi_mask) == prefix)
-          atomicAdd(&sh.hist[(key[v] >> sft) & 255u], 1u);
-      __syncthreads();
-      if (tid < 64) find_digit(sh, need, true);
-      __syncthreads();
-      prefix |= uint32_t(sh.digit) << sft;
-      need -= sh.above;
-      shift = sft;
-      thr = prefix >> sft;
-      settled = sh.at == need;  // the whole bucket is taken
-      __syncthreads();          // sh.* read by all before the next pass rewrites it
-    }
-    if (!settled) {
-      // ties on the full key: the `need` lowest j among key == prefix
-      uint32_t jprefix = 0u;
-      for (int pass = 0; pass < 4; ++pass) {
-        const int sft = 24 - 8 * pass;
-        const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (sft + 8));
-        for (int i = tid; i < 256; i += BLOCK) sh.hist[i] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-          const uint32_t j = uint32_t(tid + BLOCK * v);
-          if (key[v] == prefix && (j & hi_mask) == jprefix)
-            atomicAdd(&sh.hist[(j >> sft) & 255u], 1u);
+        for (int u = 0; u < U; ++u) {
+          const uint32_t h = kv[u] >> 21;
+          const bool live = kv[u] != 0u;
+          ts[u] = live && (h > bucket.thr || (bucket.settled && h == bucket.thr));
+          tc[u] = live && !bucket.settled && h == bucket.thr;
         }
-        __syncthreads();
-        if (tid < 64) find_digit(sh, need, false);
-        __syncthreads();
-        jprefix |= uint32_t(sh.digit) << sft;
-        need -= sh.above;
-        __syncthreads();
-      }
-      jcut = int(jprefix);
-    }
-  }
-
-  if (tid == 0) sh.cnt = 0;
-  __syncthreads();
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int j = tid + BLOCK * v;
-    const uint32_t kk = key[v] >> shift;
-    if (key[v] != 0u && (kk > thr || (kk == thr && j <= jcut))) {
-      const int pos = atomicAdd(&sh.cnt, 1);
-      if (pos < kMaxTopk) sh.cand[pos] = (uint64_t(key[v]) << 32) | uint64_t(~uint32_t(j));
-    }
-  }
-  __syncthreads();
-
-  // bitonic sort (descending) of the m winners, padded to a power of two
-  int P = 1;
-  while (P < m) P <<= 1;
-  for (int i = m + tid; i < P; i += BLOCK) sh.cand[i] = 0ull;
-  __syncthreads();
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < (P >> 1); i += BLOCK) {
-        const int lo = 2 * stride * (i / stride) + (i % stride);
-        const int hi = lo + stride;
-        const bool desc = (lo & size) == 0;
-        const uint64_t a = sh.cand[lo], c = sh.cand[hi];
-        if (desc ? (a < c) : (a > c)) {
-          sh.cand[lo] = c;
-          sh.cand[hi] = a;
+        compact(sh, kv, jv, ts, tc, nsel, ncand);
+      });
+      if (!cut.settled) {
+        // C: finish the cut on the candidate list
+        const int nc = ncand;
+        auto each_cand = [&](auto f) {
+          for (int i = tid; i < nc; i += BLOCK) f(sh.ckey[i], sh.cj[i]);
+        };
+        finish_cut(sh, cut, each_cand);
+        for (int base = 0; base < nc; base += BLOCK) {
+          const int i = base + tid;
+          const bool in = i < nc;
+          const uint32_t kv[1] = {in ? sh.ckey[i] : 0u}, jv[1] = {in ? sh.cj[i] : 0u};
+          const bool ts[1] = {in && taken(cut, kv[0], jv[0])}, tc[1] = {false};
+          int dummy = 0;
+          compact(sh, kv, jv, ts, tc, nsel, dummy);
         }
       }
-      __syncthreads();
+    } else {
+      // heavy ties in b*: finish the cut over the whole row, then select
+      finish_cut(sh, cut, each_src);
+      chunks([&](const uint32_t (&kv)[U], const uint32_t (&jv)[U]) {
+        bool ts[U], tc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          ts[u] = taken(cut, kv[u], jv[u]);
+          tc[u] = false;
+        }
+        compact(sh, kv, jv, ts, tc, nsel, ncand);
+      });
     }
+  } else {
+    chunks([&](const uint32_t (&kv)[U], const uint32_t (&jv)[U]) {
+      bool ts[U], tc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        ts[u] = kv[u] != 0u;
+        tc[u] = false;
+      }
+      compact(sh, kv, jv, ts, tc, nsel, ncand);
+    });
   }
-  int32_t* orow = idx + row * k;
-  for (int s = tid; s < k; s += BLOCK)
-    orow[s] = s < m ? int32_t(~uint32_t(sh.cand[s] & 0xFFFFFFFFull)) : -1;
+  sort_and_store(sh, m, idx + row * k, k);
 }
 
-template <int BLOCK, int V>
+template <int BLOCK, int V, int CAP>
 hipError_t launch_one(const float* logits, const int32_t* limit, int32_t* idx, int R, int K, int k,
                       hipStream_t stream) {
-  hipLaunchKernelGGL((topk_kernel<BLOCK, V>), dim3(unsigned(R)), dim3(BLOCK), 0, stream, logits,
-                     limit, idx, K, k);
+  hipLaunchKernelGGL((topk_kernel<BLOCK, V, CAP>), dim3(unsigned(R)), dim3(BLOCK), 0, stream,
+                     logits, limit, idx, K, k);
   return hipGetLastError();
 }
 
@@ -193,14 +470,11 @@ hipError_t launch_one(const float* logits, const int32_t* limit, int32_t* idx, i
 
 hipError_t launch_topk(const float* logits, const int32_t* limit, int32_t* idx, int R, int K,
                        int k, hipStream_t stream) {
-  if (K <= 256 * 4) return launch_one<256, 4>(logits, limit, idx, R, K, k, stream);
-  if (K <= 256 * 8) return launch_one<256, 8>(logits, limit, idx, R, K, k, stream);
-  if (K <= 256 * 16) return launch_one<256, 16>(logits, limit, idx, R, K, k, stream);
-  if (K <= 1024 * 8) return launch_one<1024, 8>(logits, limit, idx, R, K, k, stream);
-  if (K <= 1024 * 16) return launch_one<1024, 16>(logits, limit, idx, R, K, k, stream);
-  if (K <= 1024 * 32) return launch_one<1024, 32>(logits, limit, idx, R, K, k, stream);
-  if (K <= 1024 * 64) return launch_one<1024, 64>(logits, limit, idx, R, K, k, stream);
-  return launch_one<1024, 96>(logits, limit, idx, R, K, k, stream);
+  if (K <= 256 * 4) return launch_one<256, 4, 2048>(logits, limit, idx, R, K, k, stream);
+  if (K <= 256 * 16) return launch_one<256, 16, 2048>(logits, limit, idx, R, K, k, stream);
+  if (K <= 1024 * 8) return launch_one<1024, 8, 4096>(logits, limit, idx, R, K, k, stream);
+  if (K <= 1024 * 16) return launch_one<1024, 16, 4096>(logits, limit, idx, R, K, k, stream);
+  return launch_one<1024, 0, 4096>(logits, limit, idx, R, K, k, stream);
 }
 
 }  // namespace xk

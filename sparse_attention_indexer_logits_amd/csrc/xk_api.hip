@@ -107,7 +107,6 @@ XK_EXPORT xk_status xk_indexer_topk(const float* logits, const int32_t* limit, i
   if (!logits || !idx) return fail(XK_ERR_INVALID_ARGUMENT, "null logits or idx");
   if (R < 1 || K < 1 || k < 1) return fail(XK_ERR_INVALID_ARGUMENT, "R, K, k must be >= 1");
   if (k > xk::kMaxTopk) return fail(XK_ERR_UNSUPPORTED, "k above 2048");
-  if (K > xk::kMaxTopkRow) return fail(XK_ERR_UNSUPPORTED, "K above 98304");
   const size_t need = xk_indexer_topk_workspace_size(R, K, k);
   if (workspace_bytes < need || (need && !workspace))
     return fail(XK_ERR_INVALID_ARGUMENT, "workspace too small");

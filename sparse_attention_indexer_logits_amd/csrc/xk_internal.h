@@ -10,10 +10,10 @@ namespace xk {
 constexpr int kHeads = 64;     // DeepSeek-V4 index_n_heads
 constexpr int kHeadDim = 128;  // DeepSeek-V4 index_head_dim
 constexpr int kMaxTopk = 2048;
-constexpr int kMaxTopkRow = 98304;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;

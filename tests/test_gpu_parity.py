@@ -222,7 +222,8 @@ def _topk_case(xk, L, lim, k):
     return g
 
 
-@pytest.mark.parametrize("K", [1, 5, 300, 1024, 1025, 4096, 5000, 16384, 40000, 65536, 98304])
+@pytest.mark.parametrize("K", [1, 5, 300, 1024, 1025, 4096, 5000, 16384, 16385, 40000, 65536,
+                               98304, 150001])
 @pytest.mark.parametrize("k", [1, 16, 512, 1024, 2048])
 def test_topk_random_rows(xk, K, k):
     print(f"[parity] top-k random K={K} k={k}", flush=True)
