@@ -133,8 +133,9 @@ xk_status xk_indexer_topk(const float* logits, const int32_t* limit, int32_t* id
  *   row_seq     [R] int32       sequence of each row, or NULL (row r -> seq r,
  *                               requires R <= S)
  *   out         [R,k,D] bf16 bits (uint16), every element written
- *   bs must be a power of two, D must be 128, else XK_ERR_UNSUPPORTED;
- *   kv_fp4 must be 4-byte aligned and out 16-byte aligned.
+ *   bs must be a power of two, D must be 128, R*k and NB*bs must stay below
+ *   2^31, else XK_ERR_UNSUPPORTED; kv_fp4 must be 4-byte aligned and out
+ *   16-byte aligned.
  */
 xk_status xk_mxfp4_paged_gather(const uint8_t* kv_fp4, const uint8_t* kv_scale,
                                 const int32_t* block_table, const int32_t* sel_pos,

@@ -5,16 +5,19 @@
 // table, decode E2M1 nibbles times the E8M0 group scale 2^(b-127) with
 // 0xFF -> 0, write bf16; a slot with sel_pos < 0 gets a zero row.
 //
-// The decode builds the bf16 bit pattern with integer ops: an E2M1 magnitude
-// is 0.5, or (1 + m/2) * 2^(e-1), so times 2^(b-127) it is a bf16 with
-// biased exponent e-1+b (b-1 for code 1) and one mantissa bit; the only
-// non-normal outcomes are the two subnormal exponents (b <= 1) and overflow
-// to inf (exponent >= 255). No rounding ever happens.
+// Decode: an E2M1 magnitude is 0.5, or (1 + m/2) * 2^(e-1), so times
+// 2^(b-127) it is a bf16 with biased exponent e-1+b (b-1 for code 1) and one
+// mantissa bit; the only non-normal outcomes are the two subnormal exponents
+// (b <= 1) and overflow to inf (exponent >= 255). No rounding ever happens.
+// Scale bytes 2..252 use gfx950's scaled fp4->bf16 convert; the rest build
+// the bit pattern with integer ops.
 //
 // Work split: a 16-byte piece of output (8 elements) per thread and step; 16
-// consecutive threads write one 256-byte row, so stores are fully coalesced.
+// consecutive lanes write one 256-byte row, so stores are fully coalesced.
 // The store stream (256 B per slot) is ~80% of the bytes, so the kernel is
 // HBM-write bound; output uses non-temporal stores.
+#include <type_traits>
+
 #include "xk_internal.h"
 
 namespace xk {
@@ -33,60 +36,82 @@ __device__ __forceinline__ uint32_t e2m1_e8m0_to_bf16(uint32_t code, uint32_t sc
   return sign | ((2u + mant) << (biased + 5));
 }
 
-// Each thread owns kPer pieces spaced one grid apart and runs their
-// dependent loads (sel_pos -> block table -> nibbles + scale) side by side,
-// so kPer independent chains are in flight per thread.
-constexpr int kPer = 4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
+// Eight E2M1 elements (one dword, element 2i in the low nibble of byte i)
+// times one E8M0 scale byte -> eight bf16 (element 2i in the low half of
+// dword i). For scale bytes 2..252 every product is a normal bf16 and exact,
+// so the hardware scaled convert (2 elements per instruction, exact in that
+// range) is used; extreme bytes take the integer construction above.
+__device__ __forceinline__ u32x4 decode8(uint32_t nib, uint32_t sc) {
+  u32x4 v;
+  if (sc >= 2u && sc <= 252u) {
+    const float scale = __uint_as_float(sc << 23);  // 2^(sc-127), a normal float
+    v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(nib, scale, 0));
+    v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(nib, scale, 1));
+    v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(nib, scale, 2));
+    v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(nib, scale, 3));
+  } else {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t byte = (nib >> (8 * b)) & 0xFFu;
+      v[b] = e2m1_e8m0_to_bf16(byte & 0xFu, sc) | (e2m1_e8m0_to_bf16(byte >> 4, sc) << 16);
+    }
+  }
+  return v;
+}
+
+// A wave owns 4*STEPS consecutive slots. Lane l fetches sel_pos of slot l
+// and resolves it to a physical token (two dependent loads for the whole
+// wave); then STEPS steps each cover 4 slots x 16 pieces: the token index is
+// broadcast from its lane, all steps' nibble/scale loads are issued
+// together, and each step ends in one contiguous 1 KB store. Large outputs
+// use STEPS = 16 (fewer, longer waves); small ones fewer steps so there are
+// still thousands of waves.
+template <int STEPS>
 __global__ __launch_bounds__(256) void mxfp4_gather_kernel(
     const uint32_t* __restrict__ kv_fp4,   // [NB*bs, 16] dwords (64 B per token)
     const uint8_t* __restrict__ kv_scale,  // [NB*bs, 4]
     const int32_t* __restrict__ block_table, int MB,
     const int32_t* __restrict__ sel_pos, const int32_t* __restrict__ row_seq,
-    u32x4* __restrict__ out, int64_t n_pieces, int k, int bs_log2) {
-  const int64_t stride = int64_t(gridDim.x) * 256;
-  const int64_t first = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  int p[kPer];
-  int64_t blk[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int64_t piece = first + i * stride;
-    p[i] = piece < n_pieces ? sel_pos[piece >> 4] : -1;
-  }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    blk[i] = 0;
-    if (p[i] >= 0) {
-      const int64_t row = ((first + i * stride) >> 4) / k;
+    u32x4* __restrict__ out, int64_t n_slots, int k, int bs_log2) {
+  const int lane = threadIdx.x & 63;
+  const int64_t slot0 = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * (4 * STEPS);
+  if (slot0 >= n_slots) return;  // uniform per wave
+
+  // 1. this lane's slot -> physical token (-1: padded slot or past the end)
+  const int64_t s = slot0 + lane;
+  int tok = -1;
+  if (lane < 4 * STEPS && s < n_slots) {
+    const int p = sel_pos[s];
+    if (p >= 0) {
+      const int64_t row = s / k;
       const int seq = row_seq ? row_seq[row] : int(row);
-      blk[i] = block_table[int64_t(seq) * MB + (p[i] >> bs_log2)];
+      const int blk = block_table[int64_t(seq) * MB + (p >> bs_log2)];
+      tok = (blk << bs_log2) + (p & ((1 << bs_log2) - 1));
     }
   }
-  uint32_t nib[kPer], sc[kPer];
+  // 2. step `it` covers slots slot0 + 4*it + lane/16, piece lane%16
+  const int piece = lane & 15;
+  uint32_t nib[STEPS], sc[STEPS];
+  int tk[STEPS];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    nib[i] = 0u;
-    sc[i] = 0u;
-    if (p[i] >= 0) {
-      const int part = int((first + i * stride) & 15);  // elements [8*part, 8*part+8)
-      const int64_t token = (blk[i] << bs_log2) + (p[i] & ((1 << bs_log2) - 1));
-      nib[i] = kv_fp4[token * 16 + part];
-      sc[i] = kv_scale[token * 4 + (part >> 2)];
+  for (int it = 0; it < STEPS; ++it) {
+    tk[it] = __shfl(tok, 4 * it + (lane >> 4));
+    nib[it] = 0u;
+    sc[it] = 0u;
+    if (tk[it] >= 0) {
+      nib[it] = kv_fp4[int64_t(tk[it]) * 16 + piece];
+      sc[it] = kv_scale[int64_t(tk[it]) * 4 + (piece >> 2)];
     }
   }
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int64_t piece = first + i * stride;
-    if (piece >= n_pieces) break;
+  for (int it = 0; it < STEPS; ++it) {
+    const int64_t slot = slot0 + 4 * it + (lane >> 4);
+    if (slot >= n_slots) break;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (p[i] >= 0) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint32_t byte = (nib[i] >> (8 * b)) & 0xFFu;
-        v[b] = e2m1_e8m0_to_bf16(byte & 0xFu, sc[i]) | (e2m1_e8m0_to_bf16(byte >> 4, sc[i]) << 16);
-      }
-    }
-    __builtin_nontemporal_store(v, out + piece);
+    if (tk[it] >= 0) v = decode8(nib[it], sc[it]);
+    __builtin_nontemporal_store(v, out + slot * 16 + piece);
   }
 }
 
@@ -96,12 +121,23 @@ hipError_t launch_gather(const uint8_t* kv_fp4, const uint8_t* kv_scale,
                          const int32_t* block_table, const int32_t* sel_pos,
                          const int32_t* row_seq, uint16_t* out, int R, int k, int MB,
                          int bs, hipStream_t stream) {
-  const int64_t n_pieces = int64_t(R) * k * 16;
+  const int64_t n_slots = int64_t(R) * k;
   const int bs_log2 = __builtin_ctz(unsigned(bs));
-  const int64_t blocks = (n_pieces + 256 * kPer - 1) / (256 * kPer);
-  hipLaunchKernelGGL(mxfp4_gather_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream,
-                     reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale, block_table, MB,
-                     sel_pos, row_seq, reinterpret_cast<u32x4*>(out), n_pieces, k, bs_log2);
+  auto go = [&](auto steps_tag) {
+    constexpr int STEPS = decltype(steps_tag)::value;
+    const int64_t per_block = 4 * 4 * STEPS;  // 4 waves x 4*STEPS slots
+    const int64_t blocks = (n_slots + per_block - 1) / per_block;
+    hipLaunchKernelGGL(mxfp4_gather_kernel<STEPS>, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                       reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale, block_table, MB,
+                       sel_pos, row_seq, reinterpret_cast<u32x4*>(out), n_slots, k, bs_log2);
+  };
+  // aim for >= 4096 waves: 4*STEPS slots per wave
+  if (n_slots >= 4096 * 64)
+    go(std::integral_constant<int, 16>{});
+  else if (n_slots >= 4096 * 16)
+    go(std::integral_constant<int, 4>{});
+  else
+    go(std::integral_constant<int, 1>{});
   return hipGetLastError();
 }
 

@@ -7,9 +7,10 @@
 // min(k, n) largest scores ordered by (score desc, j asc), then -1 padding.
 //
 // One workgroup per row. Rows up to 16384 keys are read from HBM once and
-// stay in VGPRs (V values per thread, j = tid + BLOCK*v); longer rows are
-// streamed again for each pass. Scores become order-preserving u32 keys
-// (-0.0 folded to +0.0); key 0 marks a slot past the row's end.
+// stay in VGPRs (V values per thread, j = tid + BLOCK*v); longer rows keep a
+// 32768-key prefix in VGPRs and stream the rest once (topk_long_kernel).
+// Scores become order-preserving u32 keys (-0.0 folded to +0.0); key 0 marks
+// a slot past the row's end.
 //
 //  A. An LDS histogram of the top 11 key bits (sign, exponent, 2 mantissa
 //     bits) and one wave's scan give the bucket b* that holds the k-th
@@ -60,6 +61,9 @@ struct TopkShared {
   };
   int wsel[BLOCK / 64], wcand[BLOCK / 64];
   int digit, above, at;
+  int ccount;       // streamed candidate list: entries claimed so far
+  int overflow;     // 1 if the streamed list ran out of room
+  uint32_t tau;     // smallest key of the prefix selection
 };
 
 // Wave 0: find the bin that holds the `need`-th element of hist[0..NBINS),
@@ -117,21 +121,23 @@ __device__ __forceinline__ void clear_hist(TopkShared<BLOCK, CAP>& sh, int nbins
   for (int i = threadIdx.x; i < nbins; i += BLOCK) sh.hist[i] = 0u;
 }
 
-// Append the flagged entries of a chunk (U per thread) to the selection and
-// to the candidate list with one block-wide scan: per-wave ballots give each
-// lane its slot, per-wave totals in LDS give each wave its base. The running
-// totals nsel / ncand stay in registers (uniform across the block).
-template <int BLOCK, int CAP, int U>
-__device__ __forceinline__ void compact(TopkShared<BLOCK, CAP>& sh, const uint32_t (&kv)[U],
-                                        const uint32_t (&jv)[U], const bool (&to_sel)[U],
-                                        const bool (&to_cand)[U], int& nsel, int& ncand) {
+// Append entries of a chunk (U per thread) to the selection (pred == 1) or
+// to the candidate list (pred == 2) with one block-wide scan: per-wave
+// ballots give each lane its slot, per-wave totals in LDS give each wave its
+// base. key_at(u) / j_at(u) give entry u; the predicate is evaluated again
+// in the writing sweep instead of being stored. The running totals nsel /
+// ncand stay in registers (uniform across the block).
+template <int BLOCK, int CAP, int U, typename KeyAt, typename JAt, typename Pred>
+__device__ __forceinline__ void compact(TopkShared<BLOCK, CAP>& sh, KeyAt key_at, JAt j_at,
+                                        Pred pred, int& nsel, int& ncand) {
   constexpr int NW = BLOCK / 64;
   const int lane = lane_id(), wave = int(threadIdx.x) >> 6;
   int ts = 0, tc = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    ts += __popcll(__ballot(to_sel[u]));
-    tc += __popcll(__ballot(to_cand[u]));
+    const int c = pred(key_at(u), j_at(u));
+    ts += __popcll(__ballot(c == 1));
+    tc += __popcll(__ballot(c == 2));
   }
   if (lane == 0) {
     sh.wsel[wave] = ts;
@@ -151,16 +157,17 @@ __device__ __forceinline__ void compact(TopkShared<BLOCK, CAP>& sh, const uint32
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint64_t ms = __ballot(to_sel[u]), mc = __ballot(to_cand[u]);
-    if (to_sel[u]) {
+    const uint32_t kv = key_at(u), jv = j_at(u);
+    const int c = pred(kv, jv);
+    const uint64_t ms = __ballot(c == 1), mc = __ballot(c == 2);
+    if (c == 1) {
       const int pos = bs + prefix_in_wave(ms);
-      if (pos < kMaxTopk) sh.sel[pos] = (uint64_t(kv[u]) << 32) | uint64_t(~jv[u]);
-    }
-    if (to_cand[u]) {
+      if (pos < kMaxTopk) sh.sel[pos] = (uint64_t(kv) << 32) | uint64_t(~jv);
+    } else if (c == 2) {
       const int pos = bc + prefix_in_wave(mc);
       if (pos < CAP) {
-        sh.ckey[pos] = kv[u];
-        sh.cj[pos] = jv[u];
+        sh.ckey[pos] = kv;
+        sh.cj[pos] = jv;
       }
     }
     bs += __popcll(ms);
@@ -326,77 +333,22 @@ __device__ __forceinline__ void sort_and_store(TopkShared<BLOCK, CAP>& sh, int m
     orow[p] = p < m ? int32_t(~uint32_t(src[p] & 0xFFFFFFFFull)) : -1;
 }
 
-// V > 0: the row lives in V registers per thread (j = tid + BLOCK*v).
-// V == 0: long rows; every pass streams the row from memory again (the first
-// read comes from HBM, later ones mostly from L2 / the last-level cache).
-template <int BLOCK, int V, int CAP>
-__global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ logits,
-                                                     const int32_t* __restrict__ limit,
-                                                     int32_t* __restrict__ idx, int K, int k) {
-  __shared__ TopkShared<BLOCK, CAP> sh;
-  constexpr int U = V > 0 ? V : 8;  // entries per thread per chunk
-  const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const int n = limit ? max(0, min(limit[row], K - 1) + 1) : K;
-  const float* x = logits + row * K;
-
-  uint32_t key[V > 0 ? V : 1];
-  if constexpr (V > 0) {
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const int j = tid + BLOCK * v;
-      key[v] = j < n ? order_key(x[j]) : 0u;
-    }
-  }
-  // g(kv[U], jv[U]) over the row in chunks of BLOCK*U; every thread runs the
-  // same number of chunks (slots past n carry key 0)
-  auto chunks = [&](auto g) {
-    uint32_t kv[U], jv[U];
-    if constexpr (V > 0) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        kv[u] = key[u];
-        jv[u] = uint32_t(tid + BLOCK * u);
-      }
-      g(kv, jv);
-    } else {
-      // the next chunk's loads are in flight while this chunk is processed
-      float cur[U], nxt[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = BLOCK * u + tid;
-        cur[u] = j < n ? x[j] : 0.f;
-      }
-      for (int base = 0; base < n; base += BLOCK * U) {
-        const int nb = base + BLOCK * U;
-        if (nb < n) {
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const int j = nb + BLOCK * u + tid;
-            nxt[u] = j < n ? x[j] : 0.f;
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int j = base + BLOCK * u + tid;
-          kv[u] = j < n ? order_key(cur[u]) : 0u;
-          jv[u] = uint32_t(j);
-        }
-        g(kv, jv);
-#pragma unroll
-        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-      }
-    }
-  };
+// Select the min(k, n) winners of a row into sh.sel (unsorted; nsel counts
+// them). `chunks(g)` calls g(key_at, j_at) per chunk of BLOCK*U entries,
+// with key_at(u) / j_at(u) giving this thread's entry u (key 0 = no entry)
+// and the same number of chunks on every thread.
+template <int BLOCK, int CAP, int U, typename Chunks>
+__device__ __forceinline__ void select_row(TopkShared<BLOCK, CAP>& sh, int n, int k, Chunks chunks,
+                                           int& nsel) {
   auto each_src = [&](auto f) {
-    chunks([&](const uint32_t (&kv)[U], const uint32_t (&jv)[U]) {
+    chunks([&](auto key_at, auto j_at) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) f(kv[u], jv[u]);
+      for (int u = 0; u < U; ++u) f(key_at(u), j_at(u));
     });
   };
-
-  int nsel = 0, ncand = 0;
-  const int m = min(k, n);
+  const int tid = threadIdx.x;
+  int ncand = 0;
+  auto one = [](int) { return 0; };
   if (n > k) {
     // A: top 11 bits over the whole row
     Cut cut{32, 0u, 0xFFFFFFFFu, k, false};
@@ -404,16 +356,13 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ l
     if (cut.settled || sh.at <= CAP) {
       // B: above b* -> selection, in b* -> candidate list
       const Cut bucket = cut;
-      chunks([&](const uint32_t (&kv)[U], const uint32_t (&jv)[U]) {
-        bool ts[U], tc[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const uint32_t h = kv[u] >> 21;
-          const bool live = kv[u] != 0u;
-          ts[u] = live && (h > bucket.thr || (bucket.settled && h == bucket.thr));
-          tc[u] = live && !bucket.settled && h == bucket.thr;
-        }
-        compact(sh, kv, jv, ts, tc, nsel, ncand);
+      chunks([&](auto key_at, auto j_at) {
+        compact<BLOCK, CAP, U>(sh, key_at, j_at, [&](uint32_t kv, uint32_t) {
+          const uint32_t h = kv >> 21;
+          if (kv == 0u) return 0;
+          if (h > bucket.thr || (bucket.settled && h == bucket.thr)) return 1;
+          return (!bucket.settled && h == bucket.thr) ? 2 : 0;
+        }, nsel, ncand);
       });
       if (!cut.settled) {
         // C: finish the cut on the candidate list
@@ -425,37 +374,201 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ l
         for (int base = 0; base < nc; base += BLOCK) {
           const int i = base + tid;
           const bool in = i < nc;
-          const uint32_t kv[1] = {in ? sh.ckey[i] : 0u}, jv[1] = {in ? sh.cj[i] : 0u};
-          const bool ts[1] = {in && taken(cut, kv[0], jv[0])}, tc[1] = {false};
+          const uint32_t ck = in ? sh.ckey[i] : 0u, cj = in ? sh.cj[i] : 0u;
           int dummy = 0;
-          compact(sh, kv, jv, ts, tc, nsel, dummy);
+          compact<BLOCK, CAP, 1>(sh, [&](int) { return ck; }, [&](int) { return cj; },
+                                 [&](uint32_t kv, uint32_t jv) { return taken(cut, kv, jv) ? 1 : 0; },
+                                 nsel, dummy);
         }
       }
     } else {
       // heavy ties in b*: finish the cut over the whole row, then select
       finish_cut(sh, cut, each_src);
-      chunks([&](const uint32_t (&kv)[U], const uint32_t (&jv)[U]) {
-        bool ts[U], tc[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          ts[u] = taken(cut, kv[u], jv[u]);
-          tc[u] = false;
-        }
-        compact(sh, kv, jv, ts, tc, nsel, ncand);
+      chunks([&](auto key_at, auto j_at) {
+        compact<BLOCK, CAP, U>(sh, key_at, j_at,
+                               [&](uint32_t kv, uint32_t jv) { return taken(cut, kv, jv) ? 1 : 0; },
+                               nsel, ncand);
       });
     }
   } else {
-    chunks([&](const uint32_t (&kv)[U], const uint32_t (&jv)[U]) {
-      bool ts[U], tc[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        ts[u] = kv[u] != 0u;
-        tc[u] = false;
-      }
-      compact(sh, kv, jv, ts, tc, nsel, ncand);
+    __syncthreads();
+    chunks([&](auto key_at, auto j_at) {
+      compact<BLOCK, CAP, U>(sh, key_at, j_at, [](uint32_t kv, uint32_t) { return kv != 0u ? 1 : 0; },
+                             nsel, ncand);
     });
   }
-  sort_and_store(sh, m, idx + row * k, k);
+  (void)one;
+}
+
+// Append a list (entries [0, nc) of ckey/cj) to the selection: the k winners
+// when nc > k, else all of them.
+template <int BLOCK, int CAP>
+__device__ __forceinline__ void select_list(TopkShared<BLOCK, CAP>& sh, int nc, int k, int& nsel) {
+  const int tid = threadIdx.x;
+  auto each_list = [&](auto f) {
+    for (int i = tid; i < nc; i += BLOCK) f(sh.ckey[i], sh.cj[i]);
+  };
+  Cut cut{0, 0u, 0xFFFFFFFFu, 0, true};  // takes every entry
+  if (nc > k) {
+    cut = Cut{32, 0u, 0xFFFFFFFFu, k, false};
+    key_pass(sh, cut, 21, 11, each_list);
+    finish_cut(sh, cut, each_list);
+  }
+  for (int base = 0; base < nc; base += BLOCK) {
+    const int i = base + tid;
+    const bool in = i < nc;
+    const uint32_t ck = in ? sh.ckey[i] : 0u, cj = in ? sh.cj[i] : 0u;
+    int dummy = 0;
+    compact<BLOCK, CAP, 1>(sh, [&](int) { return ck; }, [&](int) { return cj; },
+                           [&](uint32_t kv, uint32_t jv) { return in && taken(cut, kv, jv) ? 1 : 0; },
+                           nsel, dummy);
+  }
+}
+
+// chunks(g) over entries [j_lo, j_hi) of x streamed from memory, BLOCK*U per
+// chunk, the next chunk's loads in flight while this one is processed.
+template <int BLOCK, int U, typename G>
+__device__ __forceinline__ void stream_chunks(const float* __restrict__ x, int j_lo, int j_hi, G g) {
+  const int tid = threadIdx.x;
+  uint32_t kv[U];
+  float cur[U], nxt[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = j_lo + BLOCK * u + tid;
+    cur[u] = j < j_hi ? x[j] : 0.f;
+    nxt[u] = 0.f;
+  }
+  for (int base = j_lo; base < j_hi; base += BLOCK * U) {
+    const int nb = base + BLOCK * U;
+    if (nb < j_hi) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = nb + BLOCK * u + tid;
+        nxt[u] = j < j_hi ? x[j] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = base + BLOCK * u + tid;
+      kv[u] = j < j_hi ? order_key(cur[u]) : 0u;
+    }
+    g([&](int u) { return kv[u]; }, [&](int u) { return uint32_t(base + BLOCK * u + tid); });
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+  }
+}
+
+// Rows of at most BLOCK*V keys: the row is read once into V registers per
+// thread (j = tid + BLOCK*v).
+template <int BLOCK, int V, int CAP>
+__global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ logits,
+                                                     const int32_t* __restrict__ limit,
+                                                     int32_t* __restrict__ idx, int K, int k) {
+  __shared__ TopkShared<BLOCK, CAP> sh;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int n = limit ? max(0, min(limit[row], K - 1) + 1) : K;
+  const float* x = logits + row * K;
+  uint32_t key[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int j = tid + BLOCK * v;
+    key[v] = j < n ? order_key(x[j]) : 0u;
+  }
+  auto chunks = [&](auto g) {
+    g([&](int v) { return key[v]; }, [&](int v) { return uint32_t(tid + BLOCK * v); });
+  };
+  int nsel = 0;
+  select_row<BLOCK, CAP, V>(sh, n, k, chunks, nsel);
+  sort_and_store(sh, min(k, n), idx + row * k, k);
+}
+
+// Longer rows. The first BLOCK*V keys are held in registers and selected
+// exactly; the smallest selected key tau is a lower bound of the row's k-th
+// largest key (a prefix's k-th largest cannot exceed the row's). The rest of
+// the row is streamed once and only keys > tau join an LDS candidate list
+// (a key equal to tau arrives with a larger j than every kept one, so it can
+// never win). The winners are then selected exactly from prefix-selection +
+// candidates. If the list runs out of room (only for adversarial rows), the
+// row falls back to multi-pass streaming selection over the whole row.
+template <int BLOCK, int V, int CAP>
+__global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restrict__ logits,
+                                                          const int32_t* __restrict__ limit,
+                                                          int32_t* __restrict__ idx, int K, int k) {
+  constexpr int U = 8;  // streamed entries per thread per chunk
+  __shared__ TopkShared<BLOCK, CAP> sh;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int64_t row = blockIdx.x;
+  const int n = limit ? max(0, min(limit[row], K - 1) + 1) : K;
+  const int prefix = min(n, BLOCK * V);
+  const float* x = logits + row * K;
+  uint32_t key[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int j = tid + BLOCK * v;
+    key[v] = j < prefix ? order_key(x[j]) : 0u;
+  }
+  auto reg_chunks = [&](auto g) {
+    g([&](int v) { return key[v]; }, [&](int v) { return uint32_t(tid + BLOCK * v); });
+  };
+  int nsel = 0;
+  select_row<BLOCK, CAP, V>(sh, prefix, k, reg_chunks, nsel);
+
+  if (n > prefix) {
+    // move the prefix winners into the candidate list; tau = their smallest key
+    if (tid == 0) {
+      sh.tau = 0xFFFFFFFFu;
+      sh.ccount = nsel;
+      sh.overflow = 0;
+    }
+    __syncthreads();
+    uint32_t mn = 0xFFFFFFFFu;
+    for (int i = tid; i < nsel; i += BLOCK) {
+      const uint64_t e = sh.sel[i];
+      const uint32_t kv = uint32_t(e >> 32);
+      sh.ckey[i] = kv;
+      sh.cj[i] = ~uint32_t(e & 0xFFFFFFFFull);
+      mn = min(mn, kv);
+    }
+    for (int d = 32; d > 0; d >>= 1) mn = min(mn, uint32_t(__shfl_xor(int(mn), d)));
+    if (lane == 0) atomicMin(&sh.tau, mn);
+    __syncthreads();
+    const uint32_t tau = nsel == k ? sh.tau : 0u;  // fewer than k so far: take every key
+    // stream the rest once; keys above tau join the list (one atomic per wave)
+    stream_chunks<BLOCK, U>(x, prefix, n, [&](auto key_at, auto j_at) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t kv = key_at(u);
+        const bool take = kv > tau;
+        const uint64_t m = __ballot(take);
+        if (m == 0) continue;
+        const int leader = __ffsll((unsigned long long)m) - 1;
+        int base = 0;
+        if (lane == leader) base = atomicAdd(&sh.ccount, __popcll(m));
+        base = __shfl(base, leader);
+        if (take) {
+          const int pos = base + prefix_in_wave(m);
+          if (pos < CAP) {
+            sh.ckey[pos] = kv;
+            sh.cj[pos] = j_at(u);
+          } else {
+            sh.overflow = 1;
+          }
+        }
+      }
+    });
+    __syncthreads();
+    nsel = 0;
+    if (!sh.overflow) {
+      // exact selection over prefix winners + streamed candidates
+      select_list(sh, sh.ccount, k, nsel);
+    } else {
+      // fallback: multi-pass selection streaming the whole row
+      auto all_chunks = [&](auto g) { stream_chunks<BLOCK, U>(x, 0, n, g); };
+      select_row<BLOCK, CAP, U>(sh, n, k, all_chunks, nsel);
+    }
+  }
+  sort_and_store(sh, min(k, n), idx + row * k, k);
 }
 
 template <int BLOCK, int V, int CAP>
@@ -474,7 +587,9 @@ hipError_t launch_topk(const float* logits, const int32_t* limit, int32_t* idx, 
   if (K <= 256 * 16) return launch_one<256, 16, 2048>(logits, limit, idx, R, K, k, stream);
   if (K <= 1024 * 8) return launch_one<1024, 8, 4096>(logits, limit, idx, R, K, k, stream);
   if (K <= 1024 * 16) return launch_one<1024, 16, 4096>(logits, limit, idx, R, K, k, stream);
-  return launch_one<1024, 0, 4096>(logits, limit, idx, R, K, k, stream);
+  hipLaunchKernelGGL((topk_long_kernel<1024, 32, 6144>), dim3(unsigned(R)), dim3(1024), 0, stream,
+                     logits, limit, idx, K, k);
+  return hipGetLastError();
 }
 
 }  // namespace xk

@@ -131,6 +131,8 @@ XK_EXPORT xk_status xk_mxfp4_paged_gather(const uint8_t* kv_fp4, const uint8_t* 
     return fail(XK_ERR_INVALID_ARGUMENT, "kv_fp4 must be 4-byte and out 16-byte aligned");
   if (int64_t(R) * k > (int64_t(1) << 31) - 1)
     return fail(XK_ERR_UNSUPPORTED, "R*k above 2^31-1");
+  if (int64_t(NB) * bs > (int64_t(1) << 31) - 1)
+    return fail(XK_ERR_UNSUPPORTED, "NB*bs (cache tokens) above 2^31-1");
   xk_status s = check_device();
   if (s != XK_OK) return s;
   return launched(xk::launch_gather(kv_fp4, kv_scale, block_table, sel_pos, row_seq, out, R, k,

@@ -93,6 +93,7 @@ def test_topk_workspace_is_host_only(lib):
     ((FAKE, FAKE, FAKE, FAKE, None, FAKE, 3, 4, 2, 1, 1, 64, 128), 1, "R <= S"),
     ((FAKE + 1, FAKE, FAKE, FAKE, None, FAKE, 1, 4, 1, 1, 1, 64, 128), 1, "aligned"),
     ((FAKE, FAKE, FAKE, FAKE, None, FAKE + 4, 1, 4, 1, 1, 1, 64, 128), 1, "aligned"),
+    ((FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 4, 1, 1, 1 << 26, 64, 128), 2, "NB*bs"),
 ])
 def test_gather_validation(lib, args, status, needle):
     assert lib.xk_mxfp4_paged_gather(*args, None) == status
