@@ -24,10 +24,11 @@
 //     atomic order, so the selected SET is fixed.
 //     If b* holds more keys than the list can take (heavy ties), the same
 //     passes run over the registers instead.
-//  D. The selection is sorted by (key << 32 | ~j), descending: 64-entry runs
-//     by a bitonic network across the lanes of a wave, then pairwise merges
-//     in which each entry's slot comes from a binary search in the other run.
+//  D. The selection is sorted by (key << 32 | ~j), descending, with a
+//     counting sort on 2048 bins spanning its key range, then an exact rank
+//     among the few entries that share a bin.
 #include <algorithm>
+#include <type_traits>
 
 #include "xk_internal.h"
 
@@ -64,6 +65,7 @@ struct TopkShared {
   int ccount;       // streamed candidate list: entries claimed so far
   int overflow;     // 1 if the streamed list ran out of room
   uint32_t tau;     // smallest key of the prefix selection
+  uint32_t lo, hi;  // key range of the selection (sort)
 };
 
 // Wave 0: find the bin that holds the `need`-th element of hist[0..NBINS),
@@ -121,30 +123,46 @@ __device__ __forceinline__ void clear_hist(TopkShared<BLOCK, CAP>& sh, int nbins
   for (int i = threadIdx.x; i < nbins; i += BLOCK) sh.hist[i] = 0u;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
 // Append entries of a chunk (U per thread) to the selection (pred == 1) or
-// to the candidate list (pred == 2) with one block-wide scan: per-wave
-// ballots give each lane its slot, per-wave totals in LDS give each wave its
-// base. key_at(u) / j_at(u) give entry u; the predicate is evaluated again
-// in the writing sweep instead of being stored. The running totals nsel /
-// ncand stay in registers (uniform across the block).
+// to the candidate list (pred == 2). Each thread counts its hits, one wave
+// scan of the packed counts plus per-wave totals in LDS give every thread
+// its first slot, and each thread then writes only its own hits. key_at(u)
+// / j_at(u) give entry u; the predicate is evaluated once, into a 2-bit
+// class per entry. The running totals nsel / ncand stay in registers
+// (uniform across the block).
 template <int BLOCK, int CAP, int U, typename KeyAt, typename JAt, typename Pred>
 __device__ __forceinline__ void compact(TopkShared<BLOCK, CAP>& sh, KeyAt key_at, JAt j_at,
                                         Pred pred, int& nsel, int& ncand) {
   constexpr int NW = BLOCK / 64;
   const int lane = lane_id(), wave = int(threadIdx.x) >> 6;
-  int ts = 0, tc = 0;
+  static_assert(U <= 32, "2-bit class mask holds 32 entries");
+  using Mask = typename std::conditional<(U > 16), uint64_t, uint32_t>::type;
+  int packed = 0;  // selection hits in the low 16 bits, candidate hits above
+  Mask cls = 0u;   // 2 bits per entry: 1 = selection, 2 = candidate list
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int c = pred(key_at(u), j_at(u));
-    ts += __popcll(__ballot(c == 1));
-    tc += __popcll(__ballot(c == 2));
+    cls |= Mask(c) << (2 * u);
+    packed += c == 1 ? 1 : (c == 2 ? 0x10000 : 0);
   }
-  if (lane == 0) {
-    sh.wsel[wave] = ts;
-    sh.wcand[wave] = tc;
+  const int incl = wave_incl_scan(packed);
+  if (lane == 63) {
+    sh.wsel[wave] = incl & 0xFFFF;
+    sh.wcand[wave] = incl >> 16;
   }
   __syncthreads();
-  int bs = nsel, bc = ncand;
+  int bs = nsel + ((incl - packed) & 0xFFFF), bc = ncand + ((incl - packed) >> 16);
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     const int a = sh.wsel[w], c = sh.wcand[w];
@@ -155,23 +173,21 @@ __device__ __forceinline__ void compact(TopkShared<BLOCK, CAP>& sh, KeyAt key_at
     nsel += a;
     ncand += c;
   }
+  if (cls != 0u) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint32_t kv = key_at(u), jv = j_at(u);
-    const int c = pred(kv, jv);
-    const uint64_t ms = __ballot(c == 1), mc = __ballot(c == 2);
-    if (c == 1) {
-      const int pos = bs + prefix_in_wave(ms);
-      if (pos < kMaxTopk) sh.sel[pos] = (uint64_t(kv) << 32) | uint64_t(~jv);
-    } else if (c == 2) {
-      const int pos = bc + prefix_in_wave(mc);
-      if (pos < CAP) {
-        sh.ckey[pos] = kv;
-        sh.cj[pos] = jv;
+    for (int u = 0; u < U; ++u) {
+      const uint32_t c = uint32_t(cls >> (2 * u)) & 3u;
+      if (c == 1u) {
+        if (bs < kMaxTopk) sh.sel[bs] = (uint64_t(key_at(u)) << 32) | uint64_t(~j_at(u));
+        ++bs;
+      } else if (c == 2u) {
+        if (bc < CAP) {
+          sh.ckey[bc] = key_at(u);
+          sh.cj[bc] = j_at(u);
+        }
+        ++bc;
       }
     }
-    bs += __popcll(ms);
-    bc += __popcll(mc);
   }
   __syncthreads();  // wsel / wcand are rewritten by the next call
 }
@@ -261,82 +277,120 @@ __device__ __forceinline__ bool taken(const Cut& c, uint32_t key, uint32_t j) {
   return key != 0u && (h > c.thr || (h == c.thr && j <= c.jcut));
 }
 
-// Sorts one 64-entry run held one per lane, descending (bitonic network
-// across the lanes of a wave).
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int sz = 2; sz <= 64; sz <<= 1) {
-#pragma unroll
-    for (int s = sz >> 1; s > 0; s >>= 1) {
-      const uint64_t o = __shfl_xor(x, s);
-      const bool desc = (lane & sz) == 0;
-      const bool lower = (lane & s) == 0;
-      const uint64_t hi = x > o ? x : o, lo = x > o ? o : x;
-      x = (lower == desc) ? hi : lo;
-    }
-  }
-  return x;
-}
-
-// Number of entries of the descending run a[0..L) that are > x (or >= x).
-template <bool OR_EQUAL>
-__device__ __forceinline__ int count_before(const uint64_t* a, int L, uint64_t x) {
-  int pos = 0;
-  for (int step = L >> 1; step > 0; step >>= 1) {
-    const uint64_t y = a[pos + step - 1];
-    if (OR_EQUAL ? y >= x : y > x) pos += step;
-  }
-  const uint64_t last = a[L - 1];
-  if (pos == L - 1 && (OR_EQUAL ? last >= x : last > x)) pos = L;
-  return pos;
-}
-
-// Sort sh.sel[0..m) descending (m <= kMaxTopk) and write the row:
-// 64-entry runs are sorted inside waves, then runs are merged pairwise; in a
-// merge every entry finds its slot as (its index in its run) + (entries of
-// the partner run that precede it), by binary search. Entries are distinct
-// except the zero padding, which the left run places first.
+// Sort sh.sel[0..m) (entries key << 32 | ~j, all distinct) descending and
+// write the row's indices, -1 past m. Counting sort on adaptive bins: with
+// hi / lo the largest / smallest key, bin = (hi - key) >> shift, shift chosen
+// so the 2048 bins span [lo, hi]. Entries are scattered to their bin's slots
+// (slot order from atomics), then every entry counts the entries of its own
+// bin that precede it in (key desc, j asc) order and moves to that rank, so
+// the final order does not depend on the atomic order. Bins of selected
+// logits hold a handful of entries; equal keys share a bin.
 template <int BLOCK, int CAP>
 __device__ __forceinline__ void sort_and_store(TopkShared<BLOCK, CAP>& sh, int m, int32_t* orow,
                                                int k) {
-  constexpr int NW = BLOCK / 64;
-  const int lane = lane_id(), wave = int(threadIdx.x) >> 6;
-  int runs = (m + 63) >> 6;
-  int P = 1;
-  while (P < runs) P <<= 1;  // runs padded to a power of two
-  const int N = P * 64;
-  for (int r = wave; r < P; r += NW) {
-    const int i = r * 64 + lane;
-    const uint64_t x = i < m ? sh.sel[i] : 0ull;
-    sh.sel[i] = wave_sort_desc(x);
+  constexpr int PER = (kMaxTopk + BLOCK - 1) / BLOCK;  // entries per thread, at most
+  const int tid = threadIdx.x, lane = lane_id();
+  if (tid == 0) {
+    sh.lo = 0xFFFFFFFFu;
+    sh.hi = 0u;
+  }
+  clear_hist(sh, kBins);
+  __syncthreads();
+  uint64_t e[PER];
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int p = tid + BLOCK * i;
+    e[i] = 0ull;
+    if (BLOCK * i >= m) continue;  // uniform
+    e[i] = p < m ? sh.sel[p] : 0ull;
+    if (p < m) {
+      mn = min(mn, uint32_t(e[i] >> 32));
+      mx = max(mx, uint32_t(e[i] >> 32));
+    }
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    mn = min(mn, uint32_t(__shfl_xor(int(mn), d)));
+    mx = max(mx, uint32_t(__shfl_xor(int(mx), d)));
+  }
+  if (lane == 0 && m > 0) {
+    atomicMin(&sh.lo, mn);
+    atomicMax(&sh.hi, mx);
   }
   __syncthreads();
-  uint64_t* src = sh.sel;
-  uint64_t* dst = sh.sel2;
-  for (int L = 64; L < N; L <<= 1) {
-    for (int i = threadIdx.x; i < N; i += BLOCK) {
-      const uint64_t x = src[i];
-      const int run = i / L, own = i % L;
-      const int base = (run & ~1) * L;
-      const uint64_t* partner = src + (run ^ 1) * L;
-      const int c = (run & 1) ? count_before<true>(partner, L, x)
-                              : count_before<false>(partner, L, x);
-      dst[base + own + c] = x;
-    }
-    __syncthreads();
-    uint64_t* t = src;
-    src = dst;
-    dst = t;
+  const uint32_t hi = sh.hi;
+  const uint32_t range = m > 0 ? hi - sh.lo : 0u;
+  const int shift = (range >> 11) == 0u ? 0 : 32 - __clz(int(range >> 11));
+  int bin[PER], slot[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int p = tid + BLOCK * i;
+    bin[i] = 0;
+    slot[i] = 0;
+    if (BLOCK * i >= m) continue;  // uniform
+    bin[i] = int((hi - uint32_t(e[i] >> 32)) >> shift);
+    if (p < m) slot[i] = int(atomicAdd(&sh.hist[bin[i]], 1u));
   }
-  for (int p = threadIdx.x; p < k; p += BLOCK)
-    orow[p] = p < m ? int32_t(~uint32_t(src[p] & 0xFFFFFFFFull)) : -1;
+  __syncthreads();
+  // exclusive scan of the bin counts (one wave, 32 bins per lane) in place
+  if (tid < 64) {
+    constexpr int PB = kBins / 64;
+    uint32_t c[PB];
+#pragma unroll
+    for (int i = 0; i < PB / 4; ++i) {
+      const u32x4 q4 = *reinterpret_cast<const u32x4*>(&sh.hist[tid * PB + 4 * i]);
+      c[4 * i] = q4[0];
+      c[4 * i + 1] = q4[1];
+      c[4 * i + 2] = q4[2];
+      c[4 * i + 3] = q4[3];
+    }
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < PB; ++i) sum += int(c[i]);
+    int run = wave_incl_scan(sum) - sum;
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int ci = int(c[i]);
+      c[i] = uint32_t(run);
+      run += ci;
+    }
+#pragma unroll
+    for (int i = 0; i < PB / 4; ++i)
+      *reinterpret_cast<u32x4*>(&sh.hist[tid * PB + 4 * i]) =
+          u32x4{c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]};
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int p = tid + BLOCK * i;
+    if (BLOCK * i >= m) continue;  // uniform
+    if (p < m) sh.sel2[sh.hist[bin[i]] + slot[i]] = e[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int p = tid + BLOCK * i;
+    if (BLOCK * i >= m) continue;  // uniform
+    if (p < m) {
+      const int start = int(sh.hist[bin[i]]);
+      const int end = bin[i] + 1 < kBins ? int(sh.hist[bin[i] + 1]) : m;
+      int rank = 0;
+      for (int q = start; q < end; ++q) rank += sh.sel2[q] > e[i] ? 1 : 0;
+      sh.sel[start + rank] = e[i];
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < k; p += BLOCK)  // m may exceed k: the first k are the winners
+    orow[p] = p < m ? int32_t(~uint32_t(sh.sel[p] & 0xFFFFFFFFull)) : -1;
 }
 
-// Select the min(k, n) winners of a row into sh.sel (unsorted; nsel counts
-// them). `chunks(g)` calls g(key_at, j_at) per chunk of BLOCK*U entries,
-// with key_at(u) / j_at(u) giving this thread's entry u (key 0 = no entry)
-// and the same number of chunks on every thread.
+// Select the winners of a row into sh.sel, unsorted; nsel counts them. That
+// is min(k, n) entries, or, when the whole threshold bucket fits, every
+// entry at or above it (at least k), to be cut to k by the sort.
+// `chunks(g)` calls g(key_at, j_at) per chunk of BLOCK*U entries, with
+// key_at(u) / j_at(u) giving this thread's entry u (key 0 = no entry) and
+// the same number of chunks on every thread.
 template <int BLOCK, int CAP, int U, typename Chunks>
 __device__ __forceinline__ void select_row(TopkShared<BLOCK, CAP>& sh, int n, int k, Chunks chunks,
                                            int& nsel) {
@@ -348,12 +402,24 @@ __device__ __forceinline__ void select_row(TopkShared<BLOCK, CAP>& sh, int n, in
   };
   const int tid = threadIdx.x;
   int ncand = 0;
-  auto one = [](int) { return 0; };
   if (n > k) {
     // A: top 11 bits over the whole row
     Cut cut{32, 0u, 0xFFFFFFFFu, k, false};
     key_pass(sh, cut, 21, 11, each_src);
-    if (cut.settled || sh.at <= CAP) {
+    const int above = k - cut.need, at = sh.at;
+    if (!cut.settled && above + at <= kMaxTopk) {
+      // B': everything at or above b* goes to the selection; the sort orders
+      // it by (key desc, j asc) and the row keeps the first k, which is
+      // exactly the cut C would find
+      const uint32_t b = cut.thr;
+      chunks([&](auto key_at, auto j_at) {
+        compact<BLOCK, CAP, U>(sh, key_at, j_at,
+                               [&](uint32_t kv, uint32_t) { return kv != 0u && (kv >> 21) >= b ? 1 : 0; },
+                               nsel, ncand);
+      });
+      return;
+    }
+    if (cut.settled || at <= CAP) {
       // B: above b* -> selection, in b* -> candidate list
       const Cut bucket = cut;
       chunks([&](auto key_at, auto j_at) {
@@ -397,7 +463,6 @@ __device__ __forceinline__ void select_row(TopkShared<BLOCK, CAP>& sh, int n, in
                              nsel, ncand);
     });
   }
-  (void)one;
 }
 
 // Append a list (entries [0, nc) of ckey/cj) to the selection: the k winners
@@ -480,15 +545,16 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ l
   };
   int nsel = 0;
   select_row<BLOCK, CAP, V>(sh, n, k, chunks, nsel);
-  sort_and_store(sh, min(k, n), idx + row * k, k);
+  sort_and_store(sh, nsel, idx + row * k, k);
 }
 
 // Longer rows. The first BLOCK*V keys are held in registers and selected
-// exactly; the smallest selected key tau is a lower bound of the row's k-th
-// largest key (a prefix's k-th largest cannot exceed the row's). The rest of
-// the row is streamed once and only keys > tau join an LDS candidate list
-// (a key equal to tau arrives with a larger j than every kept one, so it can
-// never win). The winners are then selected exactly from prefix-selection +
+// (at least k winners, every prefix key >= their smallest key tau). tau is
+// a lower bound of the row's k-th largest key (a prefix's k-th largest
+// cannot exceed the row's). The rest of the row is streamed once and only
+// keys > tau join an LDS candidate list: a streamed key equal to tau has a
+// larger j than the kept prefix keys equal to tau, of which there are
+// enough, so it can never win. The winners are then selected exactly from prefix-selection +
 // candidates. If the list runs out of room (only for adversarial rows), the
 // row falls back to multi-pass streaming selection over the whole row.
 template <int BLOCK, int V, int CAP>
@@ -533,7 +599,7 @@ __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restric
     for (int d = 32; d > 0; d >>= 1) mn = min(mn, uint32_t(__shfl_xor(int(mn), d)));
     if (lane == 0) atomicMin(&sh.tau, mn);
     __syncthreads();
-    const uint32_t tau = nsel == k ? sh.tau : 0u;  // fewer than k so far: take every key
+    const uint32_t tau = nsel >= k ? sh.tau : 0u;  // fewer than k so far: take every key
     // stream the rest once; keys above tau join the list (one atomic per wave)
     stream_chunks<BLOCK, U>(x, prefix, n, [&](auto key_at, auto j_at) {
 #pragma unroll
@@ -568,7 +634,7 @@ __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restric
       select_row<BLOCK, CAP, U>(sh, n, k, all_chunks, nsel);
     }
   }
-  sort_and_store(sh, min(k, n), idx + row * k, k);
+  sort_and_store(sh, nsel, idx + row * k, k);
 }
 
 template <int BLOCK, int V, int CAP>
