@@ -8,10 +8,25 @@
 //
 // One workgroup per row. Rows up to 16384 keys are read from HBM once and
 // stay in VGPRs (V values per thread, j = tid + BLOCK*v); longer rows keep a
-// 32768-key prefix in VGPRs and stream the rest once (topk_long_kernel).
+// 24576-key prefix in VGPRs and stream the rest once (topk_long_kernel).
 // Scores become order-preserving u32 keys (-0.0 folded to +0.0); key 0 marks
 // a slot past the row's end.
 //
+// Bucket path (every row in practice):
+//  1. The block's finite score range [lo, hi] gives 2048 bins linear in the
+//     score; an LDS histogram of the row, and one wave's descending scan of
+//     it, give each bin's first output slot and the bin b* that holds the
+//     k-th largest score.
+//  2. Every entry in a bin >= b* is scattered to its bin's slots (atomic
+//     cursors); its final position is the bin's first slot plus the number
+//     of entries of its bin that precede it in (score desc, j asc) order,
+//     counted by comparison, so the result does not depend on atomic order.
+//     Positions below k are the output.
+// Bins linear in the score spread logits over hundreds of bins, so the
+// histogram atomics rarely collide and b* holds a handful of entries.
+//
+// Radix path (fallback when the bins at or above b* hold more than 2048
+// entries: scores crowded into one bin by heavy ties or far outliers):
 //  A. An LDS histogram of the top 11 key bits (sign, exponent, 2 mantissa
 //     bits) and one wave's scan give the bucket b* that holds the k-th
 //     largest key, the count above it and the count in it.
@@ -23,10 +38,10 @@
 //     key, over j ascending (lower j wins). Histogram counts do not depend on
 //     atomic order, so the selected SET is fixed.
 //     If b* holds more keys than the list can take (heavy ties), the same
-//     passes run over the registers instead.
+//     passes run over the row instead.
 //  D. The selection is sorted by (key << 32 | ~j), descending, with a
 //     counting sort on 2048 bins spanning its key range, then an exact rank
-//     among the few entries that share a bin.
+//     among the entries that share a bin.
 #include <algorithm>
 #include <type_traits>
 
@@ -52,7 +67,10 @@ __device__ __forceinline__ int prefix_in_wave(uint64_t mask) {
 template <int BLOCK, int CAP>
 struct TopkShared {
   __attribute__((aligned(16))) uint32_t hist[kBins];
-  uint64_t sel[kMaxTopk];
+  union {
+    uint64_t sel[kMaxTopk];                           // radix path: selection
+    __attribute__((aligned(16))) uint32_t cur[kBins];  // bucket path: scatter cursors
+  };
   union {
     struct {
       uint32_t ckey[CAP];  // candidate list: keys in the threshold bucket
@@ -61,6 +79,7 @@ struct TopkShared {
     uint64_t sel2[kMaxTopk];  // merge-round buffer (the list is dead by then)
   };
   int wsel[BLOCK / 64], wcand[BLOCK / 64];
+  uint32_t wlo[BLOCK / 64], whi[BLOCK / 64];  // per-wave finite key range
   int digit, above, at;
   int ccount;       // streamed candidate list: entries claimed so far
   int overflow;     // 1 if the streamed list ran out of room
@@ -465,6 +484,175 @@ __device__ __forceinline__ void select_row(TopkShared<BLOCK, CAP>& sh, int n, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Bucket path: one histogram both finds the threshold and orders the winners.
+
+// Score of an order key (inverse of order_key).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Keys of finite scores (-inf maps to 0x007FFFFF, +inf to 0xFF800000).
+__device__ __forceinline__ bool finite_key(uint32_t key) {
+  return key > 0x007FFFFFu && key < 0xFF800000u;
+}
+
+// Bin of a key, linear in the score over the row's finite range [lo, hi]
+// (s = kBins / (hi - lo)); +-inf clamp to the end bins. Subtraction,
+// multiplication by s >= 0 and truncation all preserve order, so a larger
+// key never lands in a lower bin, which is all the selection relies on.
+// s = 0 (no finite range) sends every finite key to bin 0.
+struct ValueBins {
+  float lo, s;
+  __device__ __forceinline__ int operator()(uint32_t key) const {
+    const float t = (key_value(key) - lo) * s;
+    return t >= float(kBins - 1) ? kBins - 1 : (t > 0.f ? int(t) : 0);
+  }
+};
+
+// Wave 0: turn the bin counts in hist into descending exclusive starts
+// (entries in higher bins), copied to cur as scatter cursors, and find the
+// threshold bin b*: the bin holding the need-th largest entry, need =
+// min(k, entries). Leaves sh.digit = b* and sh.at = entries in bins >= b*
+// (b* = kBins and 0 when there are no entries).
+template <int BLOCK, int CAP>
+__device__ __forceinline__ void scan_desc(TopkShared<BLOCK, CAP>& sh, int k) {
+  constexpr int PER = kBins / 64;
+  const int lane = lane_id();
+  const int base = kBins - (lane + 1) * PER;  // lane 0 holds the top bins
+  uint32_t c[PER];
+#pragma unroll
+  for (int i = 0; i < PER / 4; ++i) {
+    const u32x4 q4 = *reinterpret_cast<const u32x4*>(&sh.hist[base + 4 * i]);
+    c[4 * i] = q4[0];
+    c[4 * i + 1] = q4[1];
+    c[4 * i + 2] = q4[2];
+    c[4 * i + 3] = q4[3];
+  }
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sum += int(c[i]);
+  const int incl = wave_incl_scan(sum);
+  const int need = min(k, __shfl(incl, 63));
+  int run = incl - sum, found = -1, upto = 0;
+#pragma unroll
+  for (int o = 0; o < PER; ++o) {  // descending bin order within the lane
+    const int i = PER - 1 - o;
+    const int cnt = int(c[i]);
+    c[i] = uint32_t(run);
+    run += cnt;
+    if (found < 0 && run - cnt < need && run >= need) {
+      found = base + i;
+      upto = run;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER / 4; ++i) {
+    const u32x4 q4{c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]};
+    *reinterpret_cast<u32x4*>(&sh.hist[base + 4 * i]) = q4;
+    *reinterpret_cast<u32x4*>(&sh.cur[base + 4 * i]) = q4;
+  }
+  if (found >= 0) {
+    sh.digit = found;
+    sh.at = upto;
+  }
+  if (need == 0 && lane == 0) {
+    sh.digit = kBins;
+    sh.at = 0;
+  }
+}
+
+// Range, histogram and scan over U entries per thread (key_at(u), key 0 =
+// no entry). Returns the bin map; afterwards hist / cur hold the bins'
+// descending starts and sh.digit / sh.at the threshold bin and the number
+// of entries at or above it.
+template <int BLOCK, int CAP, int U, typename KeyAt>
+__device__ __forceinline__ ValueBins bucket_threshold(TopkShared<BLOCK, CAP>& sh, KeyAt key_at, int k) {
+  constexpr int NW = BLOCK / 64;
+  const int lane = lane_id(), wave = int(threadIdx.x) >> 6;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t kv = key_at(u);
+    if (finite_key(kv)) {
+      mn = min(mn, kv);
+      mx = max(mx, kv);
+    }
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    mn = min(mn, uint32_t(__shfl_xor(int(mn), d)));
+    mx = max(mx, uint32_t(__shfl_xor(int(mx), d)));
+  }
+  if (lane == 0) {
+    sh.wlo[wave] = mn;
+    sh.whi[wave] = mx;
+  }
+  clear_hist(sh, kBins);
+  __syncthreads();
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    mn = min(mn, sh.wlo[w]);
+    mx = max(mx, sh.whi[w]);
+  }
+  ValueBins bins{0.f, 0.f};
+  if (mn <= mx) {
+    bins.lo = key_value(mn);
+    const float range = key_value(mx) - bins.lo;
+    bins.s = range > 0.f ? float(kBins) / range : 0.f;  // an overflowed range gives 0
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t kv = key_at(u);
+    if (kv != 0u) atomicAdd(&sh.hist[bins(kv)], 1u);
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) scan_desc(sh, k);
+  __syncthreads();
+  return bins;
+}
+
+// Exact top-k of entries held U per thread (key_at(u), j_at(u), key 0 = no
+// entry), written to orow in (score desc, j asc) order, -1 past the last
+// entry. Every entry in a bin at or above b* is scattered to its bin's
+// slots (b*'s bins hold the k-th largest, so these are the winners plus the
+// rest of b*); an entry's rank inside its bin is counted by comparison, so
+// the result does not depend on the order of the atomics. Returns false,
+// having written nothing, when those bins hold more than kMaxTopk entries
+// (scores crowded into a few bins: heavy ties, far outliers).
+template <int BLOCK, int CAP, int U, typename KeyAt, typename JAt>
+__device__ __forceinline__ bool bucket_topk(TopkShared<BLOCK, CAP>& sh, KeyAt key_at, JAt j_at,
+                                            int k, int32_t* __restrict__ orow) {
+  const int tid = threadIdx.x;
+  const ValueBins bins = bucket_threshold<BLOCK, CAP, U>(sh, key_at, k);
+  const int bstar = sh.digit, m = sh.at;
+  if (m > kMaxTopk) return false;  // uniform
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t kv = key_at(u);
+    if (kv == 0u) continue;
+    const int b = bins(kv);
+    if (b >= bstar) {
+      const uint32_t pos = atomicAdd(&sh.cur[b], 1u);
+      sh.sel2[pos] = (uint64_t(kv) << 32) | uint64_t(~j_at(u));
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < m; p += BLOCK) {
+    const uint64_t e = sh.sel2[p];
+    const int b = bins(uint32_t(e >> 32));
+    const int start = int(sh.hist[b]);
+    const int end = b == bstar ? m : int(sh.hist[b - 1]);
+    int rank = 0;
+    for (int q = start; q < end; ++q) rank += sh.sel2[q] > e ? 1 : 0;
+    if (start + rank < k) orow[start + rank] = int32_t(~uint32_t(e & 0xFFFFFFFFull));
+  }
+  for (int p = m + tid; p < k; p += BLOCK) orow[p] = -1;
+  return true;
+}
+
 // Append a list (entries [0, nc) of ckey/cj) to the selection: the k winners
 // when nc > k, else all of them.
 template <int BLOCK, int CAP>
@@ -540,101 +728,128 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ l
     const int j = tid + BLOCK * v;
     key[v] = j < n ? order_key(x[j]) : 0u;
   }
-  auto chunks = [&](auto g) {
-    g([&](int v) { return key[v]; }, [&](int v) { return uint32_t(tid + BLOCK * v); });
-  };
-  int nsel = 0;
-  select_row<BLOCK, CAP, V>(sh, n, k, chunks, nsel);
-  sort_and_store(sh, nsel, idx + row * k, k);
+  auto key_at = [&](int v) { return key[v]; };
+  auto j_at = [&](int v) { return uint32_t(tid + BLOCK * v); };
+  if (bucket_topk<BLOCK, CAP, V>(sh, key_at, j_at, k, idx + row * k)) return;
+  radix_topk<BLOCK, CAP>(sh, x, n, k, idx + row * k);
 }
 
-// Longer rows. The first BLOCK*V keys are held in registers and selected
-// (at least k winners, every prefix key >= their smallest key tau). tau is
-// a lower bound of the row's k-th largest key (a prefix's k-th largest
-// cannot exceed the row's). The rest of the row is streamed once and only
-// keys > tau join an LDS candidate list: a streamed key equal to tau has a
-// larger j than the kept prefix keys equal to tau, of which there are
-// enough, so it can never win. The winners are then selected exactly from prefix-selection +
-// candidates. If the list runs out of room (only for adversarial rows), the
-// row falls back to multi-pass streaming selection over the whole row.
+// Radix path over the whole row, re-read from memory chunk by chunk (rows
+// whose scores crowd into a few bins, where the bucket path gives up). It
+// is rare, so it is kept lean in registers rather than fast.
+template <int BLOCK, int CAP>
+__device__ __forceinline__ void radix_topk(TopkShared<BLOCK, CAP>& sh, const float* __restrict__ x,
+                                           int n, int k, int32_t* __restrict__ orow) {
+  constexpr int U = 2;
+  auto all_chunks = [&](auto g) {
+    for (int base = 0; base < n; base += BLOCK * U) {
+      uint32_t kv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = base + BLOCK * u + int(threadIdx.x);
+        kv[u] = j < n ? order_key(x[j]) : 0u;
+      }
+      g([&](int u) { return kv[u]; }, [&](int u) { return uint32_t(base + BLOCK * u + int(threadIdx.x)); });
+    }
+  };
+  int nsel = 0;
+  select_row<BLOCK, CAP, U>(sh, n, k, all_chunks, nsel);
+  sort_and_store(sh, nsel, orow, k);
+}
+
+// Append the entries of a chunk that pass take(key) to the LDS list
+// ckey / cj: one ballot and one LDS atomic per wave and entry index. The
+// list order depends on the atomics, which nothing downstream relies on.
+template <int BLOCK, int CAP, int U, typename KeyAt, typename JAt, typename Take>
+__device__ __forceinline__ void append_list(TopkShared<BLOCK, CAP>& sh, KeyAt key_at, JAt j_at,
+                                            Take take_it) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t kv = key_at(u);
+    const bool take = take_it(kv);
+    const uint64_t m = __ballot(take);
+    if (m == 0) continue;
+    const int leader = __ffsll((unsigned long long)m) - 1;
+    int base = 0;
+    if (lane == leader) base = atomicAdd(&sh.ccount, __popcll(m));
+    base = __shfl(base, leader);
+    if (take) {
+      const int pos = base + prefix_in_wave(m);
+      if (pos < CAP) {
+        sh.ckey[pos] = kv;
+        sh.cj[pos] = j_at(u);
+      } else {
+        sh.overflow = 1;
+      }
+    }
+  }
+}
+
+// Longer rows. The first BLOCK*V keys are held in registers; their
+// histogram gives the bin b* that holds the prefix's k-th largest key.
+// The row's k-th largest key is at least the prefix's (the prefix is part
+// of the row), so every winner of the row lies in a bin >= b* under the
+// prefix's bin map: those prefix keys, and the keys of the rest of the row
+// (streamed once) that land there, form an LDS candidate list, from which
+// the winners are selected exactly. If the list runs out of room (scores
+// crowded into b*), the row falls back to multi-pass streaming selection.
 template <int BLOCK, int V, int CAP>
 __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restrict__ logits,
                                                           const int32_t* __restrict__ limit,
                                                           int32_t* __restrict__ idx, int K, int k) {
-  constexpr int U = 8;  // streamed entries per thread per chunk
+  constexpr int U = 8;            // streamed entries per thread per chunk
+  constexpr int L = CAP / BLOCK;  // list entries per thread
+  static_assert(CAP % BLOCK == 0, "list spread evenly over the block");
   __shared__ TopkShared<BLOCK, CAP> sh;
-  const int tid = threadIdx.x, lane = lane_id();
+  const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int n = limit ? max(0, min(limit[row], K - 1) + 1) : K;
   const int prefix = min(n, BLOCK * V);
   const float* x = logits + row * K;
+  int32_t* orow = idx + row * k;
   uint32_t key[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int j = tid + BLOCK * v;
     key[v] = j < prefix ? order_key(x[j]) : 0u;
   }
-  auto reg_chunks = [&](auto g) {
-    g([&](int v) { return key[v]; }, [&](int v) { return uint32_t(tid + BLOCK * v); });
-  };
-  int nsel = 0;
-  select_row<BLOCK, CAP, V>(sh, prefix, k, reg_chunks, nsel);
-
-  if (n > prefix) {
-    // move the prefix winners into the candidate list; tau = their smallest key
-    if (tid == 0) {
-      sh.tau = 0xFFFFFFFFu;
-      sh.ccount = nsel;
-      sh.overflow = 0;
-    }
-    __syncthreads();
-    uint32_t mn = 0xFFFFFFFFu;
-    for (int i = tid; i < nsel; i += BLOCK) {
-      const uint64_t e = sh.sel[i];
-      const uint32_t kv = uint32_t(e >> 32);
-      sh.ckey[i] = kv;
-      sh.cj[i] = ~uint32_t(e & 0xFFFFFFFFull);
-      mn = min(mn, kv);
-    }
-    for (int d = 32; d > 0; d >>= 1) mn = min(mn, uint32_t(__shfl_xor(int(mn), d)));
-    if (lane == 0) atomicMin(&sh.tau, mn);
-    __syncthreads();
-    const uint32_t tau = nsel >= k ? sh.tau : 0u;  // fewer than k so far: take every key
-    // stream the rest once; keys above tau join the list (one atomic per wave)
-    stream_chunks<BLOCK, U>(x, prefix, n, [&](auto key_at, auto j_at) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t kv = key_at(u);
-        const bool take = kv > tau;
-        const uint64_t m = __ballot(take);
-        if (m == 0) continue;
-        const int leader = __ffsll((unsigned long long)m) - 1;
-        int base = 0;
-        if (lane == leader) base = atomicAdd(&sh.ccount, __popcll(m));
-        base = __shfl(base, leader);
-        if (take) {
-          const int pos = base + prefix_in_wave(m);
-          if (pos < CAP) {
-            sh.ckey[pos] = kv;
-            sh.cj[pos] = j_at(u);
-          } else {
-            sh.overflow = 1;
-          }
-        }
-      }
-    });
-    __syncthreads();
-    nsel = 0;
-    if (!sh.overflow) {
-      // exact selection over prefix winners + streamed candidates
-      select_list(sh, sh.ccount, k, nsel);
-    } else {
-      // fallback: multi-pass selection streaming the whole row
-      auto all_chunks = [&](auto g) { stream_chunks<BLOCK, U>(x, 0, n, g); };
-      select_row<BLOCK, CAP, U>(sh, n, k, all_chunks, nsel);
-    }
+  auto key_at = [&](int v) { return key[v]; };
+  auto j_at = [&](int v) { return uint32_t(tid + BLOCK * v); };
+  if (n <= prefix) {
+    if (!bucket_topk<BLOCK, CAP, V>(sh, key_at, j_at, k, orow)) radix_topk<BLOCK, CAP>(sh, x, n, k, orow);
+    return;
   }
-  sort_and_store(sh, nsel, idx + row * k, k);
+  if (tid == 0) {
+    sh.ccount = 0;
+    sh.overflow = 0;
+  }
+  const ValueBins bins = bucket_threshold<BLOCK, CAP, V>(sh, key_at, k);
+  const int bstar = sh.digit;
+  auto admit = [&](uint32_t kv) { return kv != 0u && bins(kv) >= bstar; };
+  append_list<BLOCK, CAP, V>(sh, key_at, j_at, admit);
+  stream_chunks<BLOCK, U>(x, prefix, n, [&](auto kat, auto jat) {
+    append_list<BLOCK, CAP, U>(sh, kat, jat, admit);
+  });
+  __syncthreads();
+  if (!sh.overflow) {
+    const int nc = sh.ccount;
+    uint32_t lkey[L], lj[L];
+#pragma unroll
+    for (int u = 0; u < L; ++u) {
+      const int i = tid + BLOCK * u;
+      lkey[u] = i < nc ? sh.ckey[i] : 0u;
+      lj[u] = i < nc ? sh.cj[i] : 0u;
+    }
+    if (bucket_topk<BLOCK, CAP, L>(sh, [&](int u) { return lkey[u]; }, [&](int u) { return lj[u]; },
+                                   k, orow))
+      return;
+    int nsel = 0;
+    select_list(sh, nc, k, nsel);
+    sort_and_store(sh, nsel, orow, k);
+    return;
+  }
+  radix_topk<BLOCK, CAP>(sh, x, n, k, orow);
 }
 
 template <int BLOCK, int V, int CAP>
@@ -653,7 +868,7 @@ hipError_t launch_topk(const float* logits, const int32_t* limit, int32_t* idx, 
   if (K <= 256 * 16) return launch_one<256, 16, 2048>(logits, limit, idx, R, K, k, stream);
   if (K <= 1024 * 8) return launch_one<1024, 8, 4096>(logits, limit, idx, R, K, k, stream);
   if (K <= 1024 * 16) return launch_one<1024, 16, 4096>(logits, limit, idx, R, K, k, stream);
-  hipLaunchKernelGGL((topk_long_kernel<1024, 32, 6144>), dim3(unsigned(R)), dim3(1024), 0, stream,
+  hipLaunchKernelGGL((topk_long_kernel<1024, 24, 8192>), dim3(unsigned(R)), dim3(1024), 0, stream,
                      logits, limit, idx, K, k);
   return hipGetLastError();
 }
