@@ -64,27 +64,67 @@ __device__ __forceinline__ int prefix_in_wave(uint64_t mask) {
   return __popcll(mask & ((uint64_t(1) << lane_id()) - 1));
 }
 
+// DPP controls (GFX9 encoding).
+constexpr int kDppQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRowShr = 0x110;      // row_shr:n = kDppRowShr + n
+constexpr int kDppRowMirror = 0x140;   // lane i <- 15 - i within a row of 16
+constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within 8 lanes
+constexpr int kDppBcast15 = 0x142;     // lane 15 of each row -> next row
+constexpr int kDppBcast31 = 0x143;     // lane 31 -> rows 2 and 3
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp0(int v) {  // lanes without a source read 0
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8
+// inside each row of 16 lanes, then the row totals carried across rows by
+// the broadcasts of lanes 15 and 31. All VALU, no LDS round trip.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp0<kDppRowShr + 1>(v);
+  v += dpp0<kDppRowShr + 2>(v);
+  v += dpp0<kDppRowShr + 4>(v);
+  v += dpp0<kDppRowShr + 8>(v);
+  v += dpp0<kDppBcast15, 0xA>(v);
+  v += dpp0<kDppBcast31, 0xC>(v);
+  return v;
+}
+
+// Minimum and maximum over the wave, uniform result: butterflies inside
+// each row of 16 lanes, then the four row results read as scalars.
+__device__ __forceinline__ void wave_min_max(uint32_t& mn, uint32_t& mx) {
+#define XK_STEP(C)                                                           \
+  mn = min(mn, uint32_t(__builtin_amdgcn_update_dpp(int(mn), int(mn), C, 0xF, 0xF, false))); \
+  mx = max(mx, uint32_t(__builtin_amdgcn_update_dpp(int(mx), int(mx), C, 0xF, 0xF, false)));
+  XK_STEP(kDppQuadSwap1)
+  XK_STEP(kDppQuadSwap2)
+  XK_STEP(kDppHalfMirror)
+  XK_STEP(kDppRowMirror)
+#undef XK_STEP
+  uint32_t a = min(uint32_t(__builtin_amdgcn_readlane(int(mn), 0)), uint32_t(__builtin_amdgcn_readlane(int(mn), 16)));
+  uint32_t b = min(uint32_t(__builtin_amdgcn_readlane(int(mn), 32)), uint32_t(__builtin_amdgcn_readlane(int(mn), 48)));
+  mn = min(a, b);
+  a = max(uint32_t(__builtin_amdgcn_readlane(int(mx), 0)), uint32_t(__builtin_amdgcn_readlane(int(mx), 16)));
+  b = max(uint32_t(__builtin_amdgcn_readlane(int(mx), 32)), uint32_t(__builtin_amdgcn_readlane(int(mx), 48)));
+  mx = max(a, b);
+}
+
+// LDS of one row. sel holds entries key << 32 | ~j (larger = better): the
+// radix path's selection, or the bucket path's bin slots. ckey / cj is a
+// candidate list: keys of the radix threshold bucket, or a long row's
+// candidates.
 template <int BLOCK, int CAP>
 struct TopkShared {
   __attribute__((aligned(16))) uint32_t hist[kBins];
-  union {
-    uint64_t sel[kMaxTopk];                           // radix path: selection
-    __attribute__((aligned(16))) uint32_t cur[kBins];  // bucket path: scatter cursors
-  };
-  union {
-    struct {
-      uint32_t ckey[CAP];  // candidate list: keys in the threshold bucket
-      uint32_t cj[CAP];    // ... and their positions
-    };
-    uint64_t sel2[kMaxTopk];  // merge-round buffer (the list is dead by then)
-  };
+  uint64_t sel[kMaxTopk];
+  uint32_t ckey[CAP];
+  uint32_t cj[CAP];
   int wsel[BLOCK / 64], wcand[BLOCK / 64];
   uint32_t wlo[BLOCK / 64], whi[BLOCK / 64];  // per-wave finite key range
   int digit, above, at;
-  int ccount;       // streamed candidate list: entries claimed so far
-  int overflow;     // 1 if the streamed list ran out of room
-  uint32_t tau;     // smallest key of the prefix selection
-  uint32_t lo, hi;  // key range of the selection (sort)
+  int ccount;    // candidate list: entries claimed so far
+  int overflow;  // 1 if the candidate list ran out of room
 };
 
 // Wave 0: find the bin that holds the `need`-th element of hist[0..NBINS),
@@ -111,12 +151,7 @@ __device__ __forceinline__ void find_bin(TopkShared<BLOCK, CAP>& sh, int need, b
   int s = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) s += int(c[i]);
-  int incl = s;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(incl, d);
-    if (lane >= d) incl += t;
-  }
+  const int incl = wave_incl_scan(s);
   int before = incl - s;
   if (before < need && incl >= need) {
     int found = -1, f_above = 0, f_at = 0;
@@ -140,17 +175,6 @@ __device__ __forceinline__ void find_bin(TopkShared<BLOCK, CAP>& sh, int need, b
 template <int BLOCK, int CAP>
 __device__ __forceinline__ void clear_hist(TopkShared<BLOCK, CAP>& sh, int nbins) {
   for (int i = threadIdx.x; i < nbins; i += BLOCK) sh.hist[i] = 0u;
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(v, d);
-    if (lane >= d) v += t;
-  }
-  return v;
 }
 
 // Append entries of a chunk (U per thread) to the selection (pred == 1) or
@@ -296,114 +320,6 @@ __device__ __forceinline__ bool taken(const Cut& c, uint32_t key, uint32_t j) {
   return key != 0u && (h > c.thr || (h == c.thr && j <= c.jcut));
 }
 
-// Sort sh.sel[0..m) (entries key << 32 | ~j, all distinct) descending and
-// write the row's indices, -1 past m. Counting sort on adaptive bins: with
-// hi / lo the largest / smallest key, bin = (hi - key) >> shift, shift chosen
-// so the 2048 bins span [lo, hi]. Entries are scattered to their bin's slots
-// (slot order from atomics), then every entry counts the entries of its own
-// bin that precede it in (key desc, j asc) order and moves to that rank, so
-// the final order does not depend on the atomic order. Bins of selected
-// logits hold a handful of entries; equal keys share a bin.
-template <int BLOCK, int CAP>
-__device__ __forceinline__ void sort_and_store(TopkShared<BLOCK, CAP>& sh, int m, int32_t* orow,
-                                               int k) {
-  constexpr int PER = (kMaxTopk + BLOCK - 1) / BLOCK;  // entries per thread, at most
-  const int tid = threadIdx.x, lane = lane_id();
-  if (tid == 0) {
-    sh.lo = 0xFFFFFFFFu;
-    sh.hi = 0u;
-  }
-  clear_hist(sh, kBins);
-  __syncthreads();
-  uint64_t e[PER];
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int p = tid + BLOCK * i;
-    e[i] = 0ull;
-    if (BLOCK * i >= m) continue;  // uniform
-    e[i] = p < m ? sh.sel[p] : 0ull;
-    if (p < m) {
-      mn = min(mn, uint32_t(e[i] >> 32));
-      mx = max(mx, uint32_t(e[i] >> 32));
-    }
-  }
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) {
-    mn = min(mn, uint32_t(__shfl_xor(int(mn), d)));
-    mx = max(mx, uint32_t(__shfl_xor(int(mx), d)));
-  }
-  if (lane == 0 && m > 0) {
-    atomicMin(&sh.lo, mn);
-    atomicMax(&sh.hi, mx);
-  }
-  __syncthreads();
-  const uint32_t hi = sh.hi;
-  const uint32_t range = m > 0 ? hi - sh.lo : 0u;
-  const int shift = (range >> 11) == 0u ? 0 : 32 - __clz(int(range >> 11));
-  int bin[PER], slot[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int p = tid + BLOCK * i;
-    bin[i] = 0;
-    slot[i] = 0;
-    if (BLOCK * i >= m) continue;  // uniform
-    bin[i] = int((hi - uint32_t(e[i] >> 32)) >> shift);
-    if (p < m) slot[i] = int(atomicAdd(&sh.hist[bin[i]], 1u));
-  }
-  __syncthreads();
-  // exclusive scan of the bin counts (one wave, 32 bins per lane) in place
-  if (tid < 64) {
-    constexpr int PB = kBins / 64;
-    uint32_t c[PB];
-#pragma unroll
-    for (int i = 0; i < PB / 4; ++i) {
-      const u32x4 q4 = *reinterpret_cast<const u32x4*>(&sh.hist[tid * PB + 4 * i]);
-      c[4 * i] = q4[0];
-      c[4 * i + 1] = q4[1];
-      c[4 * i + 2] = q4[2];
-      c[4 * i + 3] = q4[3];
-    }
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < PB; ++i) sum += int(c[i]);
-    int run = wave_incl_scan(sum) - sum;
-#pragma unroll
-    for (int i = 0; i < PB; ++i) {
-      const int ci = int(c[i]);
-      c[i] = uint32_t(run);
-      run += ci;
-    }
-#pragma unroll
-    for (int i = 0; i < PB / 4; ++i)
-      *reinterpret_cast<u32x4*>(&sh.hist[tid * PB + 4 * i]) =
-          u32x4{c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]};
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int p = tid + BLOCK * i;
-    if (BLOCK * i >= m) continue;  // uniform
-    if (p < m) sh.sel2[sh.hist[bin[i]] + slot[i]] = e[i];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int p = tid + BLOCK * i;
-    if (BLOCK * i >= m) continue;  // uniform
-    if (p < m) {
-      const int start = int(sh.hist[bin[i]]);
-      const int end = bin[i] + 1 < kBins ? int(sh.hist[bin[i] + 1]) : m;
-      int rank = 0;
-      for (int q = start; q < end; ++q) rank += sh.sel2[q] > e[i] ? 1 : 0;
-      sh.sel[start + rank] = e[i];
-    }
-  }
-  __syncthreads();
-  for (int p = tid; p < k; p += BLOCK)  // m may exceed k: the first k are the winners
-    orow[p] = p < m ? int32_t(~uint32_t(sh.sel[p] & 0xFFFFFFFFull)) : -1;
-}
-
 // Select the winners of a row into sh.sel, unsorted; nsel counts them. That
 // is min(k, n) entries, or, when the whole threshold bucket fits, every
 // entry at or above it (at least k), to be cut to k by the sort.
@@ -511,8 +427,7 @@ struct ValueBins {
 };
 
 // Wave 0: turn the bin counts in hist into descending exclusive starts
-// (entries in higher bins), copied to cur as scatter cursors, and find the
-// threshold bin b*: the bin holding the need-th largest entry, need =
+// (entries in higher bins) in place, and find the threshold bin b*: the bin holding the need-th largest entry, need =
 // min(k, entries). Leaves sh.digit = b* and sh.at = entries in bins >= b*
 // (b* = kBins and 0 when there are no entries).
 template <int BLOCK, int CAP>
@@ -533,7 +448,7 @@ __device__ __forceinline__ void scan_desc(TopkShared<BLOCK, CAP>& sh, int k) {
 #pragma unroll
   for (int i = 0; i < PER; ++i) sum += int(c[i]);
   const int incl = wave_incl_scan(sum);
-  const int need = min(k, __shfl(incl, 63));
+  const int need = min(k, __builtin_amdgcn_readlane(incl, 63));
   int run = incl - sum, found = -1, upto = 0;
 #pragma unroll
   for (int o = 0; o < PER; ++o) {  // descending bin order within the lane
@@ -548,9 +463,8 @@ __device__ __forceinline__ void scan_desc(TopkShared<BLOCK, CAP>& sh, int k) {
   }
 #pragma unroll
   for (int i = 0; i < PER / 4; ++i) {
-    const u32x4 q4{c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]};
-    *reinterpret_cast<u32x4*>(&sh.hist[base + 4 * i]) = q4;
-    *reinterpret_cast<u32x4*>(&sh.cur[base + 4 * i]) = q4;
+    *reinterpret_cast<u32x4*>(&sh.hist[base + 4 * i]) =
+        u32x4{c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]};
   }
   if (found >= 0) {
     sh.digit = found;
@@ -563,7 +477,7 @@ __device__ __forceinline__ void scan_desc(TopkShared<BLOCK, CAP>& sh, int k) {
 }
 
 // Range, histogram and scan over U entries per thread (key_at(u), key 0 =
-// no entry). Returns the bin map; afterwards hist / cur hold the bins'
+// no entry). Returns the bin map; afterwards hist holds the bins'
 // descending starts and sh.digit / sh.at the threshold bin and the number
 // of entries at or above it.
 template <int BLOCK, int CAP, int U, typename KeyAt>
@@ -579,11 +493,7 @@ __device__ __forceinline__ ValueBins bucket_threshold(TopkShared<BLOCK, CAP>& sh
       mx = max(mx, kv);
     }
   }
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) {
-    mn = min(mn, uint32_t(__shfl_xor(int(mn), d)));
-    mx = max(mx, uint32_t(__shfl_xor(int(mx), d)));
-  }
+  wave_min_max(mn, mx);
   if (lane == 0) {
     sh.wlo[wave] = mn;
     sh.whi[wave] = mx;
@@ -618,8 +528,10 @@ __device__ __forceinline__ ValueBins bucket_threshold(TopkShared<BLOCK, CAP>& sh
 // entry), written to orow in (score desc, j asc) order, -1 past the last
 // entry. Every entry in a bin at or above b* is scattered to its bin's
 // slots (b*'s bins hold the k-th largest, so these are the winners plus the
-// rest of b*); an entry's rank inside its bin is counted by comparison, so
-// the result does not depend on the order of the atomics. Returns false,
+// rest of b*), hist[b] serving as bin b's cursor: afterwards hist[b] is the
+// end of bin b and hist[b + 1] its start (bins above b* are all filled).
+// An entry's rank inside its bin is counted by comparison, so the result
+// does not depend on the order of the atomics. Returns false,
 // having written nothing, when those bins hold more than kMaxTopk entries
 // (scores crowded into a few bins: heavy ties, far outliers).
 template <int BLOCK, int CAP, int U, typename KeyAt, typename JAt>
@@ -635,18 +547,18 @@ __device__ __forceinline__ bool bucket_topk(TopkShared<BLOCK, CAP>& sh, KeyAt ke
     if (kv == 0u) continue;
     const int b = bins(kv);
     if (b >= bstar) {
-      const uint32_t pos = atomicAdd(&sh.cur[b], 1u);
-      sh.sel2[pos] = (uint64_t(kv) << 32) | uint64_t(~j_at(u));
+      const uint32_t pos = atomicAdd(&sh.hist[b], 1u);
+      sh.sel[pos] = (uint64_t(kv) << 32) | uint64_t(~j_at(u));
     }
   }
   __syncthreads();
   for (int p = tid; p < m; p += BLOCK) {
-    const uint64_t e = sh.sel2[p];
+    const uint64_t e = sh.sel[p];
     const int b = bins(uint32_t(e >> 32));
-    const int start = int(sh.hist[b]);
-    const int end = b == bstar ? m : int(sh.hist[b - 1]);
+    const int start = b == kBins - 1 ? 0 : int(sh.hist[b + 1]);
+    const int end = int(sh.hist[b]);
     int rank = 0;
-    for (int q = start; q < end; ++q) rank += sh.sel2[q] > e ? 1 : 0;
+    for (int q = start; q < end; ++q) rank += sh.sel[q] > e ? 1 : 0;
     if (start + rank < k) orow[start + rank] = int32_t(~uint32_t(e & 0xFFFFFFFFull));
   }
   for (int p = m + tid; p < k; p += BLOCK) orow[p] = -1;
@@ -678,19 +590,29 @@ __device__ __forceinline__ void select_list(TopkShared<BLOCK, CAP>& sh, int nc, 
   }
 }
 
-// chunks(g) over entries [j_lo, j_hi) of x streamed from memory, BLOCK*U per
-// chunk, the next chunk's loads in flight while this one is processed.
-template <int BLOCK, int U, typename G>
-__device__ __forceinline__ void stream_chunks(const float* __restrict__ x, int j_lo, int j_hi, G g) {
-  const int tid = threadIdx.x;
-  uint32_t kv[U];
-  float cur[U], nxt[U];
+// Loads of the chunk of BLOCK*U entries of x starting at base (this
+// thread's entries base + BLOCK*u + tid below j_hi).
+template <int BLOCK, int U>
+__device__ __forceinline__ void load_chunk(const float* __restrict__ x, int base, int j_hi, float (&c)[U]) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int j = j_lo + BLOCK * u + tid;
-    cur[u] = j < j_hi ? x[j] : 0.f;
-    nxt[u] = 0.f;
+    const int j = base + BLOCK * u + int(threadIdx.x);
+    c[u] = j < j_hi ? x[j] : 0.f;
   }
+}
+
+// chunks(g) over entries [j_lo, j_hi) of x streamed from memory, BLOCK*U per
+// chunk, the next chunk's loads in flight while this one is processed. cur
+// holds the first chunk's loads (load_chunk at j_lo), issued by the caller
+// as early as it likes.
+template <int BLOCK, int U, typename G>
+__device__ __forceinline__ void stream_chunks(const float* __restrict__ x, int j_lo, int j_hi, float (&cur)[U],
+                                              G g) {
+  const int tid = threadIdx.x;
+  uint32_t kv[U];
+  float nxt[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) nxt[u] = 0.f;
   for (int base = j_lo; base < j_hi; base += BLOCK * U) {
     const int nb = base + BLOCK * U;
     if (nb < j_hi) {
@@ -711,27 +633,23 @@ __device__ __forceinline__ void stream_chunks(const float* __restrict__ x, int j
   }
 }
 
-// Rows of at most BLOCK*V keys: the row is read once into V registers per
-// thread (j = tid + BLOCK*v).
-template <int BLOCK, int V, int CAP>
-__global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ logits,
-                                                     const int32_t* __restrict__ limit,
-                                                     int32_t* __restrict__ idx, int K, int k) {
-  __shared__ TopkShared<BLOCK, CAP> sh;
+// Order the selection sh.sel[0..nsel) (at most kMaxTopk entries, at least
+// min(k, valid keys)) and write the first k: the entries move to registers
+// and go through the bucket path, which always succeeds on so few entries.
+template <int BLOCK, int CAP>
+__device__ __forceinline__ void sort_selection(TopkShared<BLOCK, CAP>& sh, int nsel, int k,
+                                               int32_t* __restrict__ orow) {
+  constexpr int PER = kMaxTopk / BLOCK;
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const int n = limit ? max(0, min(limit[row], K - 1) + 1) : K;
-  const float* x = logits + row * K;
-  uint32_t key[V];
+  uint32_t sk[PER], sj[PER];
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int j = tid + BLOCK * v;
-    key[v] = j < n ? order_key(x[j]) : 0u;
+  for (int i = 0; i < PER; ++i) {
+    const int p = tid + BLOCK * i;
+    const uint64_t e = p < nsel ? sh.sel[p] : 0ull;
+    sk[i] = uint32_t(e >> 32);
+    sj[i] = ~uint32_t(e & 0xFFFFFFFFull);
   }
-  auto key_at = [&](int v) { return key[v]; };
-  auto j_at = [&](int v) { return uint32_t(tid + BLOCK * v); };
-  if (bucket_topk<BLOCK, CAP, V>(sh, key_at, j_at, k, idx + row * k)) return;
-  radix_topk<BLOCK, CAP>(sh, x, n, k, idx + row * k);
+  bucket_topk<BLOCK, CAP, PER>(sh, [&](int i) { return sk[i]; }, [&](int i) { return sj[i]; }, k, orow);
 }
 
 // Radix path over the whole row, re-read from memory chunk by chunk (rows
@@ -754,7 +672,33 @@ __device__ __forceinline__ void radix_topk(TopkShared<BLOCK, CAP>& sh, const flo
   };
   int nsel = 0;
   select_row<BLOCK, CAP, U>(sh, n, k, all_chunks, nsel);
-  sort_and_store(sh, nsel, orow, k);
+  sort_selection(sh, nsel, k, orow);
+}
+
+// Rows of at most BLOCK*V keys: the row is read once into V registers per
+// thread (j = tid + BLOCK*v).
+template <int BLOCK, int V, int CAP>
+__global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ logits,
+                                                     const int32_t* __restrict__ limit,
+                                                     int32_t* __restrict__ idx, int K, int k) {
+  __shared__ TopkShared<BLOCK, CAP> sh;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const float* x = logits + row * K;
+  float raw[V];  // issued before the limit arrives; keys past it are masked below
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int j = tid + BLOCK * v;
+    raw[v] = j < K ? x[j] : 0.f;
+  }
+  const int n = limit ? max(0, min(limit[row], K - 1) + 1) : K;
+  uint32_t key[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) key[v] = tid + BLOCK * v < n ? order_key(raw[v]) : 0u;
+  auto key_at = [&](int v) { return key[v]; };
+  auto j_at = [&](int v) { return uint32_t(tid + BLOCK * v); };
+  if (bucket_topk<BLOCK, CAP, V>(sh, key_at, j_at, k, idx + row * k)) return;
+  radix_topk<BLOCK, CAP>(sh, x, n, k, idx + row * k);
 }
 
 // Append the entries of a chunk that pass take(key) to the LDS list
@@ -773,7 +717,7 @@ __device__ __forceinline__ void append_list(TopkShared<BLOCK, CAP>& sh, KeyAt ke
     const int leader = __ffsll((unsigned long long)m) - 1;
     int base = 0;
     if (lane == leader) base = atomicAdd(&sh.ccount, __popcll(m));
-    base = __shfl(base, leader);
+    base = __builtin_amdgcn_readlane(base, leader);
     if (take) {
       const int pos = base + prefix_in_wave(m);
       if (pos < CAP) {
@@ -814,6 +758,8 @@ __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restric
     const int j = tid + BLOCK * v;
     key[v] = j < prefix ? order_key(x[j]) : 0u;
   }
+  float first[U];  // the streamed part's first chunk, in flight during the prefix's threshold
+  load_chunk<BLOCK, U>(x, prefix, n, first);
   auto key_at = [&](int v) { return key[v]; };
   auto j_at = [&](int v) { return uint32_t(tid + BLOCK * v); };
   if (n <= prefix) {
@@ -828,7 +774,7 @@ __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restric
   const int bstar = sh.digit;
   auto admit = [&](uint32_t kv) { return kv != 0u && bins(kv) >= bstar; };
   append_list<BLOCK, CAP, V>(sh, key_at, j_at, admit);
-  stream_chunks<BLOCK, U>(x, prefix, n, [&](auto kat, auto jat) {
+  stream_chunks<BLOCK, U>(x, prefix, n, first, [&](auto kat, auto jat) {
     append_list<BLOCK, CAP, U>(sh, kat, jat, admit);
   });
   __syncthreads();
@@ -846,7 +792,7 @@ __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restric
       return;
     int nsel = 0;
     select_list(sh, nc, k, nsel);
-    sort_and_store(sh, nsel, orow, k);
+    sort_selection(sh, nsel, k, orow);
     return;
   }
   radix_topk<BLOCK, CAP>(sh, x, n, k, orow);
@@ -864,10 +810,10 @@ hipError_t launch_one(const float* logits, const int32_t* limit, int32_t* idx, i
 
 hipError_t launch_topk(const float* logits, const int32_t* limit, int32_t* idx, int R, int K,
                        int k, hipStream_t stream) {
-  if (K <= 256 * 4) return launch_one<256, 4, 2048>(logits, limit, idx, R, K, k, stream);
-  if (K <= 256 * 16) return launch_one<256, 16, 2048>(logits, limit, idx, R, K, k, stream);
-  if (K <= 1024 * 8) return launch_one<1024, 8, 4096>(logits, limit, idx, R, K, k, stream);
-  if (K <= 1024 * 16) return launch_one<1024, 16, 4096>(logits, limit, idx, R, K, k, stream);
+  if (K <= 256 * 4) return launch_one<256, 4, 256>(logits, limit, idx, R, K, k, stream);
+  if (K <= 256 * 16) return launch_one<256, 16, 256>(logits, limit, idx, R, K, k, stream);
+  if (K <= 1024 * 8) return launch_one<1024, 8, 1024>(logits, limit, idx, R, K, k, stream);
+  if (K <= 1024 * 16) return launch_one<1024, 16, 1024>(logits, limit, idx, R, K, k, stream);
   hipLaunchKernelGGL((topk_long_kernel<1024, 24, 8192>), dim3(unsigned(R)), dim3(1024), 0, stream,
                      logits, limit, idx, K, k);
   return hipGetLastError();
