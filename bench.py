@@ -5,8 +5,16 @@ A step is one pass of the whole path over one batch of synthetic input:
 Prints ONE JSON line. `value` is the indexer-logits throughput of the whole
 step (algorithmic logits FLOPs / step wall time), `topk_gather_GBps` the
 algorithmic bytes of top-k + gather over their kernel time; `stages` has every
-kernel's average duration (HIP events on the launch stream over the timed
-steps) against its roof, and `roofline` repeats the dominant kernel.
+kernel's average duration against its roof, and `roofline` repeats the
+dominant kernel.
+
+Steps are replayed from HIP graphs (one captured step per input copy), so the
+timed loop measures the GPU rather than Python's launch cost; before timing,
+two replays are checked bit for bit against an eager step, and
+`ms_per_step_eager` reports eager launches too. A kernel's duration is
+timed with HIP events on the launch stream around replays of a graph of 20
+back-to-back launches of that kernel alone (rotating the same input
+copies), so no launch gap is counted.
 
 Inputs are resident in HBM before timing starts. Several identical copies of
 q/k/w are rotated across steps so that a decode-sized working set cannot be
@@ -175,12 +183,11 @@ def main():
     base = IndexerStep(d["q"], d["k"], d["w"], d["limit"], cfg.topk, d["kv_fp4"], d["kv_scale"],
                        d["block_table"], d["row_seq"], d["q_scale"], d["k_scale"])
     steps = [base]
-    for _ in range(n_sets - 1):
-        s = IndexerStep(d["q"].clone(), d["k"].clone(), d["w"].clone(), d["limit"], cfg.topk,
-                        d["kv_fp4"], d["kv_scale"], d["block_table"], d["row_seq"],
-                        d["q_scale"], d["k_scale"])
-        s.logits, s.idx, s.gathered = base.logits, base.idx, base.gathered   # shared outputs
-        steps.append(s)
+    for _ in range(n_sets - 1):   # more input copies, writing the same output buffers
+        steps.append(IndexerStep(d["q"].clone(), d["k"].clone(), d["w"].clone(), d["limit"],
+                                 cfg.topk, d["kv_fp4"], d["kv_scale"], d["block_table"],
+                                 d["row_seq"], d["q_scale"], d["k_scale"],
+                                 outputs=base.outputs()))
 
     # one checked pass: top-k indices must be valid positions before the gather reads them
     base.run_logits()
@@ -193,27 +200,64 @@ def main():
     base.run_gather()
     torch.cuda.synchronize()
     work = algorithmic_work(x, sel)
+    eager_out = [t.clone() for t in base.outputs()]
 
     for i in range(args.warmup):
         steps[i % n_sets]()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    # eager launches, for reference: host launch cost included
+    n_eager = min(args.steps, 50)
+    t0 = time.perf_counter()
+    for i in range(n_eager):
+        steps[i % n_sets]()
+    torch.cuda.synchronize()
+    ms_step_eager = (time.perf_counter() - t0) * 1e3 / n_eager
+
+    # one HIP graph per input copy holds a whole step (three kernels)
+    graphs = []
+    for s in steps:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for rep in range(2):   # replays must reproduce the eager outputs bit for bit
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(base.outputs(), eager_out)):
+            raise RuntimeError("graph replay differs from the eager step")
+        steps[0]()          # eager work between replays
+        torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        graphs[i % n_sets].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        s = steps[i % n_sets]
-        e = ev[i]
-        e[0].record()
-        s.run_logits()
-        e[1].record()
-        s.run_topk()
-        e[2].record()
-        s.run_gather()
-        e[3].record()
+        graphs[i % n_sets].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    ms = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
-          for j, name in enumerate(("logits", "topk", "gather"))}
+
+    # per-kernel durations: a graph of back-to-back launches of one kernel,
+    # rotating the input copies, timed with events on the launch stream
+    n_in_graph = 20
+    ms = {}
+    for name in ("logits", "topk", "gather"):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n_in_graph):
+                getattr(steps[i % n_sets], "run_" + name)()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // n_in_graph)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms[name] = e0.elapsed_time(e1) / (reps * n_in_graph)
 
     prefill = cfg.T >= 8
     mfma_peak = PEAK["mfma_fp8" if cfg.dtype == "fp8" else "mfma_bf16"]
@@ -242,6 +286,7 @@ def main():
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "ms_per_step_eager": ms_step_eager, "launch": "hip_graph",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic: seeded numpy PCG64 inputs with the DeepSeek-V4 indexer shapes",

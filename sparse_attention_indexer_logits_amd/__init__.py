@@ -83,13 +83,10 @@ def _need(t, name, dtypes, ndim):
         raise ValueError(f"{name} must be a contiguous {ndim}-d tensor, got {tuple(t.shape)}")
 
 
-def xk_indexer_logits(q, k, w, limit=None, q_scale=None, k_scale=None, out=None, stream=None):
-    """logits [B,T,K] fp32 = sum_h w * relu(q . k), -inf past limit (see include/xk.h).
-
-    q [B,T,64,128] and k [B,K,128] are bfloat16, or float8_e4m3fn / uint8
-    bytes with q_scale [B,T,64] and k_scale [B,K] fp32; w [B,T,64] fp32;
-    limit [B,T] int32 or None.
-    """
+def logits_args(q, k, w, limit=None, q_scale=None, k_scale=None, out=None):
+    """Validate the arguments of xk_indexer_logits and return (C arguments
+    without the stream, out). Callers that launch the same call repeatedly
+    (IndexerStep) keep the tuple and skip re-validation."""
     _need(q, "q", (torch.bfloat16, torch.float8_e4m3fn, torch.uint8), 4)
     B, T, H, D = q.shape
     fp8 = q.dtype != torch.bfloat16
@@ -114,9 +111,20 @@ def xk_indexer_logits(q, k, w, limit=None, q_scale=None, k_scale=None, out=None,
     _need(out, "out", (torch.float32,), 3)
     if tuple(out.shape) != (B, T, K):
         raise ValueError("out must be [B,T,K]")
-    _check(_lib.xk_indexer_logits(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w),
-                                  _ptr(limit), _ptr(out), B, T, K, H, D,
-                                  XK_FP8_E4M3_OCP if fp8 else XK_BF16, _stream(stream)))
+    args = (_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), _ptr(limit), _ptr(out),
+            B, T, K, H, D, XK_FP8_E4M3_OCP if fp8 else XK_BF16)
+    return args, out
+
+
+def xk_indexer_logits(q, k, w, limit=None, q_scale=None, k_scale=None, out=None, stream=None):
+    """logits [B,T,K] fp32 = sum_h w * relu(q . k), -inf past limit (see include/xk.h).
+
+    q [B,T,64,128] and k [B,K,128] are bfloat16, or float8_e4m3fn / uint8
+    bytes with q_scale [B,T,64] and k_scale [B,K] fp32; w [B,T,64] fp32;
+    limit [B,T] int32 or None.
+    """
+    args, out = logits_args(q, k, w, limit, q_scale, k_scale, out)
+    _check(_lib.xk_indexer_logits(*args, _stream(stream)))
     return out
 
 
@@ -124,11 +132,9 @@ def xk_indexer_topk_workspace_size(R: int, K: int, k: int) -> int:
     return int(_lib.xk_indexer_topk_workspace_size(R, K, k))
 
 
-def xk_indexer_topk(logits, k: int, limit=None, out=None, workspace=None, stream=None):
-    """idx [R,k] int32: top-k per row by (score desc, j asc), -1 padded (see include/xk.h).
-
-    logits [R,K] fp32 (a [B,T,K] tensor is viewed as [B*T,K]); limit [R] int32 or None.
-    """
+def topk_args(logits, k: int, limit=None, out=None, workspace=None):
+    """Validate the arguments of xk_indexer_topk; returns (C arguments without
+    the stream, out, workspace)."""
     if logits.dim() == 3:
         logits = logits.view(-1, logits.shape[-1])
     _need(logits, "logits", (torch.float32,), 2)
@@ -147,18 +153,24 @@ def xk_indexer_topk(logits, k: int, limit=None, out=None, workspace=None, stream
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib.xk_indexer_topk(_ptr(logits), _ptr(limit), _ptr(out), R, K, k,
-                                _ptr(workspace), ws_bytes, _stream(stream)))
+    if workspace is not None and workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace too small")
+    return (_ptr(logits), _ptr(limit), _ptr(out), R, K, k, _ptr(workspace), ws_bytes), out, workspace
+
+
+def xk_indexer_topk(logits, k: int, limit=None, out=None, workspace=None, stream=None):
+    """idx [R,k] int32: top-k per row by (score desc, j asc), -1 padded (see include/xk.h).
+
+    logits [R,K] fp32 (a [B,T,K] tensor is viewed as [B*T,K]); limit [R] int32 or None.
+    """
+    args, out, _ = topk_args(logits, k, limit, out, workspace)
+    _check(_lib.xk_indexer_topk(*args, _stream(stream)))
     return out
 
 
-def xk_mxfp4_paged_gather(kv_fp4, kv_scale, block_table, sel_pos, row_seq=None, out=None,
-                          stream=None):
-    """out [R,k,128] bf16 bits (int16 storage) of the selected mxfp4 rows (see include/xk.h).
-
-    kv_fp4 [NB,bs,64] uint8; kv_scale [NB,bs,4] uint8; block_table [S,MB] int32;
-    sel_pos [R,k] int32; row_seq [R] int32 or None.
-    """
+def gather_args(kv_fp4, kv_scale, block_table, sel_pos, row_seq=None, out=None):
+    """Validate the arguments of xk_mxfp4_paged_gather; returns (C arguments
+    without the stream, out)."""
     _need(kv_fp4, "kv_fp4", (torch.uint8,), 3)
     NB, bs, half = kv_fp4.shape
     D = 2 * half
@@ -178,7 +190,18 @@ def xk_mxfp4_paged_gather(kv_fp4, kv_scale, block_table, sel_pos, row_seq=None, 
     _need(out, "out", (torch.int16, torch.bfloat16), 3)
     if tuple(out.shape) != (R, k, D):
         raise ValueError("out must be [R,k,D]")
-    _check(_lib.xk_mxfp4_paged_gather(_ptr(kv_fp4), _ptr(kv_scale), _ptr(block_table),
-                                      _ptr(sel_pos), _ptr(row_seq), _ptr(out),
-                                      R, k, S, MB, NB, bs, D, _stream(stream)))
+    args = (_ptr(kv_fp4), _ptr(kv_scale), _ptr(block_table), _ptr(sel_pos), _ptr(row_seq),
+            _ptr(out), R, k, S, MB, NB, bs, D)
+    return args, out
+
+
+def xk_mxfp4_paged_gather(kv_fp4, kv_scale, block_table, sel_pos, row_seq=None, out=None,
+                          stream=None):
+    """out [R,k,128] bf16 bits (int16 storage) of the selected mxfp4 rows (see include/xk.h).
+
+    kv_fp4 [NB,bs,64] uint8; kv_scale [NB,bs,4] uint8; block_table [S,MB] int32;
+    sel_pos [R,k] int32; row_seq [R] int32 or None.
+    """
+    args, out = gather_args(kv_fp4, kv_scale, block_table, sel_pos, row_seq, out)
+    _check(_lib.xk_mxfp4_paged_gather(*args, _stream(stream)))
     return out

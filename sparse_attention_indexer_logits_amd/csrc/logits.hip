@@ -18,17 +18,15 @@
 // finished score. fp8 operands use the f8f6f4 MFMAs with OCP e4m3 on both
 // sides and unit block scales.
 //
-// Two kernels:
-//  * decode  (few queries, long rows; HBM bound): 32x32 tiles
-//    (v_mfma_f32_32x32x16_bf16 / v_mfma_scale_f32_32x32x64_f8f6f4; a lane
-//    holds 32 heads of one key). A workgroup owns one query and a key chunk;
-//    each wave streams its own 32-key tiles with coalesced loads, two tiles
-//    in flight, through a private LDS slab.
-//  * prefill (many queries; MFMA bound): 16x16 tiles
-//    (v_mfma_f32_16x16x32_bf16 / v_mfma_scale_f32_16x16x128_f8f6f4; a lane
-//    holds 16 heads of one key, so per-query state is small). A workgroup
-//    owns 4 (bf16) or 8 (fp8) queries, one per wave, and a key chunk;
-//    double-buffered 64-key LDS tiles are shared by all its waves.
+// Two kernels, both on 16x16 tiles (v_mfma_f32_16x16x32_bf16 /
+// v_mfma_scale_f32_16x16x128_f8f6f4; a lane holds 16 heads of one key, so
+// per-query state is small):
+//  * decode  (few queries, long rows; HBM bound). A workgroup owns one query
+//    and a key chunk; each wave streams its own keys with B fragments loaded
+//    from HBM straight into registers, 16 KB of keys in flight.
+//  * prefill (many queries; MFMA bound). A workgroup owns 4 (bf16) or 8
+//    (fp8) queries, one per wave, and a key chunk; double-buffered 64-key
+//    LDS tiles are shared by all its waves.
 // Causal tiles that lie wholly past a query's limit are skipped and filled
 // with -inf.
 #include <math.h>
@@ -40,172 +38,8 @@
 namespace xk {
 namespace {
 
-// Row (head) held in register i of lane `lane` by a 32x32 fp32 MFMA result;
-// the column (key) is lane % 32.
-__device__ __forceinline__ int acc_row(int i, int lane) {
-  return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-}
-
-template <bool FP8>
-struct Mma;
-
-template <>
-struct Mma<false> {  // bf16 operands
-  using Frag = bf16x8;                 // 8 bf16 = 16 bytes per lane
-  static constexpr int kSteps = 8;     // 8 x K16 = 128
-  static constexpr int kElemBytes = 2;
-  // First d of the fragment of step s held by lane half hf (A and B alike).
-  __device__ static int dofs(int s, int hf) { return 16 * s + 8 * hf; }
-  __device__ static Frag load(const uint8_t* p) { return *reinterpret_cast<const Frag*>(p); }
-  __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <>
-struct Mma<true> {  // OCP e4m3 operands
-  using Frag = i32x8;                  // 32 fp8 = 32 bytes per lane
-  static constexpr int kSteps = 2;     // 2 x K64 = 128
-  static constexpr int kElemBytes = 1;
-  __device__ static int dofs(int s, int hf) { return 64 * s + 32 * hf; }
-  __device__ static Frag load(const uint8_t* p) {
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 16);
-    return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-  __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
-    // operand formats 0/0 = fp8 e4m3 (OCP); E8M0 block scales 127 = 1.0
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-  }
-};
-
 __device__ __forceinline__ int clamp_limit(const int32_t* limit, int64_t bt, int K) {
   return limit ? min(limit[bt], K - 1) : K - 1;
-}
-
-// ---------------------------------------------------------------------------
-// decode: 1-D grid over (B*T rows) x (key chunks); 4 waves share one query.
-// q (and its head weights) is staged once per workgroup in LDS. Each wave
-// streams its own 32-key tiles with fully coalesced 1 KB loads, two tiles in
-// flight, and turns rows into MFMA B fragments through a private LDS slab;
-// A fragments are read from the staged q. No barrier inside the key loop.
-constexpr int kDecWaves = 4;
-constexpr int kDecTile = 32;
-
-template <bool FP8>
-__global__ __launch_bounds__(256, 2) void logits_decode_kernel(
-    const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
-    const uint8_t* __restrict__ k, const float* __restrict__ k_scale,
-    const float* __restrict__ w, const int32_t* __restrict__ limit,
-    float* __restrict__ out, int T, int K, int keys_per_wg, int n_chunks) {
-  using M = Mma<FP8>;
-  constexpr int kRowBytes = kHeadDim * M::kElemBytes;     // 256 or 128
-  constexpr int kPitch = kRowBytes + 16;                  // padded LDS row
-  constexpr int kLoads = kDecTile * kRowBytes / 1024;     // 1 KB per wave load
-  constexpr int kLanesPerRow = kRowBytes / 16;            // 16 or 8
-  constexpr int kRowsPerLoad = 64 / kLanesPerRow;         // 4 or 8
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kHeads * kPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t slab[kDecWaves][kDecTile * kPitch];
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hf = lane >> 5, col = lane & 31;
-  const int64_t bt = blockIdx.x / n_chunks;  // all chunks of a row are adjacent
-  const int chunk = int(blockIdx.x % n_chunks);
-  const int64_t b = bt / T;
-  const int lim = clamp_limit(limit, bt, K);
-  const int j_begin = chunk * keys_per_wg;
-  const int j_end = min(j_begin + keys_per_wg, K);
-  float* orow = out + bt * K;
-
-  for (int j = max(j_begin, lim + 1) + int(threadIdx.x); j < j_end; j += 256) orow[j] = -INFINITY;
-  const int c_end = min(j_end, lim + 1);  // keys [j_begin, c_end) are scored
-  if (c_end <= j_begin) return;           // uniform over the workgroup
-
-  const uint8_t* kseq = k + b * int64_t(K) * kRowBytes;
-  const float* skseq = FP8 ? k_scale + b * int64_t(K) : nullptr;
-  uint8_t* my = slab[wave];
-  // coalesced tile load: load i covers rows [i*kRowsPerLoad, ...); lane l
-  // takes 16 bytes at offset 16*l of that 1 KB
-  auto gload = [&](int j0, u32x4 (&r)[kLoads]) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int row = min(j0 + i * kRowsPerLoad + lane / kLanesPerRow, K - 1);
-      r[i] = *reinterpret_cast<const u32x4*>(kseq + int64_t(row) * kRowBytes +
-                                             (lane % kLanesPerRow) * 16);
-    }
-  };
-  auto lds_put = [&](const u32x4 (&r)[kLoads]) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int row = i * kRowsPerLoad + lane / kLanesPerRow;
-      *reinterpret_cast<u32x4*>(my + row * kPitch + (lane % kLanesPerRow) * 16) = r[i];
-    }
-  };
-
-  constexpr int kStride = kDecWaves * kDecTile;
-  u32x4 buf0[kLoads], buf1[kLoads];
-  int j0 = j_begin + wave * kDecTile;
-  if (j0 < c_end) gload(j0, buf0);
-  if (j0 + kStride < c_end) gload(j0 + kStride, buf1);
-
-  // stage q while the first tiles are in flight
-  const uint8_t* qsrc = q + bt * (kHeads * kRowBytes);
-  for (int c = threadIdx.x; c < kHeads * kLanesPerRow; c += 256) {
-    const int r = c / kLanesPerRow, cc = c % kLanesPerRow;
-    *reinterpret_cast<u32x4*>(q_lds + r * kPitch + cc * 16) =
-        *reinterpret_cast<const u32x4*>(qsrc + r * kRowBytes + cc * 16);
-  }
-  float wr[2][16];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int h = 32 * mt + acc_row(i, lane);
-      wr[mt][i] = FP8 ? w[bt * kHeads + h] * q_scale[bt * kHeads + h] : w[bt * kHeads + h];
-    }
-  __syncthreads();
-
-  auto score = [&](int jt) {
-    f32x16 acc0 = {}, acc1 = {};
-    const uint8_t* brow = my + col * kPitch;
-    const uint8_t* arow0 = q_lds + col * kPitch;
-    const uint8_t* arow1 = q_lds + (32 + col) * kPitch;
-#pragma unroll
-    for (int s = 0; s < M::kSteps; ++s) {
-      const int off = M::dofs(s, hf) * M::kElemBytes;
-      const typename M::Frag bfr = M::load(brow + off);
-      acc0 = M::mma(M::load(arow0 + off), bfr, acc0);
-      acc1 = M::mma(M::load(arow1 + off), bfr, acc1);
-    }
-    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      p0 = fmaf(wr[0][i], fmaxf(acc0[i], 0.f), p0);
-      p1 = fmaf(wr[0][i + 1], fmaxf(acc0[i + 1], 0.f), p1);
-      p2 = fmaf(wr[1][i], fmaxf(acc1[i], 0.f), p2);
-      p3 = fmaf(wr[1][i + 1], fmaxf(acc1[i + 1], 0.f), p3);
-    }
-    float tot = (p0 + p1) + (p2 + p3);
-    tot += __shfl_xor(tot, 32);
-    const int j = jt + col;
-    if (hf == 0 && j < c_end) {
-      if (FP8) tot *= skseq[j];
-      orow[j] = tot;
-    }
-  };
-
-  // two tiles in flight; the loop body handles them alternately
-  while (j0 < c_end) {
-    lds_put(buf0);
-    if (j0 + 2 * kStride < c_end) gload(j0 + 2 * kStride, buf0);
-    score(j0);
-    j0 += kStride;
-    if (j0 >= c_end) break;
-    lds_put(buf1);
-    if (j0 + 2 * kStride < c_end) gload(j0 + 2 * kStride, buf1);
-    score(j0);
-    j0 += kStride;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -311,6 +145,165 @@ __device__ __forceinline__ float subtile_total(const float (&p)[4], int lane) {
   // xor 16: even groups keep the first, odd groups the second
   const float keep = up16 ? a1 : a0, send = up16 ? a0 : a1;
   return keep + __shfl_xor(send, 16);
+}
+
+
+// ---------------------------------------------------------------------------
+// decode: 1-D grid over (B*T rows) x (key chunks); a workgroup owns one query
+// and a key chunk, split into one contiguous range per wave. q and its head
+// weights are staged once in LDS and then held by every wave as A fragments
+// in registers. Each wave streams its keys as 16-key subtiles whose B
+// fragments are loaded from HBM straight into registers (lane l: key l%16,
+// the 16-byte pieces of d named by Mma16::dofs), 16 KB in flight per wave;
+// 64 keys (four subtiles) make one coalesced 256-byte store. No LDS traffic
+// and no barrier inside the key loop.
+constexpr int kDecWaves = 4;
+constexpr int kDecGroup = 64;  // keys per store: four 16-key subtiles
+
+template <bool FP8>
+__global__ __launch_bounds__(kDecWaves * 64, 2) void logits_decode_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
+    const uint8_t* __restrict__ k, const float* __restrict__ k_scale,
+    const float* __restrict__ w, const int32_t* __restrict__ limit,
+    float* __restrict__ out, int T, int K, int keys_per_wg, int n_chunks) {
+  using M = Mma16<FP8>;
+  using Frag = typename M::Frag;
+  constexpr int kRowBytes = kHeadDim * M::kElemBytes;  // 256 or 128
+  constexpr int kPitch = kRowBytes + 16;               // padded LDS row
+  constexpr int kLanesPerRow = kRowBytes / 16;
+  constexpr int kDecRing = 16 * 1024 / (16 * kRowBytes);  // subtiles in flight: 4 or 8
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kHeads * kPitch];
+  __shared__ __attribute__((aligned(16))) float w_lds[kHeads];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int64_t bt = blockIdx.x / n_chunks;  // all chunks of a row are adjacent
+  const int chunk = int(blockIdx.x % n_chunks);
+  const int64_t b = bt / T;
+  const int lim = clamp_limit(limit, bt, K);
+  const int j_begin = chunk * keys_per_wg;
+  const int j_end = min(j_begin + keys_per_wg, K);
+  float* orow = out + bt * K;
+
+  for (int j = max(j_begin, lim + 1) + int(threadIdx.x); j < j_end; j += kDecWaves * 64)
+    orow[j] = -INFINITY;
+  const int c_end = min(j_end, lim + 1);  // keys [j_begin, c_end) are scored
+  if (c_end <= j_begin) return;           // uniform over the workgroup
+
+  const int per_wave = keys_per_wg / kDecWaves;  // a multiple of kDecGroup
+  // wave-uniform in scalar registers, so the buffer descriptors below are too
+  const int w_begin = j_begin + __builtin_amdgcn_readfirstlane(wave) * per_wave;
+  const int n_keys = max(0, min(w_begin + per_wave, c_end) - w_begin);  // this wave's keys
+  // the wave's keys, key scales and outputs as range-checked buffers: loads
+  // past the wave's last key read 0 and stores there are dropped, so the
+  // prefetch ring and the ragged tail need no branch (a fixed count of
+  // memory operations per iteration keeps the waits exact)
+  const auto krs = make_rsrc(k + (b * int64_t(K) + w_begin) * kRowBytes, n_keys * kRowBytes);
+  const auto srs = make_rsrc(FP8 ? k_scale + b * int64_t(K) + w_begin : nullptr, FP8 ? n_keys * 4 : 0);
+  const auto ors = make_rsrc(orow + w_begin, n_keys * 4);
+
+  // q chunks and head weights first, so that waiting for them does not wait
+  // for the key ring issued after them
+  constexpr int kQLoads = kHeads * kLanesPerRow / (kDecWaves * 64);
+  const uint8_t* qsrc = q + bt * (kHeads * kRowBytes);
+  u32x4 qv[kQLoads];
+#pragma unroll
+  for (int i = 0; i < kQLoads; ++i) {
+    const int c = int(threadIdx.x) + kDecWaves * 64 * i;
+    qv[i] = *reinterpret_cast<const u32x4*>(qsrc + (c / kLanesPerRow) * kRowBytes + (c % kLanesPerRow) * 16);
+  }
+  float wv = 0.f;
+  if (threadIdx.x < kHeads) {
+    const int h = threadIdx.x;
+    wv = FP8 ? w[bt * kHeads + h] * q_scale[bt * kHeads + h] : w[bt * kHeads + h];
+  }
+
+  // B fragments of the subtile whose first key is jj (relative to w_begin)
+  Frag buf[kDecRing][M::kSteps];
+  auto gload = [&](int jj, Frag (&f)[M::kSteps]) {
+    const int base = (jj + r) * kRowBytes;
+#pragma unroll
+    for (int s = 0; s < M::kSteps; ++s) {
+      const int off = base + M::dofs(s, g) * M::kElemBytes;
+      if constexpr (FP8) {
+        const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+        const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 16, 0, 0);
+        f[s] = Frag{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]),
+                    int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+      } else {
+        f[s] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+      }
+    }
+  };
+  float sk[kDecRing / 4];  // fp8: scale of key (group start + lane)
+  auto sload = [&](int jg) {
+    return FP8 ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, (jg + lane) * 4, 0, 0))
+               : 1.f;
+  };
+#pragma unroll
+  for (int i = 0; i < kDecRing; ++i) gload(16 * i, buf[i]);
+#pragma unroll
+  for (int i = 0; i < kDecRing / 4; ++i) sk[i] = sload(kDecGroup * i);
+
+#pragma unroll
+  for (int i = 0; i < kQLoads; ++i) {
+    const int c = int(threadIdx.x) + kDecWaves * 64 * i;
+    *reinterpret_cast<u32x4*>(q_lds + (c / kLanesPerRow) * kPitch + (c % kLanesPerRow) * 16) = qv[i];
+  }
+  if (threadIdx.x < kHeads) w_lds[threadIdx.x] = wv;
+  __syncthreads();
+  Frag a[4][M::kSteps];  // [M-tile][step]
+  float wr[4][4];        // head 16*mt + 4*g + i
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int s = 0; s < M::kSteps; ++s)
+      a[mt][s] = M::load(q_lds + (16 * mt + r) * kPitch + M::dofs(s, g) * M::kElemBytes);
+    const f32x4 w4 = *reinterpret_cast<const f32x4*>(&w_lds[16 * mt + 4 * g]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wr[mt][i] = w4[i];
+  }
+  // this lane's 16-head partial score of key (subtile start + r)
+  auto partial = [&](const Frag (&bf)[M::kSteps]) {
+    f32x4 acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < M::kSteps; ++s) acc[mt] = M::mma(a[mt][s], bf[s], acc[mt]);
+    }
+    float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      p0 = fmaf(wr[mt][0], fmaxf(acc[mt][0], 0.f), p0);
+      p1 = fmaf(wr[mt][1], fmaxf(acc[mt][1], 0.f), p1);
+      p0 = fmaf(wr[mt][2], fmaxf(acc[mt][2], 0.f), p0);
+      p1 = fmaf(wr[mt][3], fmaxf(acc[mt][3], 0.f), p1);
+    }
+    return p0 + p1;
+  };
+
+  for (int j0 = 0; j0 < n_keys; j0 += 16 * kDecRing) {
+#pragma unroll
+    for (int grp = 0; grp < kDecRing / 4; ++grp) {
+      const int jg = j0 + kDecGroup * grp;
+      float p[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int slot = 4 * grp + st;
+        p[st] = partial(buf[slot]);
+        gload(jg + 16 * st + 16 * kDecRing, buf[slot]);  // the slot's next subtile
+        // keep the refill here: sunk to the end of the loop, all refills
+        // would be waited for together and the ring would not overlap
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const float s_key = sk[grp];
+      sk[grp] = sload(jg + 16 * kDecRing);
+      const float tot = subtile_total(p, lane);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, FP8 ? tot * s_key : tot), ors,
+                                            (jg + lane) * 4, 0, 0);
+    }
+  }
 }
 
 // prefill grid: 1-D over (query blocks, longest causal rows first) x B x
@@ -441,11 +434,14 @@ hipError_t launch_logits(const void* q, const float* q_scale, const void* k,
   const auto* q8 = static_cast<const uint8_t*>(q);
   const auto* k8 = static_cast<const uint8_t*>(k);
   if (T < 8) {
-    // one query per workgroup; ~512 workgroups, chunks a multiple of 4 waves x 64 keys
+    // one query per workgroup; chunks of 512 or 768 keys (a multiple of four
+    // waves x 64). Short chunks keep a workgroup's life short next to the
+    // kernel's, so ragged rows balance across CUs (measured on the Flash
+    // and Pro decode shapes: 512 / 768 beat 1024 and 2048 there)
     const int64_t rows = int64_t(B) * T;
-    int64_t per = (int64_t(K) * rows + 511) / 512;
-    int kpw = int(std::min<int64_t>(std::max<int64_t>(per, 512), K));
-    kpw = round_up(kpw, kDecWaves * kDecTile);
+    const int64_t per = (int64_t(K) * rows + 2047) / 2048;
+    int kpw = int(std::min<int64_t>(std::max<int64_t>(per, 2 * kDecWaves * kDecGroup), 3 * kDecWaves * kDecGroup));
+    kpw = std::min(round_up(kpw, kDecWaves * kDecGroup), round_up(K, kDecWaves * kDecGroup));
     const int nch = (K + kpw - 1) / kpw;
     const dim3 grid(unsigned(rows * nch));
     if (fp8)

@@ -18,6 +18,14 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
+// Raw buffer resource over [base, base + bytes): the hardware range check
+// makes loads at or past `bytes` return 0 and drops such stores, with no
+// branch and no memory access (dword 3 = 0x00020000: 32-bit data format,
+// the raw-buffer setting of gfx9-family parts).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
 // Host-side launchers (one per translation unit). Arguments are validated by
 // the C ABI layer before these run; they only enqueue work and return the
 // launch status.

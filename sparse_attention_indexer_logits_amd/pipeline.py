@@ -1,49 +1,51 @@
 """The whole indexer hot path on one stream: logits -> top-k -> mxfp4 gather.
 
-IndexerStep preallocates every output once, so repeated calls only enqueue
-the three kernels of libxk (no allocation, no host synchronisation).
+IndexerStep preallocates every output and validates every argument once, so
+repeated calls only enqueue the three kernels of libxk (no allocation, no
+host synchronisation, no per-call checks). The calls can also be captured
+into a HIP graph (torch.cuda.graph) and replayed.
 """
 from __future__ import annotations
 
 import torch
 
-from . import xk_indexer_logits, xk_indexer_topk, xk_mxfp4_paged_gather, \
-    xk_indexer_topk_workspace_size
+from . import _check, _lib, _stream, gather_args, logits_args, topk_args
 
 
 class IndexerStep:
+    """One batch's launches. `outputs` = (logits, idx, gathered) of another
+    step with the same shapes makes this step write into those buffers."""
+
     def __init__(self, q, k, w, limit, topk, kv_fp4, kv_scale, block_table, row_seq,
-                 q_scale=None, k_scale=None):
+                 q_scale=None, k_scale=None, outputs=None):
         self.q, self.k, self.w, self.limit = q, k, w, limit
         self.q_scale, self.k_scale = q_scale, k_scale
         self.topk = topk
         self.kv_fp4, self.kv_scale = kv_fp4, kv_scale
         self.block_table, self.row_seq = block_table, row_seq
-        B, T = q.shape[0], q.shape[1]
-        K = k.shape[1]
-        dev = q.device
-        self.logits = torch.empty((B, T, K), dtype=torch.float32, device=dev)
-        self.idx = torch.empty((B * T, topk), dtype=torch.int32, device=dev)
-        self.gathered = torch.empty((B * T, topk, 2 * kv_fp4.shape[2]), dtype=torch.int16,
-                                    device=dev)
-        ws = xk_indexer_topk_workspace_size(B * T, K, topk)
-        self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
+        lg, ix, ga = outputs if outputs is not None else (None, None, None)
+        self._logits_args, self.logits = logits_args(q, k, w, limit, q_scale, k_scale, out=lg)
+        self._topk_args, self.idx, self.workspace = topk_args(self.logits, topk, limit, out=ix)
+        self._gather_args, self.gathered = gather_args(kv_fp4, kv_scale, block_table, self.idx,
+                                                       row_seq, out=ga)
+
+    def outputs(self):
+        return self.logits, self.idx, self.gathered
 
     def run_logits(self, stream=None):
-        return xk_indexer_logits(self.q, self.k, self.w, self.limit, self.q_scale, self.k_scale,
-                                 out=self.logits, stream=stream)
+        _check(_lib.xk_indexer_logits(*self._logits_args, _stream(stream)))
+        return self.logits
 
     def run_topk(self, stream=None):
-        return xk_indexer_topk(self.logits, self.topk, self.limit, out=self.idx,
-                               workspace=self.workspace, stream=stream)
+        _check(_lib.xk_indexer_topk(*self._topk_args, _stream(stream)))
+        return self.idx
 
-    def run_gather(self, sel_pos=None, stream=None):
-        return xk_mxfp4_paged_gather(self.kv_fp4, self.kv_scale, self.block_table,
-                                     self.idx if sel_pos is None else sel_pos, self.row_seq,
-                                     out=self.gathered, stream=stream)
+    def run_gather(self, stream=None):
+        _check(_lib.xk_mxfp4_paged_gather(*self._gather_args, _stream(stream)))
+        return self.gathered
 
     def __call__(self, stream=None):
         self.run_logits(stream)
         self.run_topk(stream)
-        self.run_gather(stream=stream)
+        self.run_gather(stream)
         return self.logits, self.idx, self.gathered
