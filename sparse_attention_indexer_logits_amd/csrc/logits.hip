@@ -175,7 +175,9 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void logits_decode_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kHeads * kPitch];
   __shared__ __attribute__((aligned(16))) float w_lds[kHeads];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index in a scalar register: per-wave values derived from it
+  // (rows, buffer descriptors) then stay scalar
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r = lane & 15;
   const int64_t bt = blockIdx.x / n_chunks;  // all chunks of a row are adjacent
   const int chunk = int(blockIdx.x % n_chunks);
@@ -191,8 +193,7 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void logits_decode_kernel(
   if (c_end <= j_begin) return;           // uniform over the workgroup
 
   const int per_wave = keys_per_wg / kDecWaves;  // a multiple of kDecGroup
-  // wave-uniform in scalar registers, so the buffer descriptors below are too
-  const int w_begin = j_begin + __builtin_amdgcn_readfirstlane(wave) * per_wave;
+  const int w_begin = j_begin + wave * per_wave;
   const int n_keys = max(0, min(w_begin + per_wave, c_end) - w_begin);  // this wave's keys
   // the wave's keys, key scales and outputs as range-checked buffers: loads
   // past the wave's last key read 0 and stores there are dropped, so the
@@ -328,7 +329,9 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
   static_assert(kPer >= 1 && kPrefillTile * kChunks % kThreads == 0, "tile split");
   __shared__ __attribute__((aligned(16))) uint8_t tile[2][kPrefillTile * kPitch];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index in a scalar register: per-wave values derived from it
+  // (rows, buffer descriptors) then stay scalar
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r = lane & 15;
   const int chunk = int(blockIdx.x % n_chunks);
   const int rest = int(blockIdx.x / n_chunks);
@@ -360,30 +363,40 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
     }
   }
   if (c_end <= j_begin) return;  // uniform over the workgroup
-  int w_end = q_end[0];
-#pragma unroll
-  for (int qi = 1; qi < QW; ++qi) w_end = max(w_end, q_end[qi]);
 
   const uint8_t* kseq = k + b * int64_t(K) * kRowBytes;
   const float* skseq = FP8 ? k_scale + b * int64_t(K) : nullptr;
-  u32x4 pre[kPer];
-  auto gload = [&](int j0) {
+  // Two tiles in flight through registers: at the start of tile t the free
+  // register buffer starts loading tile t+2; at its end the other buffer,
+  // holding tile t+1 (issued at the start of tile t-1), goes to LDS. Loads
+  // clamp to the last key and stores go through range-checked buffers, so
+  // the loop has no data-dependent memory branch and the waits stay exact.
+  u32x4 pre[2][kPer];
+  float skp[2];  // fp8: key scale of key (tile start + lane)
+  auto gload = [&](int j0, u32x4 (&dst)[kPer], float& sk) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int c = int(threadIdx.x) + kThreads * i;
       const int row = min(j0 + c / kChunks, K - 1);
-      pre[i] = *reinterpret_cast<const u32x4*>(kseq + int64_t(row) * kRowBytes + (c % kChunks) * 16);
+      dst[i] = *reinterpret_cast<const u32x4*>(kseq + int64_t(row) * kRowBytes + (c % kChunks) * 16);
     }
+    if constexpr (FP8) sk = skseq[min(j0 + lane, K - 1)];
   };
-  auto lds_put = [&](uint8_t* dst) {
+  auto lds_put = [&](uint8_t* dst, const u32x4 (&src)[kPer]) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int c = int(threadIdx.x) + kThreads * i;
-      *reinterpret_cast<u32x4*>(dst + (c / kChunks) * kPitch + (c % kChunks) * 16) = pre[i];
+      *reinterpret_cast<u32x4*>(dst + (c / kChunks) * kPitch + (c % kChunks) * 16) = src[i];
     }
   };
+  __amdgpu_buffer_rsrc_t ors[QW];  // this chunk's outputs of each query, up to its limit
+#pragma unroll
+  for (int qi = 0; qi < QW; ++qi)
+    ors[qi] = make_rsrc(out + bt[qi] * K + j_begin, max(0, q_end[qi] - j_begin) * 4);
 
-  gload(j_begin);
+  // q fragments and head weights are loaded before the key tiles: memory
+  // waits count in issue order, so waiting for them (at their first use,
+  // inside the loop) must not also wait for tiles in flight
   Query16<FP8> qr[QW];
 #pragma unroll
   for (int qi = 0; qi < QW; ++qi) {
@@ -393,34 +406,44 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
     else
       qr[qi].zero();
   }
-  lds_put(tile[0]);
+  gload(j_begin, pre[0], skp[0]);
+  gload(j_begin + kPrefillTile, pre[1], skp[1]);
+  lds_put(tile[0], pre[0]);
   __syncthreads();
 
-  int cur = 0;
-  for (int j0 = j_begin; j0 < c_end; j0 += kPrefillTile, cur ^= 1) {
-    const bool more = j0 + kPrefillTile < c_end;  // uniform
-    if (more) gload(j0 + kPrefillTile);
-    if (j0 < w_end) {
-      float p[QW][4];
+  // tile at j0 in tile[cur]; `fill` (free) starts loading the tile two
+  // ahead, `hold` (the next tile, issued a step earlier) goes to LDS at the
+  // end. The same memory operations run every step: refills past the chunk
+  // read the last key again and stores past a query's limit are dropped.
+  auto step = [&](int j0, int cur, u32x4 (&fill)[kPer], float& sk_fill, const u32x4 (&hold)[kPer]) {
+    const float sk = sk_fill;  // this tile's key scales, loaded with it
+    gload(j0 + 2 * kPrefillTile, fill, sk_fill);
+    float p[QW][4];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        typename M::Frag bf[M::kSteps];
-        const uint8_t* lrow = tile[cur] + (16 * st + r) * kPitch;
+    for (int st = 0; st < 4; ++st) {
+      typename M::Frag bf[M::kSteps];
+      const uint8_t* lrow = tile[cur] + (16 * st + r) * kPitch;
 #pragma unroll
-        for (int s = 0; s < M::kSteps; ++s) bf[s] = M::load(lrow + M::dofs(s, g) * M::kElemBytes);
+      for (int s = 0; s < M::kSteps; ++s) bf[s] = M::load(lrow + M::dofs(s, g) * M::kElemBytes);
 #pragma unroll
-        for (int qi = 0; qi < QW; ++qi) p[qi][st] = qr[qi].partial(bf);
-      }
-      const int j = j0 + lane;
-      const float sk = FP8 && j < w_end ? skseq[j] : 1.f;
-#pragma unroll
-      for (int qi = 0; qi < QW; ++qi) {
-        const float tot = subtile_total(p[qi], lane);
-        if (j < q_end[qi]) out[bt[qi] * K + j] = FP8 ? tot * sk : tot;
-      }
+      for (int qi = 0; qi < QW; ++qi) p[qi][st] = qr[qi].partial(bf);
     }
-    if (more) lds_put(tile[cur ^ 1]);
+#pragma unroll
+    for (int qi = 0; qi < QW; ++qi) {
+      const float tot = subtile_total(p[qi], lane);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, FP8 ? tot * sk : tot),
+                                            ors[qi], (j0 - j_begin + lane) * 4, 0, 0);
+    }
+    lds_put(tile[cur ^ 1], hold);
     __syncthreads();
+  };
+  // Both steps of an iteration always run (an odd last tile is followed by
+  // one redundant tile whose stores are all dropped): with no loop exit
+  // between a refill and its use, the compiler cannot sink the refill next
+  // to that use, which would expose its latency.
+  for (int j0 = j_begin; j0 < c_end; j0 += 2 * kPrefillTile) {
+    step(j0, 0, pre[0], skp[0], pre[1]);
+    step(j0 + kPrefillTile, 1, pre[1], skp[1], pre[0]);
   }
 }
 
