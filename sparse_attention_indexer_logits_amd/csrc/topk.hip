@@ -590,46 +590,54 @@ __device__ __forceinline__ void select_list(TopkShared<BLOCK, CAP>& sh, int nc, 
   }
 }
 
-// Loads of the chunk of BLOCK*U entries of x starting at base (this
-// thread's entries base + BLOCK*u + tid below j_hi).
-template <int BLOCK, int U>
-__device__ __forceinline__ void load_chunk(const float* __restrict__ x, int base, int j_hi, float (&c)[U]) {
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int j = base + BLOCK * u + int(threadIdx.x);
-    c[u] = j < j_hi ? x[j] : 0.f;
-  }
+// Row scores through a range-checked buffer descriptor (make_rsrc over the
+// row's first `len` scores): a load past the end reads 0 with no memory
+// access and no branch, so every load of a loop is issued unconditionally
+// and the compiler's wait counts stay exact (a load inside a branch is
+// waited for right there, which serialises a row's loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float* row, int len) {
+  return make_rsrc(row, len * 4);
 }
 
-// chunks(g) over entries [j_lo, j_hi) of x streamed from memory, BLOCK*U per
-// chunk, the next chunk's loads in flight while this one is processed. cur
-// holds the first chunk's loads (load_chunk at j_lo), issued by the caller
-// as early as it likes.
+__device__ __forceinline__ float load_score(__amdgpu_buffer_rsrc_t rs, int j) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, j * 4, 0, 0));
+}
+
+// Loads of the chunk of BLOCK*U entries starting at base (this thread's
+// entries base + BLOCK*u + tid).
+template <int BLOCK, int U>
+__device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t rs, int base, float (&c)[U]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) c[u] = load_score(rs, base + BLOCK * u + int(threadIdx.x));
+}
+
+// chunks(g) over entries [j_lo, j_hi) of the row streamed from memory,
+// BLOCK*U per chunk, two register buffers alternating: the next chunk's
+// loads are in flight while this one is processed. `first` holds the first
+// chunk's loads (load_chunk at j_lo), issued by the caller as early as it
+// likes; rs covers at least [0, j_hi) (and reads 0 past its end). Each
+// iteration processes two chunks unconditionally (entries past j_hi are
+// masked): with no exit between a load and its use, the compiler issues the
+// loads where they stand instead of next to their use.
 template <int BLOCK, int U, typename G>
-__device__ __forceinline__ void stream_chunks(const float* __restrict__ x, int j_lo, int j_hi, float (&cur)[U],
+__device__ __forceinline__ void stream_chunks(__amdgpu_buffer_rsrc_t rs, int j_lo, int j_hi, float (&first)[U],
                                               G g) {
   const int tid = threadIdx.x;
-  uint32_t kv[U];
   float nxt[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) nxt[u] = 0.f;
-  for (int base = j_lo; base < j_hi; base += BLOCK * U) {
-    const int nb = base + BLOCK * U;
-    if (nb < j_hi) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = nb + BLOCK * u + tid;
-        nxt[u] = j < j_hi ? x[j] : 0.f;
-      }
-    }
+  auto process = [&](const float (&c)[U], int base) {
+    uint32_t kv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = base + BLOCK * u + tid;
-      kv[u] = j < j_hi ? order_key(cur[u]) : 0u;
+      kv[u] = j < j_hi ? order_key(c[u]) : 0u;
     }
     g([&](int u) { return kv[u]; }, [&](int u) { return uint32_t(base + BLOCK * u + tid); });
-#pragma unroll
-    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+  };
+  for (int base = j_lo; base < j_hi; base += 2 * BLOCK * U) {
+    load_chunk<BLOCK, U>(rs, base + BLOCK * U, nxt);
+    process(first, base);
+    load_chunk<BLOCK, U>(rs, base + 2 * BLOCK * U, first);
+    process(nxt, base + BLOCK * U);
   }
 }
 
@@ -659,13 +667,14 @@ template <int BLOCK, int CAP>
 __device__ __forceinline__ void radix_topk(TopkShared<BLOCK, CAP>& sh, const float* __restrict__ x,
                                            int n, int k, int32_t* __restrict__ orow) {
   constexpr int U = 2;
+  const auto rs = row_rsrc(x, n);
   auto all_chunks = [&](auto g) {
     for (int base = 0; base < n; base += BLOCK * U) {
       uint32_t kv[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j = base + BLOCK * u + int(threadIdx.x);
-        kv[u] = j < n ? order_key(x[j]) : 0u;
+        kv[u] = j < n ? order_key(load_score(rs, j)) : 0u;
       }
       g([&](int u) { return kv[u]; }, [&](int u) { return uint32_t(base + BLOCK * u + int(threadIdx.x)); });
     }
@@ -686,11 +695,7 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ l
   const int64_t row = blockIdx.x;
   const float* x = logits + row * K;
   float raw[V];  // issued before the limit arrives; keys past it are masked below
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int j = tid + BLOCK * v;
-    raw[v] = j < K ? x[j] : 0.f;
-  }
+  load_chunk<BLOCK, V>(row_rsrc(x, K), 0, raw);
   const int n = limit ? max(0, min(limit[row], K - 1) + 1) : K;
   uint32_t key[V];
 #pragma unroll
@@ -742,7 +747,7 @@ template <int BLOCK, int V, int CAP>
 __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restrict__ logits,
                                                           const int32_t* __restrict__ limit,
                                                           int32_t* __restrict__ idx, int K, int k) {
-  constexpr int U = 8;            // streamed entries per thread per chunk
+  constexpr int U = 16;           // streamed entries per thread per chunk
   constexpr int L = CAP / BLOCK;  // list entries per thread
   static_assert(CAP % BLOCK == 0, "list spread evenly over the block");
   __shared__ TopkShared<BLOCK, CAP> sh;
@@ -752,14 +757,14 @@ __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restric
   const int prefix = min(n, BLOCK * V);
   const float* x = logits + row * K;
   int32_t* orow = idx + row * k;
+  const auto rs = row_rsrc(x, n);
+  float raw[V];
+  load_chunk<BLOCK, V>(rs, 0, raw);
+  float first[U];  // the streamed part's first chunk, in flight during the prefix's threshold
+  load_chunk<BLOCK, U>(rs, prefix, first);
   uint32_t key[V];
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int j = tid + BLOCK * v;
-    key[v] = j < prefix ? order_key(x[j]) : 0u;
-  }
-  float first[U];  // the streamed part's first chunk, in flight during the prefix's threshold
-  load_chunk<BLOCK, U>(x, prefix, n, first);
+  for (int v = 0; v < V; ++v) key[v] = tid + BLOCK * v < prefix ? order_key(raw[v]) : 0u;
   auto key_at = [&](int v) { return key[v]; };
   auto j_at = [&](int v) { return uint32_t(tid + BLOCK * v); };
   if (n <= prefix) {
@@ -774,7 +779,7 @@ __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restric
   const int bstar = sh.digit;
   auto admit = [&](uint32_t kv) { return kv != 0u && bins(kv) >= bstar; };
   append_list<BLOCK, CAP, V>(sh, key_at, j_at, admit);
-  stream_chunks<BLOCK, U>(x, prefix, n, first, [&](auto kat, auto jat) {
+  stream_chunks<BLOCK, U>(rs, prefix, n, first, [&](auto kat, auto jat) {
     append_list<BLOCK, CAP, U>(sh, kat, jat, admit);
   });
   __syncthreads();
