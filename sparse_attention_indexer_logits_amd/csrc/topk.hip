@@ -125,6 +125,7 @@ struct TopkShared {
   int digit, above, at;
   int ccount;    // candidate list: entries claimed so far
   int overflow;  // 1 if the candidate list ran out of room
+  uint32_t tau;  // long rows: smallest prefix key in a bin >= b*
 };
 
 // Wave 0: find the bin that holds the `need`-th element of hist[0..NBINS),
@@ -611,8 +612,10 @@ __device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t rs, int base, 
   for (int u = 0; u < U; ++u) c[u] = load_score(rs, base + BLOCK * u + int(threadIdx.x));
 }
 
-// chunks(g) over entries [j_lo, j_hi) of the row streamed from memory,
-// BLOCK*U per chunk, two register buffers alternating: the next chunk's
+// g(scores, base) over chunks of entries [j_lo, j_hi) of the row streamed
+// from memory (entry u of this thread is j = base + BLOCK*u + tid; the
+// caller masks j >= j_hi), BLOCK*U per chunk, two register buffers
+// alternating: the next chunk's
 // loads are in flight while this one is processed. `first` holds the first
 // chunk's loads (load_chunk at j_lo), issued by the caller as early as it
 // likes; rs covers at least [0, j_hi) (and reads 0 past its end). Each
@@ -622,22 +625,12 @@ __device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t rs, int base, 
 template <int BLOCK, int U, typename G>
 __device__ __forceinline__ void stream_chunks(__amdgpu_buffer_rsrc_t rs, int j_lo, int j_hi, float (&first)[U],
                                               G g) {
-  const int tid = threadIdx.x;
   float nxt[U];
-  auto process = [&](const float (&c)[U], int base) {
-    uint32_t kv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = base + BLOCK * u + tid;
-      kv[u] = j < j_hi ? order_key(c[u]) : 0u;
-    }
-    g([&](int u) { return kv[u]; }, [&](int u) { return uint32_t(base + BLOCK * u + tid); });
-  };
   for (int base = j_lo; base < j_hi; base += 2 * BLOCK * U) {
     load_chunk<BLOCK, U>(rs, base + BLOCK * U, nxt);
-    process(first, base);
+    g(first, base);
     load_chunk<BLOCK, U>(rs, base + 2 * BLOCK * U, first);
-    process(nxt, base + BLOCK * U);
+    g(nxt, base + BLOCK * U);
   }
 }
 
@@ -706,17 +699,17 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ l
   radix_topk<BLOCK, CAP>(sh, x, n, k, idx + row * k);
 }
 
-// Append the entries of a chunk that pass take(key) to the LDS list
-// ckey / cj: one ballot and one LDS atomic per wave and entry index. The
-// list order depends on the atomics, which nothing downstream relies on.
+// Append the entries u of a chunk with take(u) to the LDS list ckey / cj
+// (key_at / j_at are evaluated for taken entries only): one ballot and one
+// LDS atomic per wave and entry index. The list order depends on the
+// atomics, which nothing downstream relies on.
 template <int BLOCK, int CAP, int U, typename KeyAt, typename JAt, typename Take>
 __device__ __forceinline__ void append_list(TopkShared<BLOCK, CAP>& sh, KeyAt key_at, JAt j_at,
                                             Take take_it) {
   const int lane = lane_id();
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint32_t kv = key_at(u);
-    const bool take = take_it(kv);
+    const bool take = take_it(u);
     const uint64_t m = __ballot(take);
     if (m == 0) continue;
     const int leader = __ffsll((unsigned long long)m) - 1;
@@ -726,7 +719,7 @@ __device__ __forceinline__ void append_list(TopkShared<BLOCK, CAP>& sh, KeyAt ke
     if (take) {
       const int pos = base + prefix_in_wave(m);
       if (pos < CAP) {
-        sh.ckey[pos] = kv;
+        sh.ckey[pos] = key_at(u);
         sh.cj[pos] = j_at(u);
       } else {
         sh.overflow = 1;
@@ -736,12 +729,12 @@ __device__ __forceinline__ void append_list(TopkShared<BLOCK, CAP>& sh, KeyAt ke
 }
 
 // Longer rows. The first BLOCK*V keys are held in registers; their
-// histogram gives the bin b* that holds the prefix's k-th largest key.
-// The row's k-th largest key is at least the prefix's (the prefix is part
-// of the row), so every winner of the row lies in a bin >= b* under the
-// prefix's bin map: those prefix keys, and the keys of the rest of the row
-// (streamed once) that land there, form an LDS candidate list, from which
-// the winners are selected exactly. If the list runs out of room (scores
+// histogram gives the bin b* that holds the prefix's k-th largest key, and
+// tau, the smallest prefix key in a bin >= b*, is at most that key. The
+// row's k-th largest key is at least the prefix's (the prefix is part of
+// the row), so every winner of the row is >= tau: the prefix keys in bins
+// >= b* and the keys >= tau of the rest of the row (streamed once) form an
+// LDS candidate list, from which the winners are selected exactly. If the list runs out of room (scores
 // crowded into b*), the row falls back to multi-pass streaming selection.
 template <int BLOCK, int V, int CAP>
 __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restrict__ logits,
@@ -774,13 +767,29 @@ __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restric
   if (tid == 0) {
     sh.ccount = 0;
     sh.overflow = 0;
+    sh.tau = 0xFFFFFFFFu;
   }
   const ValueBins bins = bucket_threshold<BLOCK, CAP, V>(sh, key_at, k);
   const int bstar = sh.digit;
-  auto admit = [&](uint32_t kv) { return kv != 0u && bins(kv) >= bstar; };
-  append_list<BLOCK, CAP, V>(sh, key_at, j_at, admit);
-  stream_chunks<BLOCK, U>(rs, prefix, n, first, [&](auto kat, auto jat) {
-    append_list<BLOCK, CAP, U>(sh, kat, jat, admit);
+  // prefix keys in bins >= b* join the list; tau, the smallest of them, is
+  // at most the prefix's k-th largest key
+  uint32_t mn = 0xFFFFFFFFu, unused = 0u;
+  append_list<BLOCK, CAP, V>(sh, key_at, j_at, [&](int v) {
+    const bool t = key[v] != 0u && bins(key[v]) >= bstar;
+    if (t) mn = min(mn, key[v]);
+    return t;
+  });
+  wave_min_max(mn, unused);
+  if (lane_id() == 0) atomicMin(&sh.tau, mn);
+  __syncthreads();
+  // streamed keys >= tau join too (score >= value(tau): order keys are
+  // monotone in the score, so one float compare per key, and only joining
+  // keys are converted)
+  const float tau_f = key_value(sh.tau);
+  stream_chunks<BLOCK, U>(rs, prefix, n, first, [&](const float (&c)[U], int base) {
+    append_list<BLOCK, CAP, U>(
+        sh, [&](int u) { return order_key(c[u]); }, [&](int u) { return uint32_t(base + BLOCK * u + tid); },
+        [&](int u) { return base + BLOCK * u + tid < n && c[u] >= tau_f; });
   });
   __syncthreads();
   if (!sh.overflow) {
