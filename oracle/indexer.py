@@ -22,7 +22,10 @@ Readings where the pages are silent (each also listed in the design notes):
   * top-k order is (score descending, then lower j), -0.0 == +0.0, padded
     with -1 when fewer than k keys are valid;
   * mxfp4 byte layout: kv_fp4 [NB, bs, D/2] with element 2i in the low nibble,
-    kv_scale [NB, bs, D/32], group g covering d in [32g, 32g+32).
+    kv_scale [NB, bs, D/32], group g covering d in [32g, 32g+32);
+  * logits from a paged quantized key cache compute the same score on the
+    dequantized keys, the mxfp4 keys decoded exactly as the gather decodes
+    them (E8M0 0xFF -> 0 included).
 """
 from __future__ import annotations
 
@@ -80,6 +83,67 @@ def indexer_logits(q, k, w, limit=None, q_scale=None, k_scale=None, dtype="bf16"
             n = max(0, min(lim + 1, K))
             q_hat = dequant_q(q[b: b + 1, t: t + 1],
                               None if q_scale is None else q_scale[b: b + 1, t: t + 1], dtype)[0, 0]
+            row = np.full(K, -np.inf, dtype=np.float64)
+            if n:
+                dots = q_hat @ k_hat[:n].T                   # [H, n]
+                row[:n] = np.sum(w64[b, t][:, None] * np.maximum(dots, 0.0), axis=0)
+            out[b, t] = row.astype(np.float32)
+    return out
+
+
+# ----------------------------------------------------------------------------- paged keys
+def paged_keys(k_cache, k_scale, block_table, b, n, block_size, kfmt):
+    """k_hat [n,D] float64: the first n logical keys of sequence b, read
+    through its block table (position p -> block_table[b, p // bs], row
+    p % bs) and dequantized.
+
+    kfmt "mxfp4": k_cache [NB,bs,D/2] E2M1 nibbles (element 2i low),
+                  k_scale [NB,bs,D/32] E8M0 bytes (0xFF -> 0), group g = d in
+                  [32g, 32g+32) -- the cache format of the mxfp4 gather [P28];
+    kfmt "fp8":   k_cache [NB,bs,D] OCP e4m3 bytes, k_scale [NB,bs] float32
+                  per-token scale (the fp8 key encoding of the dense logits).
+    """
+    p = np.arange(n, dtype=np.int64)
+    blk = np.asarray(block_table, dtype=np.int64)[b, p // block_size]
+    off = p % block_size
+    if kfmt == "mxfp4":
+        packed = np.asarray(k_cache)[blk, off].astype(np.int64)       # [n, D/2]
+        D = packed.shape[-1] * 2
+        nib = np.empty((n, D), dtype=np.int64)
+        nib[:, 0::2] = packed & 0xF
+        nib[:, 1::2] = packed >> 4
+        scale = e8m0_to_f64(np.asarray(k_scale)[blk, off])             # [n, D/32]
+        return e2m1_to_f64(nib) * np.repeat(scale, D // scale.shape[-1], axis=-1)
+    if kfmt == "fp8":
+        codes = np.asarray(k_cache)[blk, off]
+        return e4m3_to_f64(codes) * np.asarray(k_scale, dtype=np.float64)[blk, off][:, None]
+    raise ValueError(kfmt)
+
+
+def indexer_logits_paged(q, q_scale, w, limit, k_cache, k_scale, block_table, block_size, K,
+                         kfmt="mxfp4", rows=None):
+    """Indexer logits [B,T,K] float32 with keys in a paged quantized cache.
+
+    The same score as indexer_logits [P27] ("fp8/fp4 packing" is an encoding
+    of the dequantized math): q is OCP e4m3 [B,T,H,D] with q_scale [B,T,H];
+    key j of sequence b is paged_keys(...)[j]; K is the logical key count of
+    the output rows.  Float64 sums, one rounding to float32, -inf past the
+    limit.  ``rows`` restricts the work to (b, t) pairs (others left NaN).
+    """
+    B, T, H, D = q.shape
+    w64 = np.asarray(w, dtype=np.float64)
+    out = np.full((B, T, K), np.nan, dtype=np.float32)
+    todo = rows if rows is not None else [(b, t) for b in range(B) for t in range(T)]
+    by_seq = {}
+    for b, t in todo:
+        by_seq.setdefault(int(b), []).append(int(t))
+    for b, ts in by_seq.items():
+        lims = [K - 1 if limit is None else int(limit[b, t]) for t in ts]
+        n_max = max(0, min(max(lims) + 1, K))
+        k_hat = paged_keys(k_cache, k_scale, block_table, b, n_max, block_size, kfmt)
+        for t, lim in zip(ts, lims):
+            n = max(0, min(lim + 1, K))
+            q_hat = dequant_q(q[b: b + 1, t: t + 1], q_scale[b: b + 1, t: t + 1], "fp8")[0, 0]
             row = np.full(K, -np.inf, dtype=np.float64)
             if n:
                 dots = q_hat @ k_hat[:n].T                   # [H, n]
