@@ -51,10 +51,17 @@ def algorithmic_work(x, sel_pos=None):
     n_valid = np.clip(lim + 1, 0, cfg.K)                      # [B,T]
     pairs = int(n_valid.sum())
     keys_read = int(n_valid.max(axis=1).sum())                # distinct valid key rows
-    logits_bytes = (keys_read * 128 * eb + cfg.rows * 64 * 128 * eb + cfg.rows * 64 * 4
-                    + pairs * 4)
+    if cfg.kcache == "mxfp4":
+        key_bytes = keys_read * (64 + 4)                       # E2M1 nibbles + E8M0 bytes
+    elif cfg.kcache == "fp8":
+        key_bytes = keys_read * (128 + 4)                      # e4m3 + fp32 scale
+    else:
+        key_bytes = keys_read * 128 * eb + (keys_read * 4 if cfg.dtype == "fp8" else 0)
+    if cfg.kcache is not None:                                 # block-table entries read
+        key_bytes += int(((n_valid.max(axis=1) + x["block_size"] - 1) // x["block_size"]).sum()) * 4
+    logits_bytes = key_bytes + cfg.rows * 64 * 128 * eb + cfg.rows * 64 * 4 + pairs * 4
     if cfg.dtype == "fp8":
-        logits_bytes += cfg.rows * 64 * 4 + keys_read * 4      # q and k scales
+        logits_bytes += cfg.rows * 64 * 4                      # q scales
     topk_bytes = pairs * 4 + cfg.rows * cfg.topk * 4
     slots = cfg.rows * cfg.topk
     distinct = slots
@@ -110,8 +117,14 @@ def cpu_baseline(x, work, budget_s):
         rows = np.sort(order[:n])
         pairs = [(int(r) // cfg.T, int(r) % cfg.T) for r in rows]
         t0 = time.perf_counter()
-        L = oracle.indexer_logits(x["q"], x["k"], x["w"], x["limit"], x["q_scale"],
-                                  x["k_scale"], cfg.dtype, rows=pairs).reshape(R, cfg.K)
+        if cfg.kcache is None:
+            L = oracle.indexer_logits(x["q"], x["k"], x["w"], x["limit"], x["q_scale"],
+                                      x["k_scale"], cfg.dtype, rows=pairs)
+        else:
+            L = oracle.indexer_logits_paged(x["q"], x["q_scale"], x["w"], x["limit"], x["kc"],
+                                            x["kc_scale"], x["block_table"], x["block_size"],
+                                            cfg.K, cfg.kcache, rows=pairs)
+        L = L.reshape(R, cfg.K)
         idx = oracle.indexer_topk(L, x["limit"].reshape(-1), cfg.topk, rows=rows)
         oracle.mxfp4_paged_gather(x["kv_fp4"], x["kv_scale"], x["block_table"], idx,
                                   x["row_seq"], x["block_size"], rows=rows)
@@ -178,16 +191,19 @@ def main():
     cfg = x["cfg"]
     d = workloads.to_device(x)
     in_bytes = sum(t.numel() * t.element_size() for key, t in d.items()
-                   if key in ("q", "k", "w") and t is not None)
+                   if key in ("q", "k", "w", "kc") and t is not None)
     n_sets = args.sets or int(min(16, max(1, -(-512 * 2 ** 20 // in_bytes))))
-    base = IndexerStep(d["q"], d["k"], d["w"], d["limit"], cfg.topk, d["kv_fp4"], d["kv_scale"],
-                       d["block_table"], d["row_seq"], d["q_scale"], d["k_scale"])
+    def make_step(q, k, w, kc, outputs=None):
+        return IndexerStep(q, k, w, d["limit"], cfg.topk, d["kv_fp4"], d["kv_scale"],
+                           d["block_table"], d["row_seq"], d["q_scale"], d["k_scale"],
+                           outputs=outputs, k_cache=kc, k_cache_scale=d.get("kc_scale"), K=cfg.K)
+
+    base = make_step(d["q"], d["k"], d["w"], d.get("kc"))
     steps = [base]
     for _ in range(n_sets - 1):   # more input copies, writing the same output buffers
-        steps.append(IndexerStep(d["q"].clone(), d["k"].clone(), d["w"].clone(), d["limit"],
-                                 cfg.topk, d["kv_fp4"], d["kv_scale"], d["block_table"],
-                                 d["row_seq"], d["q_scale"], d["k_scale"],
-                                 outputs=base.outputs()))
+        steps.append(make_step(d["q"].clone(), None if d["k"] is None else d["k"].clone(),
+                               d["w"].clone(), None if d.get("kc") is None else d["kc"].clone(),
+                               outputs=base.outputs()))
 
     # one checked pass: top-k indices must be valid positions before the gather reads them
     base.run_logits()
@@ -293,7 +309,9 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "K": cfg.K, "H": 64, "D": 128,
                    "topk": cfg.topk, "qk_dtype": cfg.dtype, "limit": "causal"
                    if cfg.causal_offset is not None else "per-sequence length",
-                   "cache": "mxfp4 E2M1+E8M0, block 64", "input_copies_rotated": n_sets},
+                   "cache": "mxfp4 E2M1+E8M0, block 64",
+                   "keys": "dense" if cfg.kcache is None else f"paged {cfg.kcache} cache, block 64",
+                   "input_copies_rotated": n_sets},
         "topk_gather_GBps": tg_gbps, "topk_gather_frac_hbm": tg_gbps / PEAK["hbm"],
         "logits_kernel_TFLOPs": work["logits_flops"] / (ms["logits"] / 1e3) / 1e12,
         "stages": stages, "roofline": roof, "work": work,

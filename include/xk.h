@@ -1,10 +1,11 @@
 /*
  * xk.h -- C ABI of the MI355X (gfx950) DeepSeek-V4 DSA indexer hot path.
  *
- * Three operations, each asynchronous on the caller's HIP stream:
- *   xk_indexer_logits      weighted-ReLU MQA score over all keys (bf16 or OCP fp8)
- *   xk_indexer_topk        deterministic per-query top-k of those scores
- *   xk_mxfp4_paged_gather  mxfp4 paged KV rows of the selected keys, decoded to bf16
+ * The operations, each asynchronous on the caller's HIP stream:
+ *   xk_indexer_logits        weighted-ReLU MQA score over all keys (bf16 or OCP fp8)
+ *   xk_indexer_logits_paged  the same score with keys in a paged mxfp4 / fp8 cache
+ *   xk_indexer_topk          deterministic per-query top-k of those scores
+ *   xk_mxfp4_paged_gather    mxfp4 paged KV rows of the selected keys, decoded to bf16
  *
  * Conventions shared by every entry point
  *   - Pointers are DEVICE pointers (hipMalloc / torch CUDA tensors) unless
@@ -82,6 +83,40 @@ xk_status xk_indexer_logits(const void* q, const float* q_scale,
                             const float* w, const int32_t* limit, float* logits,
                             int B, int T, int K, int H, int D,
                             int dtype, void* stream);
+
+typedef enum {
+  XK_KCACHE_MXFP4 = 0,        /* k_cache [NB,bs,D/2] E2M1 nibbles, k_scale [NB,bs,D/32] E8M0 */
+  XK_KCACHE_FP8_E4M3_OCP = 1  /* k_cache [NB,bs,D] e4m3 bytes, k_scale [NB,bs] fp32          */
+} xk_kcache_format;
+
+/*
+ * Indexer logits with the keys in a paged quantized cache.
+ *
+ * Defines (page "xkernels #27 -- [AMD/MI300A] DeepSeek-V4 DSA indexer +
+ * attention", comment announcing dsa_indexer_logits: fp8/fp4 key packing is
+ * an encoding of the same dequantized math; page "xkernels #28 --
+ * DeepSeek-V4 serving support", comment shipping mxfp4_paged_gather: the
+ * paged mxfp4 cache format and its block table): the xk_indexer_logits
+ * score with q = e4m3(q8[b,t,h,:]) * q_scale[b,t,h] and key j of sequence b
+ * read from page block_table[b, j / bs], row j % bs, dequantized as
+ *   XK_KCACHE_MXFP4:        E2M1(nibble d) * E8M0(k_scale byte d/32), 0xFF -> 0
+ *                           (element 2i in the low nibble; the gather's format)
+ *   XK_KCACHE_FP8_E4M3_OCP: e4m3(k_cache byte d) * k_scale[page, row]
+ *
+ *   q            [B,T,H,D] OCP e4m3 bytes (16-byte aligned); q_scale [B,T,H] fp32
+ *   w            [B,T,H]   fp32 head weights
+ *   limit        [B,T]     int32 inclusive last valid position, or NULL (K-1)
+ *   k_cache      the pool above (16-byte aligned); k_scale its scales (4-byte aligned)
+ *   block_table  [B,MB]    int32 physical page of each logical page
+ *   logits       [B,T,K]   fp32 output, -inf past the limit; every element written
+ *   H must be 64, D 128, bs a power of two >= 16, K <= MB*bs and NB*bs < 2^31,
+ *   else XK_ERR_UNSUPPORTED / XK_ERR_INVALID_ARGUMENT. Pages holding a valid
+ *   position must lie in [0, NB) (not checked on the device).
+ */
+xk_status xk_indexer_logits_paged(const void* q, const float* q_scale, const float* w,
+                                  const int32_t* limit, const void* k_cache, const void* k_scale,
+                                  const int32_t* block_table, float* logits, int B, int T, int K,
+                                  int H, int D, int MB, int NB, int bs, int kformat, void* stream);
 
 /*
  * Bytes of device workspace xk_indexer_topk needs for these sizes (may be 0).

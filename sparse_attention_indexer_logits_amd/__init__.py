@@ -18,9 +18,10 @@ LIB_PATH = os.path.join(_PKG, "libxk.so")
 
 XK_OK, XK_ERR_INVALID_ARGUMENT, XK_ERR_UNSUPPORTED, XK_ERR_HIP = 0, 1, 2, 3
 XK_BF16, XK_FP8_E4M3_OCP = 0, 1
+XK_KCACHE_MXFP4, XK_KCACHE_FP8_E4M3_OCP = 0, 1
 
-EXPORTED = ("xk_indexer_logits", "xk_indexer_topk_workspace_size", "xk_indexer_topk",
-            "xk_mxfp4_paged_gather", "xk_status_string", "xk_last_error")
+EXPORTED = ("xk_indexer_logits", "xk_indexer_logits_paged", "xk_indexer_topk_workspace_size",
+            "xk_indexer_topk", "xk_mxfp4_paged_gather", "xk_status_string", "xk_last_error")
 
 
 class XKError(RuntimeError):
@@ -37,6 +38,8 @@ def _load() -> ctypes.CDLL:
     P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.xk_indexer_logits.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P]
     lib.xk_indexer_logits.restype = I
+    lib.xk_indexer_logits_paged.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P]
+    lib.xk_indexer_logits_paged.restype = I
     lib.xk_indexer_topk_workspace_size.argtypes = [I, I, I]
     lib.xk_indexer_topk_workspace_size.restype = Z
     lib.xk_indexer_topk.argtypes = [P, P, P, I, I, I, P, Z, P]
@@ -125,6 +128,59 @@ def xk_indexer_logits(q, k, w, limit=None, q_scale=None, k_scale=None, out=None,
     """
     args, out = logits_args(q, k, w, limit, q_scale, k_scale, out)
     _check(_lib.xk_indexer_logits(*args, _stream(stream)))
+    return out
+
+
+def logits_paged_args(q, q_scale, w, k_cache, k_scale, block_table, limit=None, K=None, out=None):
+    """Validate the arguments of xk_indexer_logits_paged; returns (C arguments
+    without the stream, out). The key format follows k_cache's dtype: uint8
+    [NB,bs,64] is mxfp4 (k_scale uint8 [NB,bs,4]); float8_e4m3fn [NB,bs,128]
+    is fp8 (k_scale float32 [NB,bs])."""
+    _need(q, "q", (torch.float8_e4m3fn, torch.uint8), 4)
+    B, T, H, D = q.shape
+    _need(q_scale, "q_scale", (torch.float32,), 3)
+    _need(w, "w", (torch.float32,), 3)
+    if tuple(q_scale.shape) != (B, T, H) or tuple(w.shape) != (B, T, H):
+        raise ValueError("q_scale and w must be [B,T,H]")
+    _need(block_table, "block_table", (torch.int32,), 2)
+    MB = block_table.shape[1]
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must be [B,MB]")
+    if k_cache.dtype == torch.uint8:
+        fmt = XK_KCACHE_MXFP4
+        _need(k_cache, "k_cache", (torch.uint8,), 3)
+        NB, bs, half = k_cache.shape
+        _need(k_scale, "k_scale", (torch.uint8,), 3)
+        if 2 * half != D or tuple(k_scale.shape) != (NB, bs, D // 32):
+            raise ValueError("mxfp4 k_cache must be [NB,bs,D/2] and k_scale [NB,bs,D/32]")
+    else:
+        fmt = XK_KCACHE_FP8_E4M3_OCP
+        _need(k_cache, "k_cache", (torch.float8_e4m3fn,), 3)
+        NB, bs, dk = k_cache.shape
+        _need(k_scale, "k_scale", (torch.float32,), 2)
+        if dk != D or tuple(k_scale.shape) != (NB, bs):
+            raise ValueError("fp8 k_cache must be [NB,bs,D] and k_scale [NB,bs]")
+    if K is None:
+        K = MB * bs
+    if limit is not None:
+        _need(limit, "limit", (torch.int32,), 2)
+        if tuple(limit.shape) != (B, T):
+            raise ValueError("limit must be [B,T]")
+    if out is None:
+        out = torch.empty((B, T, K), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 3)
+    if tuple(out.shape) != (B, T, K):
+        raise ValueError("out must be [B,T,K]")
+    args = (_ptr(q), _ptr(q_scale), _ptr(w), _ptr(limit), _ptr(k_cache), _ptr(k_scale),
+            _ptr(block_table), _ptr(out), B, T, K, H, D, MB, NB, bs, fmt)
+    return args, out
+
+
+def xk_indexer_logits_paged(q, q_scale, w, k_cache, k_scale, block_table, limit=None, K=None,
+                            out=None, stream=None):
+    """logits [B,T,K] fp32 with keys in a paged mxfp4 / fp8 cache (see include/xk.h)."""
+    args, out = logits_paged_args(q, q_scale, w, k_cache, k_scale, block_table, limit, K, out)
+    _check(_lib.xk_indexer_logits_paged(*args, _stream(stream)))
     return out
 
 

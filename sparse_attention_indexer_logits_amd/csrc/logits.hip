@@ -307,6 +307,186 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void logits_decode_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// paged keys: the decode kernel's structure with keys read through a block
+// table from a quantized cache (fp8 q; mxfp4 or fp8 keys). A workgroup owns
+// one query and a chunk of positions; its block-table entries are staged in
+// LDS. Pages hold at least 16 positions, so a 16-key subtile lies in one
+// page: each subtile gets a range-checked buffer descriptor over its valid
+// keys, so positions past the limit read 0 without a branch.
+//  * mxfp4 keys (v_mfma_scale_f32_16x16x128_f8f6f4 with B in E2M1). Lane
+//    layouts measured on gfx950 (K = the contraction index the block scales
+//    follow): an E2M1 operand's lane group g holds K in [32g, 32g+32) in
+//    nibble order and lane group g's scale byte scales K-block g; an 8-bit
+//    operand's lane group g holds K in [16g, 16g+16) in bytes 0..15 and K
+//    64 higher in bytes 16..31. With K = d, a key lane (r, g) takes the 16
+//    bytes of nibbles of d in [32g, 32g+32) and its E8M0 byte g, exactly the
+//    cache layout, and a q lane takes bytes [16g, 16g+16) and [64+16g, ...)
+//    of its head row. (The dense fp8 path pairs two 8-bit operands in one
+//    consistent order with unit scales, so its order does not matter.) The
+//    hardware reads scale 0xFF as NaN where the cache means 0, so such a
+//    group's nibbles are zeroed in registers (scale 127).
+//  * fp8 keys: 32-byte fragments with unit block scales; the per-token fp32
+//    scale multiplies the finished score, as in the dense fp8 path.
+constexpr int kPagedTab = 64;  // staged table entries per workgroup (chunk / 16 + 2)
+
+template <bool MXFP4>
+__global__ __launch_bounds__(kDecWaves * 64, 2) void logits_paged_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
+    const uint8_t* __restrict__ kc, const uint8_t* __restrict__ kcs,
+    const int32_t* __restrict__ block_table, const float* __restrict__ w,
+    const int32_t* __restrict__ limit, float* __restrict__ out, int T, int K, int MB, int bs_log2,
+    int keys_per_wg, int n_chunks) {
+  using M = Mma16<true>;  // fp8 A fragments (q): one 128-deep step per M-tile
+  using Frag = M::Frag;
+  constexpr int kRowBytes = MXFP4 ? 64 : 128;  // cache bytes per key
+  constexpr int kQRow = kHeadDim;              // fp8 q bytes per head
+  constexpr int kPitch = kQRow + 16;
+  constexpr int kLanesPerRow = kQRow / 16;
+  constexpr int kRing = 8;  // subtiles in flight per wave (two groups)
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kHeads * kPitch];
+  __shared__ __attribute__((aligned(16))) float w_lds[kHeads];
+  __shared__ int32_t tab_lds[kPagedTab];
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, r = lane & 15;
+  const int64_t bt = blockIdx.x / n_chunks;
+  const int chunk = int(blockIdx.x % n_chunks);
+  const int64_t b = bt / T;
+  const int lim = clamp_limit(limit, bt, K);
+  const int j_begin = chunk * keys_per_wg;
+  const int j_end = min(j_begin + keys_per_wg, K);
+  float* orow = out + bt * K;
+
+  for (int j = max(j_begin, lim + 1) + int(threadIdx.x); j < j_end; j += kDecWaves * 64)
+    orow[j] = -INFINITY;
+  const int c_end = min(j_end, lim + 1);
+  if (c_end <= j_begin) return;  // uniform over the workgroup
+
+  const int per_wave = keys_per_wg / kDecWaves;
+  const int w_begin = j_begin + wave * per_wave;
+  const int w_end = max(w_begin, min(w_begin + per_wave, c_end));
+  const int tab0 = j_begin >> bs_log2;                      // first staged page index
+  const int n_tab = ((c_end - 1) >> bs_log2) - tab0 + 1;   // pages with a scored key
+  const auto ors = make_rsrc(orow + w_begin, (w_end - w_begin) * 4);
+
+  // q chunks, head weights (times the q scale) and the chunk's table entries
+  constexpr int kQLoads = kHeads * kLanesPerRow / (kDecWaves * 64);
+  const uint8_t* qsrc = q + bt * (kHeads * kQRow);
+  u32x4 qv[kQLoads];
+#pragma unroll
+  for (int i = 0; i < kQLoads; ++i) {
+    const int c = int(threadIdx.x) + kDecWaves * 64 * i;
+    qv[i] = *reinterpret_cast<const u32x4*>(qsrc + (c / kLanesPerRow) * kQRow + (c % kLanesPerRow) * 16);
+  }
+  float wv = 0.f;
+  if (threadIdx.x < kHeads) wv = w[bt * kHeads + threadIdx.x] * q_scale[bt * kHeads + threadIdx.x];
+  int32_t tv = 0;
+  if (int(threadIdx.x) < n_tab) tv = block_table[b * MB + tab0 + int(threadIdx.x)];
+#pragma unroll
+  for (int i = 0; i < kQLoads; ++i) {
+    const int c = int(threadIdx.x) + kDecWaves * 64 * i;
+    *reinterpret_cast<u32x4*>(q_lds + (c / kLanesPerRow) * kPitch + (c % kLanesPerRow) * 16) = qv[i];
+  }
+  if (threadIdx.x < kHeads) w_lds[threadIdx.x] = wv;
+  if (int(threadIdx.x) < n_tab) tab_lds[threadIdx.x] = tv;
+  __syncthreads();
+
+  Frag a[4];
+  float wr[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const uint8_t* qrow = q_lds + (16 * mt + r) * kPitch;
+    if constexpr (MXFP4) {  // the 8-bit operand's K order (see above)
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(qrow + 16 * g);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(qrow + 64 + 16 * g);
+      a[mt] = Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      a[mt] = M::load(qrow + M::dofs(0, g));
+    }
+    const f32x4 w4 = *reinterpret_cast<const f32x4*>(&w_lds[16 * mt + 4 * g]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wr[mt][i] = w4[i];
+  }
+
+  // one subtile: B fragment and (mxfp4) block scale of key jj + r, group g;
+  // (fp8) the scale of key jj + (lane % 16), kept by the lanes whose store
+  // slot it is (lane / 16 == subtile index in its group)
+  struct Sub {
+    Frag b;
+    uint32_t sc;
+  };
+  Sub buf[kRing];
+  float sk[kRing / 4];
+  auto gload = [&](int jj, int st, Sub& dst, float& skk) {
+    const int valid = max(0, min(16, w_end - jj));
+    const int page = min(max((jj >> bs_log2) - tab0, 0), n_tab - 1);
+    const int64_t slot = (int64_t(tab_lds[page]) << bs_log2) | (jj & ((1 << bs_log2) - 1));
+    const auto rs = make_rsrc(kc + slot * kRowBytes, valid * kRowBytes);
+    if constexpr (MXFP4) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, r * kRowBytes + 16 * g, 0, 0);
+      dst.b = Frag{int(v[0]), int(v[1]), int(v[2]), int(v[3]), 0, 0, 0, 0};
+      const auto ss = make_rsrc(kcs + slot * 4, valid * 4);
+      dst.sc = __builtin_amdgcn_raw_buffer_load_b32(ss, r * 4, 0, 0);
+    } else {
+      const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rs, r * kRowBytes + 32 * g, 0, 0);
+      const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rs, r * kRowBytes + 32 * g + 16, 0, 0);
+      dst.b = Frag{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+      const auto ss = make_rsrc(kcs + slot * 4, valid * 4);
+      const float v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ss, r * 4, 0, 0));
+      skk = (lane >> 4) == st ? v : skk;
+    }
+  };
+  auto partial = [&](const Sub& sub) {
+    Frag bf = sub.b;
+    int sb = 127;
+    if constexpr (MXFP4) {
+      sb = int((sub.sc >> (8 * g)) & 0xFFu);
+      if (sb == 0xFF) {  // E8M0 0xFF means 0 here: zero the group
+        bf = Frag{0, 0, 0, 0, 0, 0, 0, 0};
+        sb = 127;
+      }
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      // operand formats: A fp8 e4m3 (0), B E2M1 (4) or e4m3 (0); A scale 1.0
+      acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[mt], bf, f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                 0, MXFP4 ? 4 : 0, 0, 127, 0, sb);
+    }
+    float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      p0 = fmaf(wr[mt][0], fmaxf(acc[mt][0], 0.f), p0);
+      p1 = fmaf(wr[mt][1], fmaxf(acc[mt][1], 0.f), p1);
+      p0 = fmaf(wr[mt][2], fmaxf(acc[mt][2], 0.f), p0);
+      p1 = fmaf(wr[mt][3], fmaxf(acc[mt][3], 0.f), p1);
+    }
+    return p0 + p1;
+  };
+
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) gload(w_begin + 16 * i, i & 3, buf[i], sk[i >> 2]);
+  for (int j0 = w_begin; j0 < w_end; j0 += 16 * kRing) {
+#pragma unroll
+    for (int grp = 0; grp < kRing / 4; ++grp) {
+      const int jg = j0 + kDecGroup * grp;
+      float p[4];
+      const float s_key = sk[grp];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int slot = 4 * grp + st;
+        p[st] = partial(buf[slot]);
+        gload(jg + 16 * st + 16 * kRing, st, buf[slot], sk[grp]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const float tot = subtile_total(p, lane);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, MXFP4 ? tot : tot * s_key), ors,
+                                            (jg - w_begin + lane) * 4, 0, 0);
+    }
+  }
+}
+
 // prefill grid: 1-D over (query blocks, longest causal rows first) x B x
 // (key chunks). NW waves x QW queries per workgroup share double-buffered
 // 64-key LDS tiles; the next tile's global loads are issued before this
@@ -450,6 +630,31 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 }  // namespace
+
+hipError_t launch_logits_paged(const void* q, const float* q_scale, const float* w,
+                               const int32_t* limit, const void* k_cache, const void* k_scale,
+                               const int32_t* block_table, float* logits, int B, int T, int K,
+                               int MB, int bs, bool mxfp4, hipStream_t stream) {
+  // the decode kernel's chunking: 512 or 768 positions per workgroup
+  const int64_t rows = int64_t(B) * T;
+  const int64_t per = (int64_t(K) * rows + 2047) / 2048;
+  int kpw = int(std::min<int64_t>(std::max<int64_t>(per, 2 * kDecWaves * kDecGroup), 3 * kDecWaves * kDecGroup));
+  kpw = std::min(round_up(kpw, kDecWaves * kDecGroup), round_up(K, kDecWaves * kDecGroup));
+  const int nch = (K + kpw - 1) / kpw;
+  int bs_log2 = 0;
+  while ((1 << bs_log2) < bs) ++bs_log2;
+  const dim3 grid(unsigned(rows * nch));
+  const auto* q8 = static_cast<const uint8_t*>(q);
+  const auto* kc = static_cast<const uint8_t*>(k_cache);
+  const auto* ks = static_cast<const uint8_t*>(k_scale);
+  if (mxfp4)
+    hipLaunchKernelGGL(logits_paged_kernel<true>, grid, dim3(kDecWaves * 64), 0, stream, q8, q_scale, kc, ks,
+                       block_table, w, limit, logits, T, K, MB, bs_log2, kpw, nch);
+  else
+    hipLaunchKernelGGL(logits_paged_kernel<false>, grid, dim3(kDecWaves * 64), 0, stream, q8, q_scale, kc, ks,
+                       block_table, w, limit, logits, T, K, MB, bs_log2, kpw, nch);
+  return hipGetLastError();
+}
 
 hipError_t launch_logits(const void* q, const float* q_scale, const void* k,
                          const float* k_scale, const float* w, const int32_t* limit,

@@ -94,6 +94,37 @@ XK_EXPORT xk_status xk_indexer_logits(const void* q, const float* q_scale, const
                   "xk_indexer_logits launch");
 }
 
+XK_EXPORT xk_status xk_indexer_logits_paged(const void* q, const float* q_scale, const float* w,
+                                            const int32_t* limit, const void* k_cache,
+                                            const void* k_scale, const int32_t* block_table,
+                                            float* logits, int B, int T, int K, int H, int D, int MB,
+                                            int NB, int bs, int kformat, void* stream) {
+  if (!q || !q_scale || !w || !k_cache || !k_scale || !block_table || !logits)
+    return fail(XK_ERR_INVALID_ARGUMENT,
+                "null q, q_scale, w, k_cache, k_scale, block_table or logits");
+  if (B < 1 || T < 1 || K < 1 || H < 1 || D < 1 || MB < 1 || NB < 1 || bs < 1)
+    return fail(XK_ERR_INVALID_ARGUMENT, "B, T, K, H, D, MB, NB, bs must be >= 1");
+  if (kformat != XK_KCACHE_MXFP4 && kformat != XK_KCACHE_FP8_E4M3_OCP)
+    return fail(XK_ERR_INVALID_ARGUMENT, "unknown key cache format");
+  if (H != xk::kHeads || D != xk::kHeadDim)
+    return fail(XK_ERR_UNSUPPORTED, "only H=64, D=128 (DeepSeek-V4 indexer) is implemented");
+  if ((bs & (bs - 1)) != 0 || bs < 16)
+    return fail(XK_ERR_UNSUPPORTED, "block size must be a power of two >= 16");
+  if (int64_t(K) > int64_t(MB) * bs)
+    return fail(XK_ERR_INVALID_ARGUMENT, "K exceeds the positions the block table maps (MB*bs)");
+  if (int64_t(NB) * bs > (int64_t(1) << 31) - 1)
+    return fail(XK_ERR_UNSUPPORTED, "NB*bs (cache positions) above 2^31-1");
+  if (int64_t(B) * T > (int64_t(1) << 30)) return fail(XK_ERR_UNSUPPORTED, "B*T above 2^30");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(k_scale, 4))
+    return fail(XK_ERR_INVALID_ARGUMENT, "q and k_cache must be 16-byte, k_scale 4-byte aligned");
+  xk_status s = check_device();
+  if (s != XK_OK) return s;
+  return launched(xk::launch_logits_paged(q, q_scale, w, limit, k_cache, k_scale, block_table, logits,
+                                          B, T, K, MB, bs, kformat == XK_KCACHE_MXFP4,
+                                          static_cast<hipStream_t>(stream)),
+                  "xk_indexer_logits_paged launch");
+}
+
 XK_EXPORT size_t xk_indexer_topk_workspace_size(int R, int K, int k) {
   (void)R;
   (void)K;

@@ -32,6 +32,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 hipError_t launch_logits(const void* q, const float* q_scale, const void* k,
                          const float* k_scale, const float* w, const int32_t* limit,
                          float* logits, int B, int T, int K, bool fp8, hipStream_t stream);
+hipError_t launch_logits_paged(const void* q, const float* q_scale, const float* w,
+                               const int32_t* limit, const void* k_cache, const void* k_scale,
+                               const int32_t* block_table, float* logits, int B, int T, int K,
+                               int MB, int bs, bool mxfp4, hipStream_t stream);
 hipError_t launch_topk(const float* logits, const int32_t* limit, int32_t* idx, int R,
                        int K, int k, hipStream_t stream);
 hipError_t launch_gather(const uint8_t* kv_fp4, const uint8_t* kv_scale,

@@ -9,22 +9,30 @@ from __future__ import annotations
 
 import torch
 
-from . import _check, _lib, _stream, gather_args, logits_args, topk_args
+from . import _check, _lib, _stream, gather_args, logits_args, logits_paged_args, topk_args
 
 
 class IndexerStep:
     """One batch's launches. `outputs` = (logits, idx, gathered) of another
-    step with the same shapes makes this step write into those buffers."""
+    step with the same shapes makes this step write into those buffers.
+    With k None and a paged key cache (k_cache, k_cache_scale, K) the logits
+    read the keys through block_table from that cache."""
 
     def __init__(self, q, k, w, limit, topk, kv_fp4, kv_scale, block_table, row_seq,
-                 q_scale=None, k_scale=None, outputs=None):
+                 q_scale=None, k_scale=None, outputs=None, k_cache=None, k_cache_scale=None,
+                 K=None):
         self.q, self.k, self.w, self.limit = q, k, w, limit
         self.q_scale, self.k_scale = q_scale, k_scale
         self.topk = topk
         self.kv_fp4, self.kv_scale = kv_fp4, kv_scale
         self.block_table, self.row_seq = block_table, row_seq
         lg, ix, ga = outputs if outputs is not None else (None, None, None)
-        self._logits_args, self.logits = logits_args(q, k, w, limit, q_scale, k_scale, out=lg)
+        self.paged = k is None
+        if self.paged:
+            self._logits_args, self.logits = logits_paged_args(q, q_scale, w, k_cache, k_cache_scale,
+                                                               block_table, limit, K, out=lg)
+        else:
+            self._logits_args, self.logits = logits_args(q, k, w, limit, q_scale, k_scale, out=lg)
         self._topk_args, self.idx, self.workspace = topk_args(self.logits, topk, limit, out=ix)
         self._gather_args, self.gathered = gather_args(kv_fp4, kv_scale, block_table, self.idx,
                                                        row_seq, out=ga)
@@ -33,7 +41,10 @@ class IndexerStep:
         return self.logits, self.idx, self.gathered
 
     def run_logits(self, stream=None):
-        _check(_lib.xk_indexer_logits(*self._logits_args, _stream(stream)))
+        if self.paged:
+            _check(_lib.xk_indexer_logits_paged(*self._logits_args, _stream(stream)))
+        else:
+            _check(_lib.xk_indexer_logits(*self._logits_args, _stream(stream)))
         return self.logits
 
     def run_topk(self, stream=None):

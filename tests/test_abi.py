@@ -27,8 +27,9 @@ def lib():
 
 def test_header_declares_the_three_operations():
     names = declared_functions()
-    for n in ("xk_indexer_logits", "xk_indexer_topk", "xk_mxfp4_paged_gather",
-              "xk_indexer_topk_workspace_size", "xk_status_string", "xk_last_error"):
+    for n in ("xk_indexer_logits", "xk_indexer_logits_paged", "xk_indexer_topk",
+              "xk_mxfp4_paged_gather", "xk_indexer_topk_workspace_size", "xk_status_string",
+              "xk_last_error"):
         assert n in names
 
 
@@ -64,6 +65,25 @@ FAKE = 0x10000  # aligned, never dereferenced: validation fails before any HIP c
 ])
 def test_logits_validation(lib, args, status, needle):
     assert lib.xk_indexer_logits(*args, None) == status
+    assert needle in lib.xk_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    # (q, q_scale, w, limit, k_cache, k_scale, block_table, logits,
+    #  B, T, K, H, D, MB, NB, bs, kformat)
+    ((FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 128, 1, 1, 64, 0), 1, "null"),
+    ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 0, 64, 64, 128, 1, 1, 64, 0), 1, ">= 1"),
+    ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 128, 1, 1, 64, 5), 1, "format"),
+    ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 32, 128, 1, 1, 64, 0), 2, "H=64"),
+    ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 128, 8, 1, 8, 0), 2, ">= 16"),
+    ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 48, 64, 128, 1, 1, 48, 1), 2, "power of two"),
+    ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 200, 64, 128, 3, 4, 64, 0), 1, "MB*bs"),
+    ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 128, 1, 1 << 26, 64, 0), 2, "NB*bs"),
+    ((FAKE, FAKE, FAKE, None, FAKE + 8, FAKE, FAKE, FAKE, 1, 1, 64, 64, 128, 1, 1, 64, 0), 1, "aligned"),
+    ((FAKE, FAKE, FAKE, None, FAKE, FAKE + 2, FAKE, FAKE, 1, 1, 64, 64, 128, 1, 1, 64, 1), 1, "aligned"),
+])
+def test_logits_paged_validation(lib, args, status, needle):
+    assert lib.xk_indexer_logits_paged(*args, None) == status
     assert needle in lib.xk_last_error().decode()
 
 

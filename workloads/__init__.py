@@ -27,7 +27,7 @@ BLOCK_SIZE = 64   # paged-cache tokens per block
 FP8_E4M3_MAX = 448.0
 
 # order in which child streams are spawned; never reorder (changes every input)
-_STREAMS = ("q", "k", "w", "lens", "fp4", "scale", "table", "ff", "neg")
+_STREAMS = ("q", "k", "w", "lens", "fp4", "scale", "table", "ff", "neg", "kc4", "kcs")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -45,6 +45,9 @@ class Config:
     scale_hi: int = 136
     n_ff: int = 0          # E8M0 0xFF bytes planted in the scale array
     n_neg: int = 0         # sel_pos slots forced to -1 per row
+    kcache: Optional[str] = None   # indexer keys in a paged cache: "mxfp4" or "fp8"
+    kscale_lo: int = 124   # E8M0 bytes of the mxfp4 key cache
+    kscale_hi: int = 130
     description: str = ""
 
     @property
@@ -73,6 +76,17 @@ CONFIGS = {
         "long_fp8_prefill", seed=4, B=1, T=2048, K=98304, topk=1024,
         dtype="fp8", causal_offset=96256,
         description="1 seq, T=2048 at causal offset 96256, K=98304, OCP e4m3, top-1024"),
+    # logits straight from a paged quantized key cache (fp8 q, mxfp4 keys
+    # through the block table), then the same top-k and gather
+    "flash_decode_fp4": Config(
+        "flash_decode_fp4", seed=5, B=32, T=1, K=8192, topk=512, dtype="fp8",
+        len_range=(8192, 8192), kcache="mxfp4", n_ff=8,
+        description="32 seqs x 1 query, 8192 keys in a paged mxfp4 key cache, fp8 q, top-512"),
+    "pro_decode_fp4": Config(
+        "pro_decode_fp4", seed=6, B=64, T=1, K=65536, topk=1024, dtype="fp8",
+        len_range=(16384, 65536), kcache="mxfp4",
+        description="64 seqs x 1 query, context U{16384..65536} in a paged mxfp4 key cache, "
+                    "fp8 q, top-1024"),
 }
 
 
@@ -129,10 +143,12 @@ def make_inputs(cfg: Config) -> dict:
     out = {"cfg": cfg, "limit": limits(cfg), "seq_len": lens}
 
     qx = _normal(s["q"], (B, T, H, D))
-    # keys past a sequence's length are never read: keep them zero, draw only the valid ones
-    kx = np.zeros((B, K, D), dtype=np.float32)
-    for b in range(B):
-        kx[b, : lens[b]] = _normal(s["k"], (int(lens[b]), D))
+    # keys past a sequence's length are never read: keep them zero, draw only
+    # the valid ones (none at all when the keys live in an mxfp4 cache)
+    kx = np.zeros((B, K if cfg.kcache != "mxfp4" else 0, D), dtype=np.float32)
+    if cfg.kcache != "mxfp4":
+        for b in range(B):
+            kx[b, : lens[b]] = _normal(s["k"], (int(lens[b]), D))
     out["w"] = (_normal(s["w"], (B, T, H)) / np.float32(8.0)).astype(np.float32)
 
     if cfg.dtype == "bf16":
@@ -173,6 +189,27 @@ def make_inputs(cfg: Config) -> dict:
         out["ff_positions"] = np.sort(pos)
     out["kv_scale"] = sc
     out["block_table"] = table
+    if cfg.kcache == "mxfp4":
+        # indexer keys in their own mxfp4 pages, same block table
+        out["kc"] = s["kc4"].integers(0, 256, size=(NB, BLOCK_SIZE, D // 2), dtype=np.uint8)
+        kcs = s["kcs"].integers(cfg.kscale_lo, cfg.kscale_hi + 1, size=(NB, BLOCK_SIZE, D // 32),
+                                dtype=np.uint8)
+        if cfg.n_ff:
+            flat = kcs.reshape(-1)
+            flat[s["kcs"].choice(flat.size, size=cfg.n_ff, replace=False)] = 0xFF
+        out["kc_scale"] = kcs
+        out["k"] = None
+    elif cfg.kcache == "fp8":
+        # the dense fp8 keys and scales, moved into pages through the table
+        kc = np.zeros((NB, BLOCK_SIZE, D), dtype=np.uint8)
+        kcs = np.ones((NB, BLOCK_SIZE), dtype=np.float32)
+        for b in range(B):
+            p = np.arange(int(lens[b]))
+            kc[table[b, p // BLOCK_SIZE], p % BLOCK_SIZE] = out["k"][b, : lens[b]]
+            kcs[table[b, p // BLOCK_SIZE], p % BLOCK_SIZE] = out["k_scale"][b, : lens[b]]
+        out["kc"], out["kc_scale"] = kc, kcs
+    elif cfg.kcache is not None:
+        raise ValueError(cfg.kcache)
     out["row_seq"] = np.repeat(np.arange(B, dtype=np.int32), T)
     out["block_size"] = BLOCK_SIZE
     if cfg.n_neg:
@@ -192,13 +229,14 @@ def inputs(name: str) -> dict:
 
 def custom(name="custom", seed=123, B=1, T=4, K=300, topk=16, dtype="bf16",
            causal_offset=None, len_range=None, n_ff=0, n_neg=0,
-           scale_lo=118, scale_hi=136) -> dict:
+           scale_lo=118, scale_hi=136, kcache=None, kscale_lo=124, kscale_hi=130) -> dict:
     """Small ad-hoc shapes for edge-case tests (ragged tails, short rows...)."""
     if causal_offset is None and len_range is None:
         len_range = (K, K)
     return make_inputs(Config(name, seed=seed, B=B, T=T, K=K, topk=topk, dtype=dtype,
                               causal_offset=causal_offset, len_range=len_range,
-                              n_ff=n_ff, n_neg=n_neg, scale_lo=scale_lo, scale_hi=scale_hi))
+                              n_ff=n_ff, n_neg=n_neg, scale_lo=scale_lo, scale_hi=scale_hi,
+                              kcache=kcache, kscale_lo=kscale_lo, kscale_hi=kscale_hi))
 
 
 def apply_forced_negatives(idx: np.ndarray, neg_slots) -> np.ndarray:
@@ -226,9 +264,15 @@ def to_device(x: dict, device="cuda") -> dict:
         out["q_scale"] = out["k_scale"] = None
     else:
         out["q"] = dev(x["q"], torch.float8_e4m3fn)
-        out["k"] = dev(x["k"], torch.float8_e4m3fn)
+        out["k"] = dev(x["k"], torch.float8_e4m3fn) if x["k"] is not None else None
         out["q_scale"] = dev(x["q_scale"])
-        out["k_scale"] = dev(x["k_scale"])
+        out["k_scale"] = dev(x["k_scale"]) if x["k"] is not None else None
+    if cfg.kcache == "mxfp4":
+        out["kc"] = dev(x["kc"])
+        out["kc_scale"] = dev(x["kc_scale"])
+    elif cfg.kcache == "fp8":
+        out["kc"] = dev(x["kc"], torch.float8_e4m3fn)
+        out["kc_scale"] = dev(x["kc_scale"])
     out["w"] = dev(x["w"])
     out["limit"] = dev(x["limit"])
     out["kv_fp4"] = dev(x["kv_fp4"])
