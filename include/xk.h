@@ -6,6 +6,9 @@
  *   xk_indexer_logits_paged  the same score with keys in a paged mxfp4 / fp8 cache
  *   xk_indexer_topk          deterministic per-query top-k of those scores
  *   xk_mxfp4_paged_gather    mxfp4 paged KV rows of the selected keys, decoded to bf16
+ * and the producers of their quantized inputs:
+ *   xk_quant_fp8_rows        per-row OCP fp8 quantizer (q per token and head, k per token)
+ *   xk_mxfp4_cache_write     rows into the paged mxfp4 cache
  *
  * Conventions shared by every entry point
  *   - Pointers are DEVICE pointers (hipMalloc / torch CUDA tensors) unless
@@ -178,6 +181,50 @@ xk_status xk_mxfp4_paged_gather(const uint8_t* kv_fp4, const uint8_t* kv_scale,
                                 const int32_t* row_seq, uint16_t* out,
                                 int R, int k, int S, int MB, int NB, int bs, int D,
                                 void* stream);
+
+typedef enum {
+  XK_IN_FP32 = 0,  /* float32 rows          */
+  XK_IN_BF16 = 1   /* bfloat16 rows (bits)  */
+} xk_in_dtype;
+
+/*
+ * Per-row OCP fp8 quantizer: the producer of the fp8 q (one row per token
+ * and head: per-(token, head) scales) and fp8 k (one row per token).
+ *
+ * Defines (page "DeepSeek V4 Flash on a single AMD MI300X", "FP8 format"
+ * fix: the indexer's fp8 cache is OCP e4m3 written with FP8_MAX = 448; page
+ * "DeepSeek-V4 on ATOM", "Quantization & Transform": act_quant bf16 -> fp8
+ * e4m3 per 1x128): scale[n] = max_d |x[n,d]| / 448 in fp32 (1 for an
+ * all-zero row), out[n,d] = e4m3 round-to-nearest-even of the fp32
+ * quotient x[n,d] / scale[n], saturated to +-448.
+ *
+ *   x      [N,D] fp32 or bf16 (x_dtype), 8-byte (fp32) / 4-byte (bf16) aligned
+ *   out    [N,D] e4m3 bytes (2-byte aligned); scale [N] fp32
+ *   N >= 1, D must be 128 (XK_ERR_UNSUPPORTED otherwise).
+ */
+xk_status xk_quant_fp8_rows(const void* x, int x_dtype, uint8_t* out, float* scale, int64_t N, int D,
+                            void* stream);
+
+/*
+ * mxfp4 cache writer: rows into the paged mxfp4 cache that
+ * xk_mxfp4_paged_gather and xk_indexer_logits_paged read.
+ *
+ * Defines (the inverse of the gather's decode, page "xkernels #28 --
+ * DeepSeek-V4 serving support", comment shipping mxfp4_paged_gather; the
+ * rounding is the OCP MX rule, which the pages do not spell out): for row n
+ * with slot = slots[n] >= 0 (slot = page * bs + row in page), per 32-element
+ * group g: e = floor(log2(max |x|)) - 2 clamped to [-127, 127] (-127 for an
+ * all-zero group), kv_scale[slot][g] = e + 127, and element d is the E2M1
+ * round-to-nearest-even code of x[n,d] * 2^-e saturated to +-6, element 2i
+ * in the low nibble of kv_fp4[slot][i]. Rows with slots[n] < 0 or >= NB*bs
+ * are skipped. Rows with equal slots race (last writer wins).
+ *
+ *   x        [N,D] fp32 or bf16 rows; slots [N] int64
+ *   kv_fp4   [NB,bs,D/2] u8; kv_scale [NB,bs,D/32] u8 (written in place)
+ *   N >= 1, D must be 128.
+ */
+xk_status xk_mxfp4_cache_write(const void* x, int x_dtype, const int64_t* slots, uint8_t* kv_fp4,
+                               uint8_t* kv_scale, int64_t N, int NB, int bs, int D, void* stream);
 
 /* Static name of a status code. */
 const char* xk_status_string(xk_status status);

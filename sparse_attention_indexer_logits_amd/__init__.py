@@ -19,9 +19,11 @@ LIB_PATH = os.path.join(_PKG, "libxk.so")
 XK_OK, XK_ERR_INVALID_ARGUMENT, XK_ERR_UNSUPPORTED, XK_ERR_HIP = 0, 1, 2, 3
 XK_BF16, XK_FP8_E4M3_OCP = 0, 1
 XK_KCACHE_MXFP4, XK_KCACHE_FP8_E4M3_OCP = 0, 1
+XK_IN_FP32, XK_IN_BF16 = 0, 1
 
 EXPORTED = ("xk_indexer_logits", "xk_indexer_logits_paged", "xk_indexer_topk_workspace_size",
-            "xk_indexer_topk", "xk_mxfp4_paged_gather", "xk_status_string", "xk_last_error")
+            "xk_indexer_topk", "xk_mxfp4_paged_gather", "xk_quant_fp8_rows", "xk_mxfp4_cache_write",
+            "xk_status_string", "xk_last_error")
 
 
 class XKError(RuntimeError):
@@ -46,6 +48,11 @@ def _load() -> ctypes.CDLL:
     lib.xk_indexer_topk.restype = I
     lib.xk_mxfp4_paged_gather.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.xk_mxfp4_paged_gather.restype = I
+    L = ctypes.c_int64
+    lib.xk_quant_fp8_rows.argtypes = [P, I, P, P, L, I, P]
+    lib.xk_quant_fp8_rows.restype = I
+    lib.xk_mxfp4_cache_write.argtypes = [P, I, P, P, P, L, I, I, I, P]
+    lib.xk_mxfp4_cache_write.restype = I
     lib.xk_status_string.argtypes = [I]
     lib.xk_status_string.restype = ctypes.c_char_p
     lib.xk_last_error.argtypes = []
@@ -261,3 +268,41 @@ def xk_mxfp4_paged_gather(kv_fp4, kv_scale, block_table, sel_pos, row_seq=None, 
     args, out = gather_args(kv_fp4, kv_scale, block_table, sel_pos, row_seq, out)
     _check(_lib.xk_mxfp4_paged_gather(*args, _stream(stream)))
     return out
+
+
+def _rows_in(x, name):
+    _need(x, name, (torch.float32, torch.bfloat16), 2)
+    return XK_IN_BF16 if x.dtype == torch.bfloat16 else XK_IN_FP32
+
+
+def xk_quant_fp8_rows(x, out=None, scale=None, stream=None):
+    """(codes [N,D] float8_e4m3fn, scale [N] fp32) of rows x [N,D] fp32/bf16
+    (see include/xk.h): scale = amax/448, codes = e4m3(x/scale)."""
+    dt = _rows_in(x, "x")
+    N, D = x.shape
+    if out is None:
+        out = torch.empty((N, D), dtype=torch.float8_e4m3fn, device=x.device)
+    if scale is None:
+        scale = torch.empty((N,), dtype=torch.float32, device=x.device)
+    _need(out, "out", (torch.float8_e4m3fn, torch.uint8), 2)
+    _need(scale, "scale", (torch.float32,), 1)
+    if tuple(out.shape) != (N, D) or scale.shape[0] != N:
+        raise ValueError("out must be [N,D] and scale [N]")
+    _check(_lib.xk_quant_fp8_rows(_ptr(x), dt, _ptr(out), _ptr(scale), N, D, _stream(stream)))
+    return out, scale
+
+
+def xk_mxfp4_cache_write(x, slots, kv_fp4, kv_scale, stream=None):
+    """Write rows x [N,D] fp32/bf16 into the paged mxfp4 cache at slots [N]
+    int64 (page * bs + row; < 0 skips), in place (see include/xk.h)."""
+    dt = _rows_in(x, "x")
+    N, D = x.shape
+    _need(slots, "slots", (torch.int64,), 1)
+    _need(kv_fp4, "kv_fp4", (torch.uint8,), 3)
+    _need(kv_scale, "kv_scale", (torch.uint8,), 3)
+    NB, bs, half = kv_fp4.shape
+    if slots.shape[0] != N or 2 * half != D or tuple(kv_scale.shape) != (NB, bs, D // 32):
+        raise ValueError("slots [N], kv_fp4 [NB,bs,D/2], kv_scale [NB,bs,D/32] expected")
+    _check(_lib.xk_mxfp4_cache_write(_ptr(x), dt, _ptr(slots), _ptr(kv_fp4), _ptr(kv_scale), N,
+                                     NB, bs, D, _stream(stream)))
+    return kv_fp4, kv_scale

@@ -328,9 +328,9 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void logits_decode_kernel(
 //    group's nibbles are zeroed in registers (scale 127).
 //  * fp8 keys: 32-byte fragments with unit block scales; the per-token fp32
 //    scale multiplies the finished score, as in the dense fp8 path.
-constexpr int kPagedTab = 64;  // staged table entries per workgroup (chunk / 16 + 2)
+constexpr int kPagedTab = 72;  // staged table entries per workgroup (chunk / 16 + 1)
 
-template <bool MXFP4>
+template <bool MXFP4, int kRing = 8>  // kRing: subtiles in flight per wave
 __global__ __launch_bounds__(kDecWaves * 64, 2) void logits_paged_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ kcs,
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void logits_paged_kernel(
   constexpr int kQRow = kHeadDim;              // fp8 q bytes per head
   constexpr int kPitch = kQRow + 16;
   constexpr int kLanesPerRow = kQRow / 16;
-  constexpr int kRing = 8;  // subtiles in flight per wave (two groups)
+  static_assert(kRing % 4 == 0, "whole 64-key groups in flight");
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kHeads * kPitch];
   __shared__ __attribute__((aligned(16))) float w_lds[kHeads];
   __shared__ int32_t tab_lds[kPagedTab];
@@ -635,10 +635,12 @@ hipError_t launch_logits_paged(const void* q, const float* q_scale, const float*
                                const int32_t* limit, const void* k_cache, const void* k_scale,
                                const int32_t* block_table, float* logits, int B, int T, int K,
                                int MB, int bs, bool mxfp4, hipStream_t stream) {
-  // the decode kernel's chunking: 512 or 768 positions per workgroup
+  // 512 to 1024 positions per workgroup (a quarter of the bytes of a bf16
+  // key per position, so longer chunks than the dense decode kernel's;
+  // measured on the Flash and Pro decode shapes)
   const int64_t rows = int64_t(B) * T;
   const int64_t per = (int64_t(K) * rows + 2047) / 2048;
-  int kpw = int(std::min<int64_t>(std::max<int64_t>(per, 2 * kDecWaves * kDecGroup), 3 * kDecWaves * kDecGroup));
+  int kpw = int(std::min<int64_t>(std::max<int64_t>(per, 2 * kDecWaves * kDecGroup), 4 * kDecWaves * kDecGroup));
   kpw = std::min(round_up(kpw, kDecWaves * kDecGroup), round_up(K, kDecWaves * kDecGroup));
   const int nch = (K + kpw - 1) / kpw;
   int bs_log2 = 0;

@@ -125,6 +125,43 @@ XK_EXPORT xk_status xk_indexer_logits_paged(const void* q, const float* q_scale,
                   "xk_indexer_logits_paged launch");
 }
 
+XK_EXPORT xk_status xk_quant_fp8_rows(const void* x, int x_dtype, uint8_t* out, float* scale,
+                                      int64_t N, int D, void* stream) {
+  if (!x || !out || !scale) return fail(XK_ERR_INVALID_ARGUMENT, "null x, out or scale");
+  if (N < 1 || D < 1) return fail(XK_ERR_INVALID_ARGUMENT, "N, D must be >= 1");
+  if (x_dtype != XK_IN_FP32 && x_dtype != XK_IN_BF16)
+    return fail(XK_ERR_INVALID_ARGUMENT, "unknown x dtype");
+  if (D != xk::kHeadDim) return fail(XK_ERR_UNSUPPORTED, "only D=128 is implemented");
+  if (N > (int64_t(1) << 40)) return fail(XK_ERR_UNSUPPORTED, "N above 2^40");
+  if (!aligned(x, x_dtype == XK_IN_FP32 ? 8 : 4) || !aligned(out, 2) || !aligned(scale, 4))
+    return fail(XK_ERR_INVALID_ARGUMENT, "x, out or scale misaligned");
+  xk_status s = check_device();
+  if (s != XK_OK) return s;
+  return launched(xk::launch_quant_fp8_rows(x, x_dtype == XK_IN_BF16, out, scale, N,
+                                            static_cast<hipStream_t>(stream)),
+                  "xk_quant_fp8_rows launch");
+}
+
+XK_EXPORT xk_status xk_mxfp4_cache_write(const void* x, int x_dtype, const int64_t* slots,
+                                         uint8_t* kv_fp4, uint8_t* kv_scale, int64_t N, int NB,
+                                         int bs, int D, void* stream) {
+  if (!x || !slots || !kv_fp4 || !kv_scale)
+    return fail(XK_ERR_INVALID_ARGUMENT, "null x, slots, kv_fp4 or kv_scale");
+  if (N < 1 || NB < 1 || bs < 1 || D < 1)
+    return fail(XK_ERR_INVALID_ARGUMENT, "N, NB, bs, D must be >= 1");
+  if (x_dtype != XK_IN_FP32 && x_dtype != XK_IN_BF16)
+    return fail(XK_ERR_INVALID_ARGUMENT, "unknown x dtype");
+  if (D != xk::kHeadDim) return fail(XK_ERR_UNSUPPORTED, "only D=128 is implemented");
+  if (N > (int64_t(1) << 40)) return fail(XK_ERR_UNSUPPORTED, "N above 2^40");
+  if (!aligned(x, x_dtype == XK_IN_FP32 ? 8 : 4) || !aligned(slots, 8))
+    return fail(XK_ERR_INVALID_ARGUMENT, "x or slots misaligned");
+  xk_status s = check_device();
+  if (s != XK_OK) return s;
+  return launched(xk::launch_mxfp4_write(x, x_dtype == XK_IN_BF16, slots, kv_fp4, kv_scale, N,
+                                         int64_t(NB) * bs, static_cast<hipStream_t>(stream)),
+                  "xk_mxfp4_cache_write launch");
+}
+
 XK_EXPORT size_t xk_indexer_topk_workspace_size(int R, int K, int k) {
   (void)R;
   (void)K;

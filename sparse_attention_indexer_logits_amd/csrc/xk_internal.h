@@ -36,6 +36,10 @@ hipError_t launch_logits_paged(const void* q, const float* q_scale, const float*
                                const int32_t* limit, const void* k_cache, const void* k_scale,
                                const int32_t* block_table, float* logits, int B, int T, int K,
                                int MB, int bs, bool mxfp4, hipStream_t stream);
+hipError_t launch_quant_fp8_rows(const void* x, bool bf16, uint8_t* out, float* scale, int64_t N,
+                                 hipStream_t stream);
+hipError_t launch_mxfp4_write(const void* x, bool bf16, const int64_t* slots, uint8_t* kv_fp4,
+                              uint8_t* kv_scale, int64_t N, int64_t n_slots, hipStream_t stream);
 hipError_t launch_topk(const float* logits, const int32_t* limit, int32_t* idx, int R,
                        int K, int k, hipStream_t stream);
 hipError_t launch_gather(const uint8_t* kv_fp4, const uint8_t* kv_scale,

@@ -28,8 +28,8 @@ def lib():
 def test_header_declares_the_three_operations():
     names = declared_functions()
     for n in ("xk_indexer_logits", "xk_indexer_logits_paged", "xk_indexer_topk",
-              "xk_mxfp4_paged_gather", "xk_indexer_topk_workspace_size", "xk_status_string",
-              "xk_last_error"):
+              "xk_mxfp4_paged_gather", "xk_indexer_topk_workspace_size", "xk_quant_fp8_rows",
+              "xk_mxfp4_cache_write", "xk_status_string", "xk_last_error"):
         assert n in names
 
 
@@ -117,6 +117,32 @@ def test_topk_workspace_is_host_only(lib):
 ])
 def test_gather_validation(lib, args, status, needle):
     assert lib.xk_mxfp4_paged_gather(*args, None) == status
+    assert needle in lib.xk_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    # (x, x_dtype, out, scale, N, D)
+    ((None, 0, FAKE, FAKE, 4, 128), 1, "null"),
+    ((FAKE, 0, FAKE, FAKE, 0, 128), 1, ">= 1"),
+    ((FAKE, 3, FAKE, FAKE, 4, 128), 1, "dtype"),
+    ((FAKE, 0, FAKE, FAKE, 4, 64), 2, "D=128"),
+    ((FAKE + 4, 0, FAKE, FAKE, 4, 128), 1, "misaligned"),
+])
+def test_quant_fp8_rows_validation(lib, args, status, needle):
+    assert lib.xk_quant_fp8_rows(*args, None) == status
+    assert needle in lib.xk_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    # (x, x_dtype, slots, kv_fp4, kv_scale, N, NB, bs, D)
+    ((FAKE, 1, None, FAKE, FAKE, 4, 2, 64, 128), 1, "null"),
+    ((FAKE, 1, FAKE, FAKE, FAKE, 4, 0, 64, 128), 1, ">= 1"),
+    ((FAKE, 2, FAKE, FAKE, FAKE, 4, 2, 64, 128), 1, "dtype"),
+    ((FAKE, 1, FAKE, FAKE, FAKE, 4, 2, 64, 256), 2, "D=128"),
+    ((FAKE, 1, FAKE + 4, FAKE, FAKE, 4, 2, 64, 128), 1, "misaligned"),
+])
+def test_mxfp4_cache_write_validation(lib, args, status, needle):
+    assert lib.xk_mxfp4_cache_write(*args, None) == status
     assert needle in lib.xk_last_error().decode()
 
 
