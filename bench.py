@@ -150,6 +150,109 @@ def cpu_baseline(x, work, budget_s):
             "kind": "oracle", "sample": sample, "ms_per_step": step_s * 1e3}
 
 
+def producers(args):
+    """The producers of the path's quantized inputs on a config's shapes: q
+    (B*T*64 rows) and k (the valid keys) quantized per row to OCP fp8, and k
+    written into the paged mxfp4 cache. Inputs are bf16 rows resident in HBM,
+    drawn N(0,1) with a per-row power-of-two spread; one JSON line."""
+    import torch
+    import oracle
+    import workloads
+    import sparse_attention_indexer_logits_amd as xk
+
+    cfg = workloads.CONFIGS[args.config]
+    rng = np.random.default_rng(cfg.seed)
+    nq = cfg.rows * 64
+    nk = int(workloads.seq_lengths(cfg).sum())
+    bs = workloads.BLOCK_SIZE
+    NB = (nk + bs - 1) // bs
+
+    def draw(n):
+        x = rng.standard_normal((n, 128), dtype=np.float32) * np.exp2(rng.integers(-4, 4, (n, 1)))
+        return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+
+    qx, kx = draw(nq), draw(nk)
+    slots = torch.from_numpy(rng.permutation(NB * bs)[:nk].astype(np.int64))
+    dq, dk, ds = qx.cuda(), kx.cuda(), slots.cuda()
+    q8 = torch.empty((nq, 128), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((nq,), dtype=torch.float32, device="cuda")
+    k8 = torch.empty((nk, 128), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((nk,), dtype=torch.float32, device="cuda")
+    kv = torch.zeros((NB, bs, 64), dtype=torch.uint8, device="cuda")
+    kvs = torch.zeros((NB, bs, 4), dtype=torch.uint8, device="cuda")
+    runs = {
+        "quant_fp8_q": (lambda: xk.xk_quant_fp8_rows(dq, out=q8, scale=qs), nq * (256 + 128 + 4)),
+        "quant_fp8_k": (lambda: xk.xk_quant_fp8_rows(dk, out=k8, scale=ks), nk * (256 + 128 + 4)),
+        "mxfp4_write_k": (lambda: xk.xk_mxfp4_cache_write(dk, ds, kv, kvs), nk * (256 + 8 + 68)),
+    }
+    # checked pass: the GPU results against the oracle on the first rows
+    for f, _ in runs.values():
+        f()
+    torch.cuda.synchronize()
+    n_chk = min(4096, nk)
+    c, s_ = oracle.quant_fp8_rows(kx[:n_chk].float().numpy())
+    if not (np.array_equal(k8[:n_chk].cpu().numpy(), c) and np.array_equal(ks[:n_chk].cpu().numpy(), s_)):
+        raise RuntimeError("fp8 quantizer differs from the oracle")
+    stages = {}
+    total_bytes, total_s = 0, 0.0
+    n_in_graph = 20
+    for name, (f, nbytes) in runs.items():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n_in_graph):
+                f()
+        for _ in range(max(1, args.warmup // n_in_graph)):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // n_in_graph)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / (reps * n_in_graph)
+        ach = nbytes / sec / 1e9
+        stages[name] = {"bound": "hbm", "us": sec * 1e6, "achieved": ach, "peak": PEAK["hbm"],
+                        "unit": "GB/s", "frac": ach / PEAK["hbm"], "bytes": nbytes}
+        total_bytes += nbytes
+        total_s += sec
+    dom = max(stages, key=lambda k: stages[k]["us"])
+    roof = {k: stages[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roof["kernel"], roof["traffic"] = dom, None
+    line = {
+        "metric": "indexer input producers GB/s (fp8 row quantizer, mxfp4 cache writer)",
+        "value": total_bytes / total_s / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": total_s * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16->fp8/mxfp4",
+        "data": "synthetic: seeded N(0,1) bf16 rows with a per-row power-of-two spread",
+        "config": {"workload": f"{cfg.name} producers", "q_rows": nq, "k_rows": nk, "D": 128,
+                   "cache": "mxfp4 E2M1+E8M0, block 64"},
+        "stages": stages, "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        except Exception:
+            cores = 1
+        n = min(nk, 65536)
+        xs = kx[:n].float().numpy()
+        t0 = time.perf_counter()
+        oracle.quant_fp8_rows(xs)
+        t_q = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.mxfp4_encode_rows(xs)
+        t_e = time.perf_counter() - t0
+        step_s = (nq + nk) * t_q / n + nk * t_e / n
+        line["cpu_baseline"] = {"value": total_bytes / step_s / 1e9, "unit": "GB/s", "cores": int(cores),
+                                "kind": "oracle",
+                                "sample": f"{n} k rows quantized to fp8 ({t_q:.1f} s) and encoded to mxfp4 "
+                                          f"({t_e:.1f} s), numpy, scaled to the step's q and k rows",
+                                "ms_per_step": step_s * 1e3}
+    print(json.dumps(line), flush=True)
+
+
 def copy_calibration(nbytes=1 << 30, reps=4):
     """A plain device copy of known size, to scale rocprofv3 FETCH_SIZE/WRITE_SIZE."""
     import torch
@@ -173,9 +276,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (PMC byte-counter calibration)")
+    ap.add_argument("--producers", action="store_true",
+                    help="time the input producers (fp8 row quantizer for q and k, mxfp4 cache "
+                         "writer for k) on the config's shapes instead of the step")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.producers:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        producers(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the indexer path here "

@@ -198,8 +198,8 @@ typedef enum {
  * all-zero row), out[n,d] = e4m3 round-to-nearest-even of the fp32
  * quotient x[n,d] / scale[n], saturated to +-448.
  *
- *   x      [N,D] fp32 or bf16 (x_dtype), 8-byte (fp32) / 4-byte (bf16) aligned
- *   out    [N,D] e4m3 bytes (2-byte aligned); scale [N] fp32
+ *   x      [N,D] fp32 or bf16 (x_dtype), 16-byte aligned
+ *   out    [N,D] e4m3 bytes (8-byte aligned); scale [N] fp32
  *   N >= 1, D must be 128 (XK_ERR_UNSUPPORTED otherwise).
  */
 xk_status xk_quant_fp8_rows(const void* x, int x_dtype, uint8_t* out, float* scale, int64_t N, int D,
@@ -219,8 +219,8 @@ xk_status xk_quant_fp8_rows(const void* x, int x_dtype, uint8_t* out, float* sca
  * in the low nibble of kv_fp4[slot][i]. Rows with slots[n] < 0 or >= NB*bs
  * are skipped. Rows with equal slots race (last writer wins).
  *
- *   x        [N,D] fp32 or bf16 rows; slots [N] int64
- *   kv_fp4   [NB,bs,D/2] u8; kv_scale [NB,bs,D/32] u8 (written in place)
+ *   x        [N,D] fp32 or bf16 rows (16-byte aligned); slots [N] int64
+ *   kv_fp4   [NB,bs,D/2] u8 (4-byte aligned); kv_scale [NB,bs,D/32] u8 (in place)
  *   N >= 1, D must be 128.
  */
 xk_status xk_mxfp4_cache_write(const void* x, int x_dtype, const int64_t* slots, uint8_t* kv_fp4,

@@ -13,11 +13,14 @@
 //    group), E8M0 byte e + 127, element = E2M1 round-to-nearest-even of
 //    x * 2^-e saturated to +-6, element 2i in the low nibble.
 //
-// One wave per 128-element row, two elements per lane: lane l holds
-// elements 2l and 2l+1, so a row of 16 lanes is one 32-element group and a
-// lane's two nibbles are one cache byte. Integer codes are decided from
-// float32 values exactly as the definitions state them (IEEE division,
-// power-of-two scaling, rint = round-to-nearest-even).
+// Sixteen lanes per 128-element row, eight consecutive elements per lane
+// (one 16- or 32-byte load): a DPP row of 16 lanes is one data row, four
+// lanes one 32-element group, and a lane's eight nibbles one 32-bit word
+// of the cache row. A wave takes 4 rows per pass and issues the loads of
+// kPasses passes before any arithmetic, to keep enough bytes in flight.
+// Integer codes are decided from float32 values exactly as the definitions
+// state them (IEEE division, power-of-two scaling, rint = round to nearest
+// even).
 #include <math.h>
 
 #include "xk_internal.h"
@@ -25,26 +28,20 @@
 namespace xk {
 namespace {
 
-constexpr int kQuantWaves = 4;  // rows per 256-thread workgroup
+constexpr int kQuantWaves = 4;                   // waves per workgroup
+constexpr int kPasses = 4;                       // 4 rows per wave per pass
+constexpr int kRowsPerWave = 4 * kPasses;
+constexpr int kRowsPerBlock = kQuantWaves * kRowsPerWave;
 
-// max over the 16 lanes of a DPP row (quad swaps, half mirror, mirror)
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x140, 0xF, 0xF, false)));
-  return v;
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF,
+                                                             false)));
 }
 
-// max over the wave (row maxima read as scalars)
-__device__ __forceinline__ float wave_max(float v) {
-  v = row16_max(v);
-  const float a = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
-                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16)));
-  const float b = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
-                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
-  return fmaxf(a, b);
-}
+// max over each quad of lanes (a 32-element group), then over each row of 16 (a data row)
+__device__ __forceinline__ float quad_max(float v) { return dpp_max<0x4E>(dpp_max<0xB1>(v)); }
+__device__ __forceinline__ float row16_max(float v) { return dpp_max<0x140>(dpp_max<0x141>(quad_max(v))); }
 
 // OCP e4m3 code of v: round to nearest even, saturated to +-448.
 __device__ __forceinline__ uint32_t e4m3_rne(float v) {
@@ -75,62 +72,109 @@ __device__ __forceinline__ uint32_t e2m1_rne(float v) {
   return sign | m;
 }
 
+// Eight consecutive elements of a row: lane (row % 4 in the pass, l % 16)
+// holds elements 8*(l % 16) .. +7.
+struct Eight {
+  u32x4 w[2];  // bf16: w[0] holds eight bf16; fp32: w[0], w[1] hold eight floats
+};
+
 template <bool BF16>
-__device__ __forceinline__ void load_pair(const void* x, int64_t row, int lane, float& x0, float& x1) {
+__device__ __forceinline__ Eight load8(const void* x, int64_t row, int col) {
+  Eight e;
   if constexpr (BF16) {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(x)[row * 64 + lane];  // two bf16
-    x0 = __uint_as_float(w << 16);
-    x1 = __uint_as_float(w & 0xFFFF0000u);
+    e.w[0] = reinterpret_cast<const u32x4*>(x)[row * 16 + col];
+    e.w[1] = u32x4{0u, 0u, 0u, 0u};
   } else {
-    const float2 f = reinterpret_cast<const float2*>(x)[row * 64 + lane];
-    x0 = f.x;
-    x1 = f.y;
+    e.w[0] = reinterpret_cast<const u32x4*>(x)[row * 32 + 2 * col];
+    e.w[1] = reinterpret_cast<const u32x4*>(x)[row * 32 + 2 * col + 1];
+  }
+  return e;
+}
+
+template <bool BF16>
+__device__ __forceinline__ float elem(const Eight& e, int i) {
+  if constexpr (BF16) {
+    const uint32_t w = e.w[0][i >> 1];
+    return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  } else {
+    return __uint_as_float(e.w[i >> 2][i & 3]);
   }
 }
 
 template <bool BF16>
 __global__ __launch_bounds__(kQuantWaves * 64) void quant_fp8_rows_kernel(
     const void* __restrict__ x, uint8_t* __restrict__ out, float* __restrict__ scale, int64_t N) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * kQuantWaves + (threadIdx.x >> 6);
-  if (row >= N) return;  // whole wave
-  float x0, x1;
-  load_pair<BF16>(x, row, lane, x0, x1);
-  const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-  const float s = amax > 0.f ? amax / 448.f : 1.f;
-  const uint32_t c = e4m3_rne(x0 / s) | (e4m3_rne(x1 / s) << 8);
-  reinterpret_cast<uint16_t*>(out)[row * 64 + lane] = uint16_t(c);
-  if (lane == 0) scale[row] = s;
+  const int lane = threadIdx.x & 63, col = lane & 15;
+  const int64_t base = int64_t(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6) * kRowsPerWave + (lane >> 4);
+  Eight v[kPasses];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {  // all loads first (rows past N read row N-1)
+    const int64_t row = min(base + 4 * p, N - 1);
+    v[p] = load8<BF16>(x, row, col);
+  }
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int64_t row = base + 4 * p;
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(elem<BF16>(v[p], i)));
+    amax = row16_max(amax);
+    const float s = amax > 0.f ? amax / 448.f : 1.f;
+    uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= e4m3_rne(elem<BF16>(v[p], i) / s) << (8 * i);
+      hi |= e4m3_rne(elem<BF16>(v[p], 4 + i) / s) << (8 * i);
+    }
+    if (row < N) {
+      reinterpret_cast<uint2*>(out)[row * 16 + col] = make_uint2(lo, hi);
+      if (col == 0) scale[row] = s;
+    }
+  }
 }
 
 template <bool BF16>
 __global__ __launch_bounds__(kQuantWaves * 64) void mxfp4_write_kernel(
     const void* __restrict__ x, const int64_t* __restrict__ slots, uint8_t* __restrict__ kv_fp4,
     uint8_t* __restrict__ kv_scale, int64_t N, int64_t n_slots) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * kQuantWaves + (threadIdx.x >> 6);
-  if (row >= N) return;
-  const int64_t slot = slots[row];
-  if (slot < 0 || slot >= n_slots) return;  // skipped row (whole wave)
-  float x0, x1;
-  load_pair<BF16>(x, row, lane, x0, x1);
-  const float amax = row16_max(fmaxf(fabsf(x0), fabsf(x1)));  // this lane's 32-element group
-  int e = -127;
-  if (amax > 0.f) {
-    int ex;
-    frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1): floor(log2 amax) = ex - 1
-    e = min(max(ex - 1 - 2, -127), 127);
+  const int lane = threadIdx.x & 63, col = lane & 15;
+  const int64_t base = int64_t(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6) * kRowsPerWave + (lane >> 4);
+  Eight v[kPasses];
+  int64_t slot[kPasses];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int64_t row = min(base + 4 * p, N - 1);
+    v[p] = load8<BF16>(x, row, col);
+    slot[p] = base + 4 * p < N ? slots[row] : -1;
   }
-  const uint32_t b = e2m1_rne(ldexpf(x0, -e)) | (e2m1_rne(ldexpf(x1, -e)) << 4);
-  kv_fp4[slot * 64 + lane] = uint8_t(b);
-  if ((lane & 15) == 0) kv_scale[slot * 4 + (lane >> 4)] = uint8_t(e + 127);
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(elem<BF16>(v[p], i)));
+    amax = quad_max(amax);  // this lane's 32-element group
+    int e = -127;
+    if (amax > 0.f) {
+      int ex;
+      frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1): floor(log2 amax) = ex - 1
+      e = min(max(ex - 1 - 2, -127), 127);
+    }
+    uint32_t word = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word |= e2m1_rne(ldexpf(elem<BF16>(v[p], i), -e)) << (4 * i);
+    const int64_t sl = slot[p];
+    if (sl >= 0 && sl < n_slots) {
+      reinterpret_cast<uint32_t*>(kv_fp4)[sl * 16 + col] = word;
+      if ((col & 3) == 0) kv_scale[sl * 4 + (col >> 2)] = uint8_t(e + 127);
+    }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_quant_fp8_rows(const void* x, bool bf16, uint8_t* out, float* scale, int64_t N,
                                  hipStream_t stream) {
-  const dim3 grid(unsigned((N + kQuantWaves - 1) / kQuantWaves));
+  const dim3 grid(unsigned((N + kRowsPerBlock - 1) / kRowsPerBlock));
   if (bf16)
     hipLaunchKernelGGL(quant_fp8_rows_kernel<true>, grid, dim3(kQuantWaves * 64), 0, stream, x, out, scale, N);
   else
@@ -140,7 +184,7 @@ hipError_t launch_quant_fp8_rows(const void* x, bool bf16, uint8_t* out, float* 
 
 hipError_t launch_mxfp4_write(const void* x, bool bf16, const int64_t* slots, uint8_t* kv_fp4,
                               uint8_t* kv_scale, int64_t N, int64_t n_slots, hipStream_t stream) {
-  const dim3 grid(unsigned((N + kQuantWaves - 1) / kQuantWaves));
+  const dim3 grid(unsigned((N + kRowsPerBlock - 1) / kRowsPerBlock));
   if (bf16)
     hipLaunchKernelGGL(mxfp4_write_kernel<true>, grid, dim3(kQuantWaves * 64), 0, stream, x, slots, kv_fp4,
                        kv_scale, N, n_slots);

@@ -133,8 +133,8 @@ XK_EXPORT xk_status xk_quant_fp8_rows(const void* x, int x_dtype, uint8_t* out, 
     return fail(XK_ERR_INVALID_ARGUMENT, "unknown x dtype");
   if (D != xk::kHeadDim) return fail(XK_ERR_UNSUPPORTED, "only D=128 is implemented");
   if (N > (int64_t(1) << 40)) return fail(XK_ERR_UNSUPPORTED, "N above 2^40");
-  if (!aligned(x, x_dtype == XK_IN_FP32 ? 8 : 4) || !aligned(out, 2) || !aligned(scale, 4))
-    return fail(XK_ERR_INVALID_ARGUMENT, "x, out or scale misaligned");
+  if (!aligned(x, 16) || !aligned(out, 8) || !aligned(scale, 4))
+    return fail(XK_ERR_INVALID_ARGUMENT, "x, out or scale misaligned (16, 8, 4 bytes)");
   xk_status s = check_device();
   if (s != XK_OK) return s;
   return launched(xk::launch_quant_fp8_rows(x, x_dtype == XK_IN_BF16, out, scale, N,
@@ -153,8 +153,8 @@ XK_EXPORT xk_status xk_mxfp4_cache_write(const void* x, int x_dtype, const int64
     return fail(XK_ERR_INVALID_ARGUMENT, "unknown x dtype");
   if (D != xk::kHeadDim) return fail(XK_ERR_UNSUPPORTED, "only D=128 is implemented");
   if (N > (int64_t(1) << 40)) return fail(XK_ERR_UNSUPPORTED, "N above 2^40");
-  if (!aligned(x, x_dtype == XK_IN_FP32 ? 8 : 4) || !aligned(slots, 8))
-    return fail(XK_ERR_INVALID_ARGUMENT, "x or slots misaligned");
+  if (!aligned(x, 16) || !aligned(slots, 8) || !aligned(kv_fp4, 4))
+    return fail(XK_ERR_INVALID_ARGUMENT, "x, slots or kv_fp4 misaligned (16, 8, 4 bytes)");
   xk_status s = check_device();
   if (s != XK_OK) return s;
   return launched(xk::launch_mxfp4_write(x, x_dtype == XK_IN_BF16, slots, kv_fp4, kv_scale, N,
