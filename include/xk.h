@@ -143,7 +143,7 @@ size_t xk_indexer_topk_workspace_size(int R, int K, int k);
  *   limit      [R]   int32 inclusive last valid key, or NULL (n = K)
  *   idx        [R,k] int32 output; every element is written
  *   1 <= k <= 2048, else XK_ERR_UNSUPPORTED; K >= 1 (rows up to 16384 keys
- *   are held in registers; longer rows keep a 24576-key prefix there and
+ *   are held in registers; longer rows keep a 16384-key prefix there and
  *   stream the rest once).
  *   workspace  device buffer of xk_indexer_topk_workspace_size(R,K,k) bytes
  *              (may be NULL when that size is 0)

@@ -8,7 +8,7 @@
 //
 // One workgroup per row. Rows up to 16384 keys are read from HBM once and
 // stay in VGPRs (V values per thread, j = tid + BLOCK*v); longer rows keep a
-// 24576-key prefix in VGPRs and stream the rest once (topk_long_kernel).
+// 16384-key prefix in VGPRs and stream the rest once (topk_long_kernel).
 // Scores become order-preserving u32 keys (-0.0 folded to +0.0); key 0 marks
 // a slot past the row's end.
 //
@@ -614,23 +614,37 @@ __device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t rs, int base, 
 
 // g(scores, base) over chunks of entries [j_lo, j_hi) of the row streamed
 // from memory (entry u of this thread is j = base + BLOCK*u + tid; the
-// caller masks j >= j_hi), BLOCK*U per chunk, two register buffers
-// alternating: the next chunk's
-// loads are in flight while this one is processed. `first` holds the first
-// chunk's loads (load_chunk at j_lo), issued by the caller as early as it
-// likes; rs covers at least [0, j_hi) (and reads 0 past its end). Each
-// iteration processes two chunks unconditionally (entries past j_hi are
-// masked): with no exit between a load and its use, the compiler issues the
-// loads where they stand instead of next to their use.
-template <int BLOCK, int U, typename G>
-__device__ __forceinline__ void stream_chunks(__amdgpu_buffer_rsrc_t rs, int j_lo, int j_hi, float (&first)[U],
-                                              G g) {
-  float nxt[U];
-  for (int base = j_lo; base < j_hi; base += 2 * BLOCK * U) {
-    load_chunk<BLOCK, U>(rs, base + BLOCK * U, nxt);
-    g(first, base);
-    load_chunk<BLOCK, U>(rs, base + 2 * BLOCK * U, first);
-    g(nxt, base + BLOCK * U);
+// caller masks j >= j_hi), BLOCK*U per chunk, three register buffers in
+// rotation: two chunks' loads are in flight while one is processed. `c0`
+// and `c1` hold the first two chunks' loads (load_chunk at j_lo and
+// j_lo + BLOCK*U), issued by the caller as early as it likes; rs covers at
+// least [0, j_hi) (and reads 0 past its end). Each iteration processes
+// three chunks unconditionally (entries past j_hi are masked): with no exit
+// between a load and its use, the compiler issues the loads where they
+// stand instead of next to their use.
+template <int BLOCK, int U, int NBUF, typename G>
+__device__ __forceinline__ void stream_chunks(__amdgpu_buffer_rsrc_t rs, int j_lo, int j_hi, float (&c0)[U],
+                                              float (&c1)[U], G g) {
+  static_assert(NBUF == 2 || NBUF == 3, "two or three buffers");
+  constexpr int C = BLOCK * U;
+  if constexpr (NBUF == 3) {
+    float c2[U];
+    for (int base = j_lo; base < j_hi; base += 3 * C) {
+      load_chunk<BLOCK, U>(rs, base + 2 * C, c2);
+      g(c0, base);
+      load_chunk<BLOCK, U>(rs, base + 3 * C, c0);
+      g(c1, base + C);
+      load_chunk<BLOCK, U>(rs, base + 4 * C, c1);
+      g(c2, base + 2 * C);
+    }
+  } else {  // c1 unused: one chunk in flight while one is processed
+    float nxt[U];
+    for (int base = j_lo; base < j_hi; base += 2 * C) {
+      load_chunk<BLOCK, U>(rs, base + C, nxt);
+      g(c0, base);
+      load_chunk<BLOCK, U>(rs, base + 2 * C, c0);
+      g(nxt, base + C);
+    }
   }
 }
 
@@ -736,7 +750,7 @@ __device__ __forceinline__ void append_list(TopkShared<BLOCK, CAP>& sh, KeyAt ke
 // >= b* and the keys >= tau of the rest of the row (streamed once) form an
 // LDS candidate list, from which the winners are selected exactly. If the list runs out of room (scores
 // crowded into b*), the row falls back to multi-pass streaming selection.
-template <int BLOCK, int V, int CAP>
+template <int BLOCK, int V, int CAP, int NBUF = 2>
 __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restrict__ logits,
                                                           const int32_t* __restrict__ limit,
                                                           int32_t* __restrict__ idx, int K, int k) {
@@ -753,8 +767,9 @@ __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restric
   const auto rs = row_rsrc(x, n);
   float raw[V];
   load_chunk<BLOCK, V>(rs, 0, raw);
-  float first[U];  // the streamed part's first chunk, in flight during the prefix's threshold
+  float first[U], second[U];  // the streamed part's first chunks, in flight during the prefix's threshold
   load_chunk<BLOCK, U>(rs, prefix, first);
+  if constexpr (NBUF == 3) load_chunk<BLOCK, U>(rs, prefix + BLOCK * U, second);
   uint32_t key[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) key[v] = tid + BLOCK * v < prefix ? order_key(raw[v]) : 0u;
@@ -786,7 +801,7 @@ __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restric
   // monotone in the score, so one float compare per key, and only joining
   // keys are converted)
   const float tau_f = key_value(sh.tau);
-  stream_chunks<BLOCK, U>(rs, prefix, n, first, [&](const float (&c)[U], int base) {
+  stream_chunks<BLOCK, U, NBUF>(rs, prefix, n, first, second, [&](const float (&c)[U], int base) {
     append_list<BLOCK, CAP, U>(
         sh, [&](int u) { return order_key(c[u]); }, [&](int u) { return uint32_t(base + BLOCK * u + tid); },
         [&](int u) { return base + BLOCK * u + tid < n && c[u] >= tau_f; });
@@ -828,7 +843,7 @@ hipError_t launch_topk(const float* logits, const int32_t* limit, int32_t* idx, 
   if (K <= 256 * 16) return launch_one<256, 16, 256>(logits, limit, idx, R, K, k, stream);
   if (K <= 1024 * 8) return launch_one<1024, 8, 1024>(logits, limit, idx, R, K, k, stream);
   if (K <= 1024 * 16) return launch_one<1024, 16, 1024>(logits, limit, idx, R, K, k, stream);
-  hipLaunchKernelGGL((topk_long_kernel<1024, 24, 8192>), dim3(unsigned(R)), dim3(1024), 0, stream,
+  hipLaunchKernelGGL((topk_long_kernel<1024, 16, 8192>), dim3(unsigned(R)), dim3(1024), 0, stream,
                      logits, limit, idx, K, k);
   return hipGetLastError();
 }
