@@ -6,7 +6,8 @@ Prints ONE JSON line. `value` is the indexer-logits throughput of the whole
 step (algorithmic logits FLOPs / step wall time), `topk_gather_GBps` the
 algorithmic bytes of top-k + gather over their kernel time; `stages` has every
 kernel's average duration against its roof, and `roofline` repeats the
-dominant kernel.
+dominant kernel. Prefill configs also time the fused step
+(xk_indexer_logits_topk -> gather, no score matrix) under `fused`.
 
 Steps are replayed from HIP graphs (one captured step per input copy), so the
 timed loop measures the GPU rather than Python's launch cost; before timing,
@@ -253,6 +254,66 @@ def producers(args):
     print(json.dumps(line), flush=True)
 
 
+def _graph_us(torch, launches, reps):
+    """Average duration of one launch in a graph of back-to-back launches,
+    timed with events on the launch stream."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in launches:
+            f()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * len(launches))
+
+
+def fused_timing(args, cfg, steps, n_sets, eager_out, ms):
+    """Prefill shapes: the step with the fused logits -> top-k call in place of
+    the two kernels (xk_indexer_logits_topk, then the gather). Its indices and
+    gathered rows must equal the eager three-kernel step's bit for bit."""
+    import torch
+    ws = None
+    for s in steps:
+        ws = s.enable_fused(ws)
+    base = steps[0]
+    base.idx.fill_(-7)
+    base.gathered.fill_(-7)
+    base.run_fused()
+    torch.cuda.synchronize()
+    if not (torch.equal(base.idx, eager_out[1]) and torch.equal(base.gathered, eager_out[2])):
+        raise RuntimeError("fused logits -> top-k differs from the three-kernel step")
+    graphs = []
+    for s in steps:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s.run_fused()
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % n_sets].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % n_sets].replay()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    if not (torch.equal(base.idx, eager_out[1]) and torch.equal(base.gathered, eager_out[2])):
+        raise RuntimeError("fused graph replays differ from the three-kernel step")
+    n_in_graph = 20
+    us = _graph_us(torch, [steps[i % n_sets].run_logits_topk for i in range(n_in_graph)],
+                   max(1, args.steps // n_in_graph))
+    unfused = (ms["logits"] + ms["topk"]) * 1e3
+    return {"ms_per_step": ms_step, "logits_topk_us": us, "unfused_logits_plus_topk_us": unfused,
+            "speedup_vs_unfused": unfused / us,
+            "workspace_MiB": ws.numel() * ws.element_size() / 2 ** 20,
+            "score_matrix_MiB": cfg.B * cfg.T * cfg.K * 4 / 2 ** 20,
+            "note": "xk_indexer_logits_topk + gather; same indices and rows as the step"}
+
+
 def copy_calibration(nbytes=1 << 30, reps=4):
     """A plain device copy of known size, to scale rocprofv3 FETCH_SIZE/WRITE_SIZE."""
     import torch
@@ -387,6 +448,8 @@ def main():
         torch.cuda.synchronize()
         ms[name] = e0.elapsed_time(e1) / (reps * n_in_graph)
 
+    fused = fused_timing(args, cfg, steps, n_sets, eager_out, ms) if cfg.T >= 8 and cfg.kcache is None else None
+
     prefill = cfg.T >= 8
     mfma_peak = PEAK["mfma_fp8" if cfg.dtype == "fp8" else "mfma_bf16"]
     stages = {}
@@ -428,6 +491,9 @@ def main():
         "logits_kernel_TFLOPs": work["logits_flops"] / (ms["logits"] / 1e3) / 1e12,
         "stages": stages, "roofline": roof, "work": work,
     }
+    if fused is not None:
+        fused["value"] = work["logits_flops"] / (fused["ms_per_step"] / 1e3) / 1e12
+        line["fused"] = fused
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x, work, args.cpu_budget)
     print(json.dumps(line), flush=True)

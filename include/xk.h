@@ -5,6 +5,7 @@
  *   xk_indexer_logits        weighted-ReLU MQA score over all keys (bf16 or OCP fp8)
  *   xk_indexer_logits_paged  the same score with keys in a paged mxfp4 / fp8 cache
  *   xk_indexer_topk          deterministic per-query top-k of those scores
+ *   xk_indexer_logits_topk   both at once, without the score matrix for prefill shapes
  *   xk_mxfp4_paged_gather    mxfp4 paged KV rows of the selected keys, decoded to bf16
  * and the producers of their quantized inputs:
  *   xk_quant_fp8_rows        per-row OCP fp8 quantizer (q per token and head, k per token)
@@ -151,6 +152,45 @@ size_t xk_indexer_topk_workspace_size(int R, int K, int k);
 xk_status xk_indexer_topk(const float* logits, const int32_t* limit, int32_t* idx,
                           int R, int K, int k,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace xk_indexer_logits_topk needs for these sizes.
+ * Pure host function; returns 0 for sizes xk_indexer_logits_topk would
+ * reject. Prefill shapes need about 8 * min(K, 16384) bytes per query plus
+ * up to 64 scratch rows of K scores; few-query shapes need the B*T*K scores.
+ */
+size_t xk_indexer_logits_topk_workspace_size(int B, int T, int K, int k, int dtype);
+
+/*
+ * Fused indexer logits -> top-k.
+ *
+ * Defines the composition of the two calls above (page "DeepSeek V4 Flash
+ * on a single AMD MI300X", "The patches": a global top-k index preparation
+ * for prefill and the deterministic top-k; "Performance", prefill: the
+ * deterministic top-k milestone): idx[b*T+t, :] is exactly what
+ * xk_indexer_logits followed by xk_indexer_topk (limit read as [B*T])
+ * write for the same arguments, element for element, but for prefill
+ * shapes without the [B,T,K] score matrix: keys whose score reaches a lower
+ * bound on the query's k-th largest score (derived on the fly from scores
+ * already seen) are kept as candidates, and the top-k is selected from
+ * them. Rows whose candidates overflow their room are rescored and
+ * selected from the full row, so the result is exact for any input.
+ *
+ *   q, q_scale, k, k_scale, w, limit, B, T, K, H, D, dtype: as for
+ *               xk_indexer_logits
+ *   idx         [B*T, topk] int32 output; every element is written
+ *   1 <= topk <= 2048, else XK_ERR_UNSUPPORTED.
+ *   workspace   device buffer of at least
+ *               xk_indexer_logits_topk_workspace_size(B, T, K, topk, dtype)
+ *               bytes, 256-byte aligned; its contents on entry do not
+ *               matter and are clobbered. Calls that share a workspace
+ *               must be ordered on one stream.
+ */
+xk_status xk_indexer_logits_topk(const void* q, const float* q_scale,
+                                 const void* k, const float* k_scale,
+                                 const float* w, const int32_t* limit, int32_t* idx,
+                                 int B, int T, int K, int H, int D, int topk, int dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * mxfp4 paged KV gather.

@@ -22,7 +22,8 @@ XK_KCACHE_MXFP4, XK_KCACHE_FP8_E4M3_OCP = 0, 1
 XK_IN_FP32, XK_IN_BF16 = 0, 1
 
 EXPORTED = ("xk_indexer_logits", "xk_indexer_logits_paged", "xk_indexer_topk_workspace_size",
-            "xk_indexer_topk", "xk_mxfp4_paged_gather", "xk_quant_fp8_rows", "xk_mxfp4_cache_write",
+            "xk_indexer_topk", "xk_indexer_logits_topk_workspace_size", "xk_indexer_logits_topk",
+            "xk_mxfp4_paged_gather", "xk_quant_fp8_rows", "xk_mxfp4_cache_write",
             "xk_status_string", "xk_last_error")
 
 
@@ -46,6 +47,10 @@ def _load() -> ctypes.CDLL:
     lib.xk_indexer_topk_workspace_size.restype = Z
     lib.xk_indexer_topk.argtypes = [P, P, P, I, I, I, P, Z, P]
     lib.xk_indexer_topk.restype = I
+    lib.xk_indexer_logits_topk_workspace_size.argtypes = [I, I, I, I, I]
+    lib.xk_indexer_logits_topk_workspace_size.restype = Z
+    lib.xk_indexer_logits_topk.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P]
+    lib.xk_indexer_logits_topk.restype = I
     lib.xk_mxfp4_paged_gather.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.xk_mxfp4_paged_gather.restype = I
     L = ctypes.c_int64
@@ -93,10 +98,9 @@ def _need(t, name, dtypes, ndim):
         raise ValueError(f"{name} must be a contiguous {ndim}-d tensor, got {tuple(t.shape)}")
 
 
-def logits_args(q, k, w, limit=None, q_scale=None, k_scale=None, out=None):
-    """Validate the arguments of xk_indexer_logits and return (C arguments
-    without the stream, out). Callers that launch the same call repeatedly
-    (IndexerStep) keep the tuple and skip re-validation."""
+def _logits_inputs(q, k, w, limit, q_scale, k_scale):
+    """Check the score inputs shared by xk_indexer_logits and
+    xk_indexer_logits_topk; returns (B, T, K, H, D, fp8)."""
     _need(q, "q", (torch.bfloat16, torch.float8_e4m3fn, torch.uint8), 4)
     B, T, H, D = q.shape
     fp8 = q.dtype != torch.bfloat16
@@ -116,6 +120,14 @@ def logits_args(q, k, w, limit=None, q_scale=None, k_scale=None, out=None):
         _need(k_scale, "k_scale", (torch.float32,), 2)
         if tuple(q_scale.shape) != (B, T, H) or tuple(k_scale.shape) != (B, K):
             raise ValueError("q_scale must be [B,T,H] and k_scale [B,K]")
+    return B, T, K, H, D, fp8
+
+
+def logits_args(q, k, w, limit=None, q_scale=None, k_scale=None, out=None):
+    """Validate the arguments of xk_indexer_logits and return (C arguments
+    without the stream, out). Callers that launch the same call repeatedly
+    (IndexerStep) keep the tuple and skip re-validation."""
+    B, T, K, H, D, fp8 = _logits_inputs(q, k, w, limit, q_scale, k_scale)
     if out is None:
         out = torch.empty((B, T, K), dtype=torch.float32, device=q.device)
     _need(out, "out", (torch.float32,), 3)
@@ -228,6 +240,43 @@ def xk_indexer_topk(logits, k: int, limit=None, out=None, workspace=None, stream
     """
     args, out, _ = topk_args(logits, k, limit, out, workspace)
     _check(_lib.xk_indexer_topk(*args, _stream(stream)))
+    return out
+
+
+def xk_indexer_logits_topk_workspace_size(B: int, T: int, K: int, k: int, dtype: int) -> int:
+    return int(_lib.xk_indexer_logits_topk_workspace_size(B, T, K, k, dtype))
+
+
+def logits_topk_args(q, k, w, topk: int, limit=None, q_scale=None, k_scale=None, out=None,
+                     workspace=None):
+    """Validate the arguments of xk_indexer_logits_topk; returns (C arguments
+    without the stream, out, workspace). A workspace of the size the library
+    asks for is allocated when none is given."""
+    B, T, K, H, D, fp8 = _logits_inputs(q, k, w, limit, q_scale, k_scale)
+    dtype = XK_FP8_E4M3_OCP if fp8 else XK_BF16
+    if out is None:
+        out = torch.empty((B * T, topk), dtype=torch.int32, device=q.device)
+    _need(out, "out", (torch.int32,), 2)
+    if tuple(out.shape) != (B * T, topk):
+        raise ValueError("out must be [B*T,topk]")
+    need = xk_indexer_logits_topk_workspace_size(B, T, K, topk, dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if ws_bytes < need:
+        raise ValueError("workspace too small")
+    args = (_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), _ptr(limit), _ptr(out),
+            B, T, K, H, D, topk, dtype, _ptr(workspace), ws_bytes)
+    return args, out, workspace
+
+
+def xk_indexer_logits_topk(q, k, w, topk: int, limit=None, q_scale=None, k_scale=None, out=None,
+                           workspace=None, stream=None):
+    """idx [B*T,topk] int32 = xk_indexer_topk(xk_indexer_logits(...)), without the
+    score matrix for prefill shapes (see include/xk.h). Inputs as for
+    xk_indexer_logits."""
+    args, out, _ = logits_topk_args(q, k, w, topk, limit, q_scale, k_scale, out, workspace)
+    _check(_lib.xk_indexer_logits_topk(*args, _stream(stream)))
     return out
 
 

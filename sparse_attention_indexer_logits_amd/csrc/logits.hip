@@ -32,8 +32,9 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
-#include "xk_internal.h"
+#include "tile16.h"
 
 namespace xk {
 namespace {
@@ -41,112 +42,6 @@ namespace {
 __device__ __forceinline__ int clamp_limit(const int32_t* limit, int64_t bt, int K) {
   return limit ? min(limit[bt], K - 1) : K - 1;
 }
-
-// ---------------------------------------------------------------------------
-// prefill: 16x16 MFMA tiles. For one query the 64 heads are four 16-row
-// M-tiles and 16 keys the N dimension; a 16x16 fp32 accumulator gives lane l
-// rows 4*(l/16)+i (i < 4) of column l%16, i.e. 16 heads of one key per lane
-// across the four M-tiles. That keeps the per-query state small (16 head
-// weights + 16 accumulators per lane) so a wave can own QW queries and each
-// B fragment read from LDS feeds 4*QW MFMAs. After the four 16-key subtiles
-// of a 64-key tile, a 3-shuffle butterfly leaves lane l with the full score
-// of key l, so stores are 64 consecutive floats.
-template <bool FP8>
-struct Mma16;
-
-template <>
-struct Mma16<false> {  // bf16: v_mfma_f32_16x16x32_bf16, 4 steps over D = 128
-  using Frag = bf16x8;
-  static constexpr int kSteps = 4;
-  static constexpr int kElemBytes = 2;
-  __device__ static int dofs(int s, int g) { return 32 * s + 8 * g; }  // g = lane / 16
-  __device__ static Frag load(const uint8_t* p) { return *reinterpret_cast<const Frag*>(p); }
-  __device__ static f32x4 mma(Frag a, Frag b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <>
-struct Mma16<true> {  // OCP e4m3: v_mfma_scale_f32_16x16x128_f8f6f4, 1 step
-  using Frag = i32x8;
-  static constexpr int kSteps = 1;
-  static constexpr int kElemBytes = 1;
-  __device__ static int dofs(int, int g) { return 32 * g; }
-  __device__ static Frag load(const uint8_t* p) {
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 16);
-    return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-  __device__ static f32x4 mma(Frag a, Frag b, f32x4 c) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-  }
-};
-
-template <bool FP8>
-struct Query16 {
-  using M = Mma16<FP8>;
-  typename M::Frag a[4][M::kSteps];  // [M-tile][step]
-  float wr[4][4];                    // head 16*mt + 4*(lane/16) + i
-
-  __device__ void load(const uint8_t* qrow, const float* wrow, const float* sqrow, int lane) {
-    const int g = lane >> 4, r = lane & 15;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int s = 0; s < M::kSteps; ++s)
-        a[mt][s] = M::load(qrow + ((16 * mt + r) * kHeadDim + M::dofs(s, g)) * M::kElemBytes);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = 16 * mt + 4 * g + i;
-        wr[mt][i] = FP8 ? wrow[h] * sqrow[h] : wrow[h];
-      }
-  }
-  __device__ void zero() {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int s = 0; s < M::kSteps; ++s) a[mt][s] = typename M::Frag{};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wr[mt][i] = 0.f;
-    }
-  }
-  // this lane's 16-head partial score of key (lane % 16) of a 16-key subtile
-  __device__ float partial(const typename M::Frag (&b)[M::kSteps]) const {
-    f32x4 acc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < M::kSteps; ++s) acc[mt] = M::mma(a[mt][s], b[s], acc[mt]);
-    }
-    float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      p0 = fmaf(wr[mt][0], fmaxf(acc[mt][0], 0.f), p0);
-      p1 = fmaf(wr[mt][1], fmaxf(acc[mt][1], 0.f), p1);
-      p0 = fmaf(wr[mt][2], fmaxf(acc[mt][2], 0.f), p0);
-      p1 = fmaf(wr[mt][3], fmaxf(acc[mt][3], 0.f), p1);
-    }
-    return p0 + p1;
-  }
-};
-
-// p[st] = this lane's partial for key 16*st + lane%16; returns the full score
-// of key `lane` (sum over the four lane groups, routed by a butterfly).
-__device__ __forceinline__ float subtile_total(const float (&p)[4], int lane) {
-  const bool up32 = lane >= 32, up16 = (lane & 16) != 0;
-  // xor 32: lower half keeps subtiles 0,1; upper half keeps 2,3
-  const float k0 = up32 ? p[2] : p[0], k1 = up32 ? p[3] : p[1];
-  const float s0 = up32 ? p[0] : p[2], s1 = up32 ? p[1] : p[3];
-  const float a0 = k0 + __shfl_xor(s0, 32);
-  const float a1 = k1 + __shfl_xor(s1, 32);
-  // xor 16: even groups keep the first, odd groups the second
-  const float keep = up16 ? a1 : a0, send = up16 ? a0 : a1;
-  return keep + __shfl_xor(send, 16);
-}
-
 
 // ---------------------------------------------------------------------------
 // decode: 1-D grid over (B*T rows) x (key chunks); a workgroup owns one query
@@ -491,15 +386,44 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void logits_paged_kernel(
 // (key chunks). NW waves x QW queries per workgroup share double-buffered
 // 64-key LDS tiles; the next tile's global loads are issued before this
 // tile's MFMAs and stored to LDS after them, one barrier per tile.
+//
+// With NL > 0 the kernel writes no logits: it is the first half of the
+// fused logits -> top-k path, one query per wave. Each lane keeps the NL
+// largest scores it has seen in a sorted register list (one med3 per entry
+// and key). The wave's 64 lists hold 64*NL >= k distinct scores of the
+// row, so their minimum, the bound tau, is at most the row's k-th largest
+// score. Keys scoring >= tau are appended to the (row, chunk) candidate
+// region as (order key, j): every key of the row's top-k scores >= the
+// k-th largest >= tau, so the candidates hold the whole top-k, ties
+// included. The count written at the end may exceed the region's capacity
+// (entries past it are dropped); the selection kernel then has the row
+// recomputed.
 constexpr int kPrefillTile = 64;
 
-template <bool FP8, int QW, int NW>
+// minimum over the wave, uniform result (DPP butterflies in each row of 16
+// lanes, then the four rows read as scalars)
+__device__ __forceinline__ float wave_min(float v) {
+#define XK_MIN_DPP(C) \
+  v = fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), C, 0xF, 0xF, false)));
+  XK_MIN_DPP(0xB1)   // quad_perm [1,0,3,2]
+  XK_MIN_DPP(0x4E)   // quad_perm [2,3,0,1]
+  XK_MIN_DPP(0x141)  // row_half_mirror
+  XK_MIN_DPP(0x140)  // row_mirror
+#undef XK_MIN_DPP
+  const auto lane_v = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+  return fminf(fminf(lane_v(0), lane_v(16)), fminf(lane_v(32), lane_v(48)));
+}
+
+template <bool FP8, int QW, int NW, int NL>
 __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ k, const float* __restrict__ k_scale,
     const float* __restrict__ w, const int32_t* __restrict__ limit,
-    float* __restrict__ out, int B, int T, int K, int keys_per_wg, int n_chunks, int n_qblocks) {
+    float* __restrict__ out, CandidateOut co, int B, int T, int K, int keys_per_wg, int n_chunks,
+    int n_qblocks) {
   using M = Mma16<FP8>;
+  constexpr bool kCand = NL > 0;
+  static_assert(!kCand || QW == 1, "the candidate epilogue keeps one query per wave");
   constexpr int QB = QW * NW;  // queries per workgroup
   constexpr int kRowBytes = kHeadDim * M::kElemBytes;
   constexpr int kPitch = kRowBytes + 16;  // 16-byte pad: conflict-free fragment reads
@@ -537,12 +461,16 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
     bt[qi] = b * T + (qvalid[qi] ? t : 0);
     const int lim = qvalid[qi] ? clamp_limit(limit, bt[qi], K) : -1;
     q_end[qi] = min(j_end, lim + 1);
-    if (qvalid[qi]) {
+    if (!kCand && qvalid[qi]) {
       float* orow = out + bt[qi] * K;
       for (int j = max(j_begin, lim + 1) + lane; j < j_end; j += 64) orow[j] = -INFINITY;
     }
   }
-  if (c_end <= j_begin) return;  // uniform over the workgroup
+  if (kCand && blockIdx.x == 0 && threadIdx.x < 2) co.ctrl[threadIdx.x] = 0;  // queue counters
+  if (c_end <= j_begin) {  // uniform over the workgroup
+    if (kCand && qvalid[0] && lane == 0) co.count[bt[0] * n_chunks + chunk] = 0;
+    return;
+  }
 
   const uint8_t* kseq = k + b * int64_t(K) * kRowBytes;
   const float* skseq = FP8 ? k_scale + b * int64_t(K) : nullptr;
@@ -569,10 +497,21 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
       *reinterpret_cast<u32x4*>(dst + (c / kChunks) * kPitch + (c % kChunks) * 16) = src[i];
     }
   };
-  __amdgpu_buffer_rsrc_t ors[QW];  // this chunk's outputs of each query, up to its limit
+  // logits: this chunk's outputs of each query, up to its limit; candidates:
+  // the (row, chunk) region
+  __amdgpu_buffer_rsrc_t ors[QW];
 #pragma unroll
-  for (int qi = 0; qi < QW; ++qi)
-    ors[qi] = make_rsrc(out + bt[qi] * K + j_begin, max(0, q_end[qi] - j_begin) * 4);
+  for (int qi = 0; qi < QW; ++qi) {
+    if constexpr (kCand)
+      ors[qi] = make_rsrc(co.cand + (bt[qi] * n_chunks + chunk) * int64_t(co.capc), co.capc * 8);
+    else
+      ors[qi] = make_rsrc(out + bt[qi] * K + j_begin, max(0, q_end[qi] - j_begin) * 4);
+  }
+  float best[kCand ? NL : 1];  // descending; -inf until the lane has seen NL keys
+#pragma unroll
+  for (int i = 0; i < (kCand ? NL : 1); ++i) best[i] = -INFINITY;
+  float tau = -INFINITY;  // the row bound (uniform)
+  int cnt = 0;            // candidates this wave has emitted (uniform)
 
   // q fragments and head weights are loaded before the key tiles: memory
   // waits count in issue order, so waiting for them (at their first use,
@@ -594,7 +533,8 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
   // tile at j0 in tile[cur]; `fill` (free) starts loading the tile two
   // ahead, `hold` (the next tile, issued a step earlier) goes to LDS at the
   // end. The same memory operations run every step: refills past the chunk
-  // read the last key again and stores past a query's limit are dropped.
+  // read the last key again and stores past a query's limit (or, for
+  // candidates, of keys that do not qualify) are dropped.
   auto step = [&](int j0, int cur, u32x4 (&fill)[kPer], float& sk_fill, const u32x4 (&hold)[kPer]) {
     const float sk = sk_fill;  // this tile's key scales, loaded with it
     gload(j0 + 2 * kPrefillTile, fill, sk_fill);
@@ -611,8 +551,24 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
 #pragma unroll
     for (int qi = 0; qi < QW; ++qi) {
       const float tot = subtile_total(p[qi], lane);
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, FP8 ? tot * sk : tot),
-                                            ors[qi], (j0 - j_begin + lane) * 4, 0, 0);
+      const float sc = FP8 ? tot * sk : tot;
+      if constexpr (kCand) {
+        const int j = j0 + lane;
+        const bool valid = j < q_end[qi];
+        const float sv = valid ? sc : -INFINITY;
+#pragma unroll
+        for (int i = NL - 1; i > 0; --i) best[i] = __builtin_amdgcn_fmed3f(best[i], best[i - 1], sv);
+        best[0] = fmaxf(best[0], sv);
+        const bool pass = valid && sc >= tau;
+        const uint64_t m = __ballot(pass);
+        const int rank = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{order_key(sc), uint32_t(j)}, ors[qi],
+                                              pass ? (cnt + rank) * 8 : co.capc * 8, 0, 0);
+        cnt += __popcll(m);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors[qi],
+                                              (j0 - j_begin + lane) * 4, 0, 0);
+      }
     }
     lds_put(tile[cur ^ 1], hold);
     __syncthreads();
@@ -620,11 +576,15 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
   // Both steps of an iteration always run (an odd last tile is followed by
   // one redundant tile whose stores are all dropped): with no loop exit
   // between a refill and its use, the compiler cannot sink the refill next
-  // to that use, which would expose its latency.
-  for (int j0 = j_begin; j0 < c_end; j0 += 2 * kPrefillTile) {
+  // to that use, which would expose its latency. Candidates: every fourth
+  // iteration the wave raises tau to its lists' minimum.
+  int it = 0;
+  for (int j0 = j_begin; j0 < c_end; j0 += 2 * kPrefillTile, ++it) {
+    if (kCand && (it & 3) == 3) tau = fmaxf(tau, wave_min(best[kCand ? NL - 1 : 0]));
     step(j0, 0, pre[0], skp[0], pre[1]);
     step(j0 + kPrefillTile, 1, pre[1], skp[1], pre[0]);
   }
+  if (kCand && qvalid[0] && lane == 0) co.count[bt[0] * n_chunks + chunk] = cnt;
 }
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -695,12 +655,45 @@ hipError_t launch_logits(const void* q, const float* q_scale, const void* k,
     const int nch = (K + kpw - 1) / kpw;
     const dim3 grid(unsigned(int64_t(nch) * qblocks));
     if (fp8)
-      hipLaunchKernelGGL((logits_prefill_kernel<true, 1, 8>), grid, dim3(8 * 64), 0, stream, q8,
-                         q_scale, k8, k_scale, w, limit, logits, B, T, K, kpw, nch, nqb);
+      hipLaunchKernelGGL((logits_prefill_kernel<true, 1, 8, 0>), grid, dim3(8 * 64), 0, stream, q8,
+                         q_scale, k8, k_scale, w, limit, logits, CandidateOut{}, B, T, K, kpw, nch, nqb);
     else
-      hipLaunchKernelGGL((logits_prefill_kernel<false, 1, 4>), grid, dim3(4 * 64), 0, stream, q8,
-                         q_scale, k8, k_scale, w, limit, logits, B, T, K, kpw, nch, nqb);
+      hipLaunchKernelGGL((logits_prefill_kernel<false, 1, 4, 0>), grid, dim3(4 * 64), 0, stream, q8,
+                         q_scale, k8, k_scale, w, limit, logits, CandidateOut{}, B, T, K, kpw, nch, nqb);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_logits_candidates(const void* q, const float* q_scale, const void* k,
+                                    const float* k_scale, const float* w, const int32_t* limit,
+                                    const FusedPlan& p, const CandidateOut& co, int B, int T, int K,
+                                    bool fp8, hipStream_t stream) {
+  const auto* q8 = static_cast<const uint8_t*>(q);
+  const auto* k8 = static_cast<const uint8_t*>(k);
+  const dim3 grid(unsigned(int64_t(p.nch) * p.nqb * B));
+  auto go = [&](auto fp8_tag, auto nl_tag) {
+    constexpr bool F = decltype(fp8_tag)::value;
+    constexpr int NL = decltype(nl_tag)::value;
+    constexpr int NW = F ? 8 : 4;
+    hipLaunchKernelGGL((logits_prefill_kernel<F, 1, NW, NL>), grid, dim3(NW * 64), 0, stream, q8, q_scale,
+                       k8, k_scale, w, limit, nullptr, co, B, T, K, p.kpw, p.nch, p.nqb);
+  };
+  using T4 = std::integral_constant<int, 4>;
+  using T8 = std::integral_constant<int, 8>;
+  using T16 = std::integral_constant<int, 16>;
+  using T32 = std::integral_constant<int, 32>;
+  auto by_nl = [&](auto fp8_tag) {
+    switch (p.nl) {
+      case 4: go(fp8_tag, T4{}); break;
+      case 8: go(fp8_tag, T8{}); break;
+      case 16: go(fp8_tag, T16{}); break;
+      default: go(fp8_tag, T32{}); break;
+    }
+  };
+  if (fp8)
+    by_nl(std::true_type{});
+  else
+    by_nl(std::false_type{});
   return hipGetLastError();
 }
 

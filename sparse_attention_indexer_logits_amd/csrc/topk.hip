@@ -45,18 +45,12 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "xk_internal.h"
+#include "tile16.h"
 
 namespace xk {
 namespace {
 
 constexpr int kBins = 2048;  // 11-bit digits
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;  // -0.0 ties with +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 __device__ __forceinline__ int lane_id() { return int(threadIdx.x & 63); }
 
@@ -404,11 +398,6 @@ __device__ __forceinline__ void select_row(TopkShared<BLOCK, CAP>& sh, int n, in
 // ---------------------------------------------------------------------------
 // Bucket path: one histogram both finds the threshold and orders the winners.
 
-// Score of an order key (inverse of order_key).
-__device__ __forceinline__ float key_value(uint32_t key) {
-  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
-}
-
 // Keys of finite scores (-inf maps to 0x007FFFFF, +inf to 0xFF800000).
 __device__ __forceinline__ bool finite_key(uint32_t key) {
   return key > 0x007FFFFFu && key < 0xFF800000u;
@@ -750,20 +739,14 @@ __device__ __forceinline__ void append_list(TopkShared<BLOCK, CAP>& sh, KeyAt ke
 // >= b* and the keys >= tau of the rest of the row (streamed once) form an
 // LDS candidate list, from which the winners are selected exactly. If the list runs out of room (scores
 // crowded into b*), the row falls back to multi-pass streaming selection.
-template <int BLOCK, int V, int CAP, int NBUF = 2>
-__global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restrict__ logits,
-                                                          const int32_t* __restrict__ limit,
-                                                          int32_t* __restrict__ idx, int K, int k) {
+template <int BLOCK, int V, int CAP, int NBUF>
+__device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const float* __restrict__ x, int n,
+                                              int k, int32_t* __restrict__ orow) {
   constexpr int U = 16;           // streamed entries per thread per chunk
   constexpr int L = CAP / BLOCK;  // list entries per thread
   static_assert(CAP % BLOCK == 0, "list spread evenly over the block");
-  __shared__ TopkShared<BLOCK, CAP> sh;
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const int n = limit ? max(0, min(limit[row], K - 1) + 1) : K;
   const int prefix = min(n, BLOCK * V);
-  const float* x = logits + row * K;
-  int32_t* orow = idx + row * k;
   const auto rs = row_rsrc(x, n);
   float raw[V];
   load_chunk<BLOCK, V>(rs, 0, raw);
@@ -827,6 +810,135 @@ __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restric
   radix_topk<BLOCK, CAP>(sh, x, n, k, orow);
 }
 
+template <int BLOCK, int V, int CAP, int NBUF = 2>
+__global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restrict__ logits,
+                                                          const int32_t* __restrict__ limit,
+                                                          int32_t* __restrict__ idx, int K, int k) {
+  __shared__ TopkShared<BLOCK, CAP> sh;
+  const int64_t row = blockIdx.x;
+  const int n = limit ? max(0, min(limit[row], K - 1) + 1) : K;
+  long_row_topk<BLOCK, V, CAP, NBUF>(sh, logits + row * K, n, k, idx + row * k);
+}
+
+// ---------------------------------------------------------------------------
+// Fused logits -> top-k, second half. The candidate pass (the prefill
+// logits kernel with its candidate epilogue) leaves, per row, nch regions
+// of capc (order key, j) entries that hold every key of the row's top-k.
+// One workgroup per row selects the top-k of those entries exactly (the
+// bucket path). A row whose regions overflowed, or whose candidates crowd
+// the bucket path's threshold bin, is queued for the recompute kernel.
+
+constexpr int kSelBlock = 1024;
+
+template <int L>  // region slots per thread: nch * capc <= kSelBlock * L
+__global__ __launch_bounds__(kSelBlock) void fused_select_kernel(const uint2* __restrict__ cand,
+                                                                 const int* __restrict__ count, int nch,
+                                                                 int capc, int k, int32_t* __restrict__ idx,
+                                                                 int* __restrict__ ctrl, int* __restrict__ over) {
+  __shared__ TopkShared<kSelBlock, 64> sh;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int* crow = count + row * nch;
+  const int slots = nch * capc;
+  const auto rs = make_rsrc(cand + row * slots, slots * 8);
+  u32x2 e[L];  // slots past a region's count read (0, 0) without a memory access
+#pragma unroll
+  for (int u = 0; u < L; ++u) {
+    const int s = tid + kSelBlock * u;
+    const int c = s / capc;
+    const bool valid = c < nch && s - c * capc < crow[min(c, nch - 1)];
+    e[u] = __builtin_amdgcn_raw_buffer_load_b64(rs, valid ? s * 8 : slots * 8, 0, 0);
+  }
+  const bool spill = __syncthreads_or(tid < nch && crow[tid] > capc);
+  int32_t* orow = idx + row * k;
+  if (!spill && bucket_topk<kSelBlock, 64, L>(
+                    sh, [&](int u) { return e[u][0]; }, [&](int u) { return e[u][1]; }, k, orow))
+    return;
+  if (tid == 0) over[atomicAdd(&ctrl[0], 1)] = int(row);
+}
+
+// Rows the selection could not finish: a work queue over the listed rows
+// (ctrl[0] rows, claimed through ctrl[1]) for a fixed grid of workgroups,
+// each with a scratch row of K scores. The row's scores are recomputed with
+// the logits kernels' tile arithmetic (Query16 and subtile_total on the
+// same fragments, so the same bits), then the long-row selection runs on
+// them. Every workgroup leaves once the queue is drained.
+constexpr int kRecBlock = 1024;
+
+// Scores of row `row` (n valid keys) into x, 64-key tiles spread over the
+// block's waves. Kept out of line: its fragments and the selection's
+// registers are then allocated separately instead of competing.
+template <bool FP8>
+__device__ __attribute__((noinline)) void score_row(const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
+                                                    const uint8_t* __restrict__ kmat, const float* __restrict__ k_scale,
+                                                    const float* __restrict__ w, int64_t row, int64_t b, int K, int n,
+                                                    float* __restrict__ x) {
+  using M = Mma16<FP8>;
+  using Frag = typename M::Frag;
+  constexpr int kRowBytes = kHeadDim * M::kElemBytes;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, r = lane & 15;
+  Query16<FP8> qr;
+  qr.load(q + row * (kHeads * kRowBytes), w + row * kHeads, FP8 ? q_scale + row * kHeads : nullptr, lane);
+  const auto krs = make_rsrc(kmat + b * int64_t(K) * kRowBytes, n * kRowBytes);
+  const auto srs = make_rsrc(FP8 ? k_scale + b * int64_t(K) : nullptr, FP8 ? n * 4 : 0);
+  const auto xrs = make_rsrc(x, n * 4);
+  for (int j0 = 64 * wave; j0 < n; j0 += 64 * int(blockDim.x / 64)) {
+    float p[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      Frag bf[M::kSteps];
+      const int base = (j0 + 16 * st + r) * kRowBytes;
+#pragma unroll
+      for (int s = 0; s < M::kSteps; ++s) {
+        const int off = base + M::dofs(s, g) * M::kElemBytes;
+        if constexpr (FP8) {
+          const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+          const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 16, 0, 0);
+          bf[s] = Frag{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]),
+                       int(hi[3])};
+        } else {
+          bf[s] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+        }
+      }
+      p[st] = qr.partial(bf);
+    }
+    const float tot = subtile_total(p, lane);
+    const float sk =
+        FP8 ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, (j0 + lane) * 4, 0, 0)) : 1.f;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, FP8 ? tot * sk : tot), xrs, (j0 + lane) * 4,
+                                          0, 0);
+  }
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(kRecBlock) void fused_recompute_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const uint8_t* __restrict__ kmat,
+    const float* __restrict__ k_scale, const float* __restrict__ w, const int32_t* __restrict__ limit, int T,
+    int K, int ktop, int32_t* __restrict__ idx, int* __restrict__ ctrl, const int* __restrict__ over,
+    float* __restrict__ scratch) {
+  __shared__ TopkShared<kRecBlock, 8192> sh;
+  __shared__ int claimed;
+  float* x = scratch + int64_t(blockIdx.x) * K;
+  for (;;) {
+    if (threadIdx.x == 0) claimed = atomicAdd(&ctrl[1], 1);
+    __syncthreads();
+    const int i = claimed;
+    const int queued = ctrl[0];
+    __syncthreads();
+    if (i >= queued) break;  // uniform
+    const int64_t row = over[i];
+    const int n = limit ? max(0, min(limit[row], K - 1) + 1) : K;
+    score_row<FP8>(q, q_scale, kmat, k_scale, w, row, row / T, K, n, x);
+    // the row's scores, written by every wave, are read back by every wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    long_row_topk<kRecBlock, 8, 8192, 2>(sh, x, n, ktop, idx + row * ktop);
+    __syncthreads();  // the scratch row and LDS are reused by the next claim
+  }
+}
+
 template <int BLOCK, int V, int CAP>
 hipError_t launch_one(const float* logits, const int32_t* limit, int32_t* idx, int R, int K, int k,
                       hipStream_t stream) {
@@ -845,6 +957,34 @@ hipError_t launch_topk(const float* logits, const int32_t* limit, int32_t* idx, 
   if (K <= 1024 * 16) return launch_one<1024, 16, 1024>(logits, limit, idx, R, K, k, stream);
   hipLaunchKernelGGL((topk_long_kernel<1024, 16, 8192>), dim3(unsigned(R)), dim3(1024), 0, stream,
                      logits, limit, idx, K, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_select(const FusedPlan& p, const CandidateOut& co, int R, int k, int32_t* idx,
+                               int* ctrl, int* over, hipStream_t stream) {
+  const int slots = p.nch * p.capc;
+  if (slots <= kSelBlock * 4)
+    hipLaunchKernelGGL(fused_select_kernel<4>, dim3(unsigned(R)), dim3(kSelBlock), 0, stream, co.cand, co.count,
+                       p.nch, p.capc, k, idx, ctrl, over);
+  else
+    hipLaunchKernelGGL(fused_select_kernel<16>, dim3(unsigned(R)), dim3(kSelBlock), 0, stream, co.cand, co.count,
+                       p.nch, p.capc, k, idx, ctrl, over);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_recompute(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                                  const float* w, const int32_t* limit, const FusedPlan& p, int T, int K,
+                                  int ktop, bool fp8, int32_t* idx, int* ctrl, const int* over, float* scratch,
+                                  hipStream_t stream) {
+  const auto* q8 = static_cast<const uint8_t*>(q);
+  const auto* k8 = static_cast<const uint8_t*>(k);
+  const dim3 grid(unsigned(p.fallback_blocks));
+  if (fp8)
+    hipLaunchKernelGGL(fused_recompute_kernel<true>, grid, dim3(kRecBlock), 0, stream, q8, q_scale, k8, k_scale,
+                       w, limit, T, K, ktop, idx, ctrl, over, scratch);
+  else
+    hipLaunchKernelGGL(fused_recompute_kernel<false>, grid, dim3(kRecBlock), 0, stream, q8, q_scale, k8, k_scale,
+                       w, limit, T, K, ktop, idx, ctrl, over, scratch);
   return hipGetLastError();
 }
 

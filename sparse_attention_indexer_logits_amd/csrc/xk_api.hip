@@ -53,6 +53,23 @@ xk_status launched(hipError_t e, const char* what) {
   return ok();
 }
 
+// Checks shared by xk_indexer_logits and xk_indexer_logits_topk.
+xk_status check_logits_args(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                            const float* w, const void* out, int B, int T, int K, int H, int D, int dtype) {
+  if (!q || !k || !w || !out) return fail(XK_ERR_INVALID_ARGUMENT, "null q, k, w or output");
+  if (B < 1 || T < 1 || K < 1 || H < 1 || D < 1)
+    return fail(XK_ERR_INVALID_ARGUMENT, "B, T, K, H, D must be >= 1");
+  if (dtype != XK_BF16 && dtype != XK_FP8_E4M3_OCP) return fail(XK_ERR_INVALID_ARGUMENT, "unknown dtype");
+  const bool fp8 = dtype == XK_FP8_E4M3_OCP;
+  if (fp8 && (!q_scale || !k_scale)) return fail(XK_ERR_INVALID_ARGUMENT, "fp8 needs q_scale and k_scale");
+  if (!fp8 && (q_scale || k_scale)) return fail(XK_ERR_INVALID_ARGUMENT, "bf16 takes no scales");
+  if (H != xk::kHeads || D != xk::kHeadDim)
+    return fail(XK_ERR_UNSUPPORTED, "only H=64, D=128 (DeepSeek-V4 indexer) is implemented");
+  if (!aligned(q, 16) || !aligned(k, 16)) return fail(XK_ERR_INVALID_ARGUMENT, "q and k must be 16-byte aligned");
+  if (int64_t(B) * T > (int64_t(1) << 30)) return fail(XK_ERR_UNSUPPORTED, "B*T above 2^30");
+  return XK_OK;
+}
+
 }  // namespace
 
 XK_EXPORT const char* xk_status_string(xk_status s) {
@@ -71,23 +88,10 @@ XK_EXPORT xk_status xk_indexer_logits(const void* q, const float* q_scale, const
                                       const float* k_scale, const float* w, const int32_t* limit,
                                       float* logits, int B, int T, int K, int H, int D, int dtype,
                                       void* stream) {
-  if (!q || !k || !w || !logits) return fail(XK_ERR_INVALID_ARGUMENT, "null q, k, w or logits");
-  if (B < 1 || T < 1 || K < 1 || H < 1 || D < 1)
-    return fail(XK_ERR_INVALID_ARGUMENT, "B, T, K, H, D must be >= 1");
-  if (dtype != XK_BF16 && dtype != XK_FP8_E4M3_OCP)
-    return fail(XK_ERR_INVALID_ARGUMENT, "unknown dtype");
+  xk_status s = check_logits_args(q, q_scale, k, k_scale, w, logits, B, T, K, H, D, dtype);
+  if (s != XK_OK) return s;
   const bool fp8 = dtype == XK_FP8_E4M3_OCP;
-  if (fp8 && (!q_scale || !k_scale))
-    return fail(XK_ERR_INVALID_ARGUMENT, "fp8 needs q_scale and k_scale");
-  if (!fp8 && (q_scale || k_scale))
-    return fail(XK_ERR_INVALID_ARGUMENT, "bf16 takes no scales");
-  if (H != xk::kHeads || D != xk::kHeadDim)
-    return fail(XK_ERR_UNSUPPORTED, "only H=64, D=128 (DeepSeek-V4 indexer) is implemented");
-  if (!aligned(q, 16) || !aligned(k, 16))
-    return fail(XK_ERR_INVALID_ARGUMENT, "q and k must be 16-byte aligned");
-  if (int64_t(B) * T > (int64_t(1) << 30))
-    return fail(XK_ERR_UNSUPPORTED, "B*T above 2^30");
-  xk_status s = check_device();
+  s = check_device();
   if (s != XK_OK) return s;
   return launched(xk::launch_logits(q, q_scale, k, k_scale, w, limit, logits, B, T, K, fp8,
                                     static_cast<hipStream_t>(stream)),
@@ -182,6 +186,32 @@ XK_EXPORT xk_status xk_indexer_topk(const float* logits, const int32_t* limit, i
   if (s != XK_OK) return s;
   return launched(xk::launch_topk(logits, limit, idx, R, K, k, static_cast<hipStream_t>(stream)),
                   "xk_indexer_topk launch");
+}
+
+XK_EXPORT size_t xk_indexer_logits_topk_workspace_size(int B, int T, int K, int k, int dtype) {
+  if (B < 1 || T < 1 || K < 1 || k < 1 || k > xk::kMaxTopk) return 0;
+  if (dtype != XK_BF16 && dtype != XK_FP8_E4M3_OCP) return 0;
+  if (int64_t(B) * T > (int64_t(1) << 30)) return 0;
+  return xk::plan_fused(B, T, K, k, dtype == XK_FP8_E4M3_OCP).bytes;
+}
+
+XK_EXPORT xk_status xk_indexer_logits_topk(const void* q, const float* q_scale, const void* k,
+                                           const float* k_scale, const float* w, const int32_t* limit,
+                                           int32_t* idx, int B, int T, int K, int H, int D, int topk, int dtype,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  xk_status s = check_logits_args(q, q_scale, k, k_scale, w, idx, B, T, K, H, D, dtype);
+  if (s != XK_OK) return s;
+  if (topk < 1) return fail(XK_ERR_INVALID_ARGUMENT, "topk must be >= 1");
+  if (topk > xk::kMaxTopk) return fail(XK_ERR_UNSUPPORTED, "topk above 2048");
+  if (int64_t(B) * T * topk > (int64_t(1) << 31) - 1) return fail(XK_ERR_UNSUPPORTED, "B*T*topk above 2^31-1");
+  const size_t need = xk_indexer_logits_topk_workspace_size(B, T, K, topk, dtype);
+  if (!workspace || workspace_bytes < need) return fail(XK_ERR_INVALID_ARGUMENT, "workspace too small");
+  if (!aligned(workspace, 256)) return fail(XK_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  s = check_device();
+  if (s != XK_OK) return s;
+  return launched(xk::launch_logits_topk(q, q_scale, k, k_scale, w, limit, idx, B, T, K, topk,
+                                         dtype == XK_FP8_E4M3_OCP, workspace, static_cast<hipStream_t>(stream)),
+                  "xk_indexer_logits_topk launch");
 }
 
 XK_EXPORT xk_status xk_mxfp4_paged_gather(const uint8_t* kv_fp4, const uint8_t* kv_scale,

@@ -9,7 +9,8 @@ from __future__ import annotations
 
 import torch
 
-from . import _check, _lib, _stream, gather_args, logits_args, logits_paged_args, topk_args
+from . import (_check, _lib, _stream, gather_args, logits_args, logits_paged_args, logits_topk_args,
+               topk_args)
 
 
 class IndexerStep:
@@ -54,6 +55,28 @@ class IndexerStep:
     def run_gather(self, stream=None):
         _check(_lib.xk_mxfp4_paged_gather(*self._gather_args, _stream(stream)))
         return self.gathered
+
+    def enable_fused(self, workspace=None):
+        """Prepare run_logits_topk (dense keys only): the same top-k written to
+        self.idx by xk_indexer_logits_topk, which for prefill shapes does not
+        write the score matrix. Steps run in order on one stream may share a
+        workspace; returns the one this step uses."""
+        if self.paged:
+            raise ValueError("the fused call reads dense keys")
+        self._fused_args, _, self.fused_workspace = logits_topk_args(
+            self.q, self.k, self.w, self.topk, self.limit, self.q_scale, self.k_scale, out=self.idx,
+            workspace=workspace)
+        return self.fused_workspace
+
+    def run_logits_topk(self, stream=None):
+        _check(_lib.xk_indexer_logits_topk(*self._fused_args, _stream(stream)))
+        return self.idx
+
+    def run_fused(self, stream=None):
+        """Top-k straight from q and k, then the gather (self.logits untouched)."""
+        self.run_logits_topk(stream)
+        self.run_gather(stream)
+        return self.idx, self.gathered
 
     def __call__(self, stream=None):
         self.run_logits(stream)

@@ -28,6 +28,7 @@ def lib():
 def test_header_declares_the_three_operations():
     names = declared_functions()
     for n in ("xk_indexer_logits", "xk_indexer_logits_paged", "xk_indexer_topk",
+              "xk_indexer_logits_topk", "xk_indexer_logits_topk_workspace_size",
               "xk_mxfp4_paged_gather", "xk_indexer_topk_workspace_size", "xk_quant_fp8_rows",
               "xk_mxfp4_cache_write", "xk_status_string", "xk_last_error"):
         assert n in names
@@ -102,6 +103,40 @@ def test_topk_validation(lib, args, status, needle):
 
 def test_topk_workspace_is_host_only(lib):
     assert lib.xk_indexer_topk_workspace_size(4096, 4096, 512) == 0
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    # (q, q_scale, k, k_scale, w, limit, idx, B, T, K, H, D, topk, dtype, workspace, ws_bytes)
+    ((None, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 64, 128, 4, 0, FAKE, 1 << 20), 1, "null"),
+    ((FAKE, None, FAKE, None, FAKE, None, None, 1, 1, 8, 64, 128, 4, 0, FAKE, 1 << 20), 1, "null"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 0, 8, 64, 128, 4, 0, FAKE, 1 << 20), 1, ">= 1"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 64, 128, 4, 1, FAKE, 1 << 20), 1, "scale"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 64, 64, 4, 0, FAKE, 1 << 20), 2, "H=64"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 64, 128, 0, 0, FAKE, 1 << 20), 1, "topk"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 64, 128, 4096, 0, FAKE, 1 << 20), 2, "2048"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 64, 128, 4, 0, None, 1 << 20), 1, "workspace"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 64, 128, 4, 0, FAKE, 16), 1, "workspace"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 64, 128, 4, 0, FAKE + 64, 1 << 20), 1, "256-byte"),
+])
+def test_logits_topk_validation(lib, args, status, needle):
+    assert lib.xk_indexer_logits_topk(*args, None) == status
+    assert needle in lib.xk_last_error().decode()
+
+
+def test_logits_topk_workspace_sizes(lib):
+    ws = lib.xk_indexer_logits_topk_workspace_size
+    # rejected sizes report 0
+    assert ws(1, 1, 8, 0, 0) == 0 and ws(1, 1, 8, 4096, 0) == 0 and ws(1, 1, 8, 4, 9) == 0
+    assert ws(0, 1, 8, 4, 0) == 0
+    # few queries: the score matrix itself (B*T*K fp32, 256-byte aligned)
+    assert ws(32, 1, 8192, 512, 0) == 32 * 8192 * 4
+    assert ws(1, 8, 100, 16, 0) == 3328
+    # the long fp8 prefill shape: candidate regions (8 bytes x 16384 slots per
+    # query) and 64 scratch rows, well under its 768 MiB score matrix
+    big = ws(1, 2048, 98304, 1024, 1)
+    assert 2048 * 16384 * 8 < big < 2048 * 98304 * 4 // 2
+    # more keys per row leave the per-query room unchanged
+    assert ws(1, 2048, 196608, 1024, 1) - big == 64 * 98304 * 4
 
 
 @pytest.mark.parametrize("args,status,needle", [
