@@ -467,16 +467,19 @@ __device__ __forceinline__ void scan_desc(TopkShared<BLOCK, CAP>& sh, int k) {
 }
 
 // Range, histogram and scan over U entries per thread (key_at(u), key 0 =
-// no entry). Returns the bin map; afterwards hist holds the bins'
-// descending starts and sh.digit / sh.at the threshold bin and the number
-// of entries at or above it.
+// no entry; entries u >= nu, a uniform count, are all empty and skipped).
+// Returns the bin map and each entry's bin in bin[u] (-1 for none);
+// afterwards hist holds the bins' descending starts and sh.digit / sh.at
+// the threshold bin and the number of entries at or above it.
 template <int BLOCK, int CAP, int U, typename KeyAt>
-__device__ __forceinline__ ValueBins bucket_threshold(TopkShared<BLOCK, CAP>& sh, KeyAt key_at, int k) {
+__device__ __forceinline__ ValueBins bucket_threshold(TopkShared<BLOCK, CAP>& sh, KeyAt key_at, int k, int nu,
+                                                      int (&bin)[U]) {
   constexpr int NW = BLOCK / 64;
   const int lane = lane_id(), wave = int(threadIdx.x) >> 6;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
+    if (u >= nu) break;
     const uint32_t kv = key_at(u);
     if (finite_key(kv)) {
       mn = min(mn, kv);
@@ -505,8 +508,13 @@ __device__ __forceinline__ ValueBins bucket_threshold(TopkShared<BLOCK, CAP>& sh
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
+    bin[u] = -1;
+    if (u >= nu) continue;
     const uint32_t kv = key_at(u);
-    if (kv != 0u) atomicAdd(&sh.hist[bins(kv)], 1u);
+    if (kv != 0u) {
+      bin[u] = bins(kv);
+      atomicAdd(&sh.hist[bin[u]], 1u);
+    }
   }
   __syncthreads();
   if (threadIdx.x < 64) scan_desc(sh, k);
@@ -526,19 +534,17 @@ __device__ __forceinline__ ValueBins bucket_threshold(TopkShared<BLOCK, CAP>& sh
 // (scores crowded into a few bins: heavy ties, far outliers).
 template <int BLOCK, int CAP, int U, typename KeyAt, typename JAt>
 __device__ __forceinline__ bool bucket_topk(TopkShared<BLOCK, CAP>& sh, KeyAt key_at, JAt j_at,
-                                            int k, int32_t* __restrict__ orow) {
+                                            int k, int32_t* __restrict__ orow, int nu = U) {
   const int tid = threadIdx.x;
-  const ValueBins bins = bucket_threshold<BLOCK, CAP, U>(sh, key_at, k);
+  int bin[U];
+  const ValueBins bins = bucket_threshold<BLOCK, CAP, U>(sh, key_at, k, nu, bin);
   const int bstar = sh.digit, m = sh.at;
   if (m > kMaxTopk) return false;  // uniform
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint32_t kv = key_at(u);
-    if (kv == 0u) continue;
-    const int b = bins(kv);
-    if (b >= bstar) {
-      const uint32_t pos = atomicAdd(&sh.hist[b], 1u);
-      sh.sel[pos] = (uint64_t(kv) << 32) | uint64_t(~j_at(u));
+    if (bin[u] >= bstar) {
+      const uint32_t pos = atomicAdd(&sh.hist[bin[u]], 1u);
+      sh.sel[pos] = (uint64_t(key_at(u)) << 32) | uint64_t(~j_at(u));
     }
   }
   __syncthreads();
@@ -681,14 +687,16 @@ __device__ __forceinline__ void radix_topk(TopkShared<BLOCK, CAP>& sh, const flo
 }
 
 // Rows of at most BLOCK*V keys: the row is read once into V registers per
-// thread (j = tid + BLOCK*v).
+// thread (j = tid + BLOCK*v). Rows run last to first: under a causal limit
+// the longest rows are the last ones, and starting them first leaves the
+// short rows to fill the end of the grid.
 template <int BLOCK, int V, int CAP>
 __global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ logits,
                                                      const int32_t* __restrict__ limit,
                                                      int32_t* __restrict__ idx, int K, int k) {
   __shared__ TopkShared<BLOCK, CAP> sh;
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
+  const int64_t row = int64_t(gridDim.x) - 1 - blockIdx.x;
   const float* x = logits + row * K;
   float raw[V];  // issued before the limit arrives; keys past it are masked below
   load_chunk<BLOCK, V>(row_rsrc(x, K), 0, raw);
@@ -698,7 +706,8 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ l
   for (int v = 0; v < V; ++v) key[v] = tid + BLOCK * v < n ? order_key(raw[v]) : 0u;
   auto key_at = [&](int v) { return key[v]; };
   auto j_at = [&](int v) { return uint32_t(tid + BLOCK * v); };
-  if (bucket_topk<BLOCK, CAP, V>(sh, key_at, j_at, k, idx + row * k)) return;
+  // register chunks wholly past the row's end are skipped (causal rows)
+  if (bucket_topk<BLOCK, CAP, V>(sh, key_at, j_at, k, idx + row * k, (n + BLOCK - 1) / BLOCK)) return;
   radix_topk<BLOCK, CAP>(sh, x, n, k, idx + row * k);
 }
 
@@ -759,7 +768,8 @@ __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const 
   auto key_at = [&](int v) { return key[v]; };
   auto j_at = [&](int v) { return uint32_t(tid + BLOCK * v); };
   if (n <= prefix) {
-    if (!bucket_topk<BLOCK, CAP, V>(sh, key_at, j_at, k, orow)) radix_topk<BLOCK, CAP>(sh, x, n, k, orow);
+    if (!bucket_topk<BLOCK, CAP, V>(sh, key_at, j_at, k, orow, (n + BLOCK - 1) / BLOCK))
+      radix_topk<BLOCK, CAP>(sh, x, n, k, orow);
     return;
   }
   if (tid == 0) {
@@ -767,13 +777,14 @@ __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const 
     sh.overflow = 0;
     sh.tau = 0xFFFFFFFFu;
   }
-  const ValueBins bins = bucket_threshold<BLOCK, CAP, V>(sh, key_at, k);
+  int bin[V];
+  bucket_threshold<BLOCK, CAP, V>(sh, key_at, k, V, bin);
   const int bstar = sh.digit;
   // prefix keys in bins >= b* join the list; tau, the smallest of them, is
   // at most the prefix's k-th largest key
   uint32_t mn = 0xFFFFFFFFu, unused = 0u;
   append_list<BLOCK, CAP, V>(sh, key_at, j_at, [&](int v) {
-    const bool t = key[v] != 0u && bins(key[v]) >= bstar;
+    const bool t = bin[v] >= bstar;
     if (t) mn = min(mn, key[v]);
     return t;
   });
