@@ -7,7 +7,9 @@ step (algorithmic logits FLOPs / step wall time), `topk_gather_GBps` the
 algorithmic bytes of top-k + gather over their kernel time; `stages` has every
 kernel's average duration against its roof, and `roofline` repeats the
 dominant kernel. Prefill configs also time the fused step
-(xk_indexer_logits_topk -> gather, no score matrix) under `fused`.
+(xk_indexer_logits_topk -> gather, no score matrix) under `fused`, and every
+config times the sparse attention that consumes the selection under
+`consumer` (not part of the step).
 
 Steps are replayed from HIP graphs (one captured step per input copy), so the
 timed loop measures the GPU rather than Python's launch cost; before timing,
@@ -314,6 +316,44 @@ def fused_timing(args, cfg, steps, n_sets, eager_out, ms):
             "note": "xk_indexer_logits_topk + gather; same indices and rows as the step"}
 
 
+def consumer_timing(args, x, d, steps, n_sets):
+    """The sparse attention that consumes the step's selection
+    (xk_sparse_attention_mxfp4 on the top-k indices and the mxfp4 cache),
+    timed like the step's kernels. Algorithmic work per valid slot: the
+    cache row (64 B nibbles + 4 B scales) and its sel_pos entry, and
+    4*H*128 FLOPs (scores and weighted sum); per row: q (bf16) and out
+    (fp32)."""
+    import torch
+    import workloads
+    import sparse_attention_indexer_logits_amd as xk
+    cfg = x["cfg"]
+    a = workloads.attention_inputs(cfg)
+    H = a["q"].shape[1]
+    q = torch.from_numpy(a["q"].view(np.int16)).cuda().view(torch.bfloat16)
+    sink = torch.from_numpy(a["sink"]).cuda()
+    idx = steps[0].idx
+    n_valid = int((idx >= 0).sum().item())
+    calls, outs = [], []  # outs keeps every output alive while launches hold its pointer
+    for s in steps[:n_sets]:
+        cargs, out = xk.attention_args(q, d["kv_fp4"], d["kv_scale"], d["block_table"], s.idx, d["row_seq"],
+                                       sink, a["scale"])
+        outs.append(out)
+        calls.append(lambda c=cargs: xk._check(xk.lib().xk_sparse_attention_mxfp4(*c, xk._stream(None))))
+    n_in_graph = 20
+    us = _graph_us(torch, [calls[i % len(calls)] for i in range(n_in_graph)], max(1, args.steps // n_in_graph))
+    torch.cuda.synchronize()
+    del calls, outs
+    nbytes = n_valid * (68 + 4) + cfg.rows * H * 128 * (2 + 4)
+    flops = n_valid * 4 * H * 128
+    gbps = nbytes / (us / 1e6) / 1e9
+    tflops = flops / (us / 1e6) / 1e12
+    bound = "hbm" if nbytes / (PEAK["hbm"] * 1e9) >= flops / (PEAK["mfma_bf16"] * 1e12) else "mfma"
+    return {"us": us, "heads": H, "valid_slots": n_valid, "bytes": nbytes, "flops": flops,
+            "GBps": gbps, "frac_hbm": gbps / PEAK["hbm"], "TFLOPs": tflops,
+            "frac_bf16": tflops / PEAK["mfma_bf16"], "bound": bound,
+            "note": "xk_sparse_attention_mxfp4 over the step's top-k (64 heads, sink, scale 1/sqrt(128))"}
+
+
 def copy_calibration(nbytes=1 << 30, reps=4):
     """A plain device copy of known size, to scale rocprofv3 FETCH_SIZE/WRITE_SIZE."""
     import torch
@@ -449,6 +489,7 @@ def main():
         ms[name] = e0.elapsed_time(e1) / (reps * n_in_graph)
 
     fused = fused_timing(args, cfg, steps, n_sets, eager_out, ms) if cfg.T >= 8 and cfg.kcache is None else None
+    consumer = consumer_timing(args, x, d, steps, n_sets)
 
     prefill = cfg.T >= 8
     mfma_peak = PEAK["mfma_fp8" if cfg.dtype == "fp8" else "mfma_bf16"]
@@ -494,6 +535,7 @@ def main():
     if fused is not None:
         fused["value"] = work["logits_flops"] / (fused["ms_per_step"] / 1e3) / 1e12
         line["fused"] = fused
+    line["consumer"] = consumer
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x, work, args.cpu_budget)
     print(json.dumps(line), flush=True)

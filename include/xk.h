@@ -7,6 +7,7 @@
  *   xk_indexer_topk          deterministic per-query top-k of those scores
  *   xk_indexer_logits_topk   both at once, without the score matrix for prefill shapes
  *   xk_mxfp4_paged_gather    mxfp4 paged KV rows of the selected keys, decoded to bf16
+ *   xk_sparse_attention_mxfp4  attention of each query over its selected rows (the consumer)
  * and the producers of their quantized inputs:
  *   xk_quant_fp8_rows        per-row OCP fp8 quantizer (q per token and head, k per token)
  *   xk_mxfp4_cache_write     rows into the paged mxfp4 cache
@@ -152,6 +153,35 @@ size_t xk_indexer_topk_workspace_size(int R, int K, int k);
 xk_status xk_indexer_topk(const float* logits, const int32_t* limit, int32_t* idx,
                           int R, int K, int k,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sparse attention over the selected rows, read from the paged mxfp4 cache.
+ *
+ * Defines (page "DeepSeek-V4 on ATOM" tracker, "CSA": the sparse attention
+ * path is an index gather, an online softmax and an attention-sink bias;
+ * the rows are the ones xk_mxfp4_paged_gather decodes, page "xkernels #28 --
+ * DeepSeek-V4 serving support"): with v_j the decoded cache row of slot j
+ * (row r's selected position sel_pos[r,j]; slots < 0 take no part), serving
+ * as key and value for every head (MQA over the latent row),
+ *   s_j        = scale * (q[r,h,:] . v_j)
+ *   out[r,h,:] = sum_j exp(s_j) v_j / (sum_j exp(s_j) + exp(sink[h]))
+ * and 0 for a row without a valid slot (sink NULL: no sink term).
+ *
+ *   q            [R,H,D] bf16 (16-byte aligned)
+ *   kv_fp4, kv_scale, block_table, sel_pos [R,k], row_seq, S, MB, NB, bs:
+ *                as for xk_mxfp4_paged_gather (kv_fp4 16-byte aligned)
+ *   sink         [H] fp32 per-head sink logit, or NULL
+ *   scale        the softmax scale (finite)
+ *   out          [R,H,D] fp32 (16-byte aligned); every element is written
+ *   D must be 128, H a multiple of 64 and k <= 2048, else XK_ERR_UNSUPPORTED.
+ * Scores and sums are fp32; the weights enter the value sum rounded to bf16,
+ * so |out - exact| <= ~2^-9 * max_j |v_j| per row.
+ */
+xk_status xk_sparse_attention_mxfp4(const void* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
+                                    const int32_t* block_table, const int32_t* sel_pos,
+                                    const int32_t* row_seq, const float* sink, float scale,
+                                    float* out, int R, int H, int k, int S, int MB, int NB, int bs,
+                                    int D, void* stream);
 
 /*
  * Bytes of device workspace xk_indexer_logits_topk needs for these sizes.

@@ -23,7 +23,7 @@ XK_IN_FP32, XK_IN_BF16 = 0, 1
 
 EXPORTED = ("xk_indexer_logits", "xk_indexer_logits_paged", "xk_indexer_topk_workspace_size",
             "xk_indexer_topk", "xk_indexer_logits_topk_workspace_size", "xk_indexer_logits_topk",
-            "xk_mxfp4_paged_gather", "xk_quant_fp8_rows", "xk_mxfp4_cache_write",
+            "xk_mxfp4_paged_gather", "xk_sparse_attention_mxfp4", "xk_quant_fp8_rows", "xk_mxfp4_cache_write",
             "xk_status_string", "xk_last_error")
 
 
@@ -51,6 +51,9 @@ def _load() -> ctypes.CDLL:
     lib.xk_indexer_logits_topk_workspace_size.restype = Z
     lib.xk_indexer_logits_topk.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P]
     lib.xk_indexer_logits_topk.restype = I
+    lib.xk_sparse_attention_mxfp4.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, I, I, I, I, I,
+                                              I, I, I, P]
+    lib.xk_sparse_attention_mxfp4.restype = I
     lib.xk_mxfp4_paged_gather.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.xk_mxfp4_paged_gather.restype = I
     L = ctypes.c_int64
@@ -316,6 +319,52 @@ def xk_mxfp4_paged_gather(kv_fp4, kv_scale, block_table, sel_pos, row_seq=None, 
     """
     args, out = gather_args(kv_fp4, kv_scale, block_table, sel_pos, row_seq, out)
     _check(_lib.xk_mxfp4_paged_gather(*args, _stream(stream)))
+    return out
+
+
+def attention_args(q, kv_fp4, kv_scale, block_table, sel_pos, row_seq=None, sink=None, scale=None,
+                   out=None):
+    """Validate the arguments of xk_sparse_attention_mxfp4; returns (C
+    arguments without the stream, out). scale None means 1/sqrt(D)."""
+    _need(q, "q", (torch.bfloat16,), 3)
+    R, H, D = q.shape
+    _need(kv_fp4, "kv_fp4", (torch.uint8,), 3)
+    _need(kv_scale, "kv_scale", (torch.uint8,), 3)
+    NB, bs, half = kv_fp4.shape
+    if 2 * half != D or tuple(kv_scale.shape) != (NB, bs, D // 32):
+        raise ValueError("kv_fp4 must be [NB,bs,D/2] and kv_scale [NB,bs,D/32]")
+    _need(block_table, "block_table", (torch.int32,), 2)
+    S, MB = block_table.shape
+    _need(sel_pos, "sel_pos", (torch.int32,), 2)
+    if sel_pos.shape[0] != R:
+        raise ValueError("sel_pos must be [R,k]")
+    k = sel_pos.shape[1]
+    if row_seq is not None:
+        _need(row_seq, "row_seq", (torch.int32,), 1)
+        if row_seq.shape[0] != R:
+            raise ValueError("row_seq must have R entries")
+    if sink is not None:
+        _need(sink, "sink", (torch.float32,), 1)
+        if sink.shape[0] != H:
+            raise ValueError("sink must have H entries")
+    if scale is None:
+        scale = 1.0 / D ** 0.5
+    if out is None:
+        out = torch.empty((R, H, D), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 3)
+    if tuple(out.shape) != (R, H, D):
+        raise ValueError("out must be [R,H,D]")
+    args = (_ptr(q), _ptr(kv_fp4), _ptr(kv_scale), _ptr(block_table), _ptr(sel_pos), _ptr(row_seq),
+            _ptr(sink), float(scale), _ptr(out), R, H, k, S, MB, NB, bs, D)
+    return args, out
+
+
+def xk_sparse_attention_mxfp4(q, kv_fp4, kv_scale, block_table, sel_pos, row_seq=None, sink=None,
+                              scale=None, out=None, stream=None):
+    """out [R,H,D] fp32: attention of each query over its selected mxfp4 cache
+    rows with a per-head sink logit (see include/xk.h)."""
+    args, out = attention_args(q, kv_fp4, kv_scale, block_table, sel_pos, row_seq, sink, scale, out)
+    _check(_lib.xk_sparse_attention_mxfp4(*args, _stream(stream)))
     return out
 
 

@@ -1,0 +1,212 @@
+// Sparse attention over the indexer's selection, reading the paged mxfp4
+// cache directly (gfx950): the consumer of the top-k indices.
+//
+// Semantics (page "DeepSeek-V4 on ATOM" tracker, "CSA": index gather, online
+// softmax, attention-sink bias; the rows are the cache rows the mxfp4 paged
+// gather of page "xkernels #28 -- DeepSeek-V4 serving support" decodes): for
+// row r with selected positions sel_pos[r, :] and head h,
+//   s_j = scale * (q[r,h,:] . v_j)   over slots j with sel_pos >= 0
+//   out[r,h,:] = sum_j exp(s_j) v_j / (sum_j exp(s_j) + exp(sink[h]))
+// where v_j, the decoded cache row, is both key and value (MQA over the
+// latent row). A row with no valid slot gives 0.
+//
+// One workgroup per (row, 64 heads), one wave per 16 heads. The row's slots
+// are resolved to cache tokens once (sel_pos -> block table) into LDS.
+// Then per chunk of 64 slots:
+//  * 256 threads decode the chunk's mxfp4 rows (exact, as the gather does)
+//    into a K tile [slot][d] and a transposed V tile [d][slot] in LDS; the
+//    next chunk's nibbles are loaded into registers meanwhile;
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (keys as rows, this wave's 16
+//    heads as columns): lane l holds head l%16's scores of keys 4(l/16)+i of
+//    each 16-key subtile;
+//  * online softmax in base 2 per head (max and sum across the four lane
+//    groups of a head by two shuffles), accumulators rescaled;
+//  * O^T += V^T P^T on the same MFMA: P^T is the B operand straight from the
+//    S^T registers (rounded to bf16). The contraction over keys only needs A
+//    and B to agree on the key order, so K-slot 8g+e of a 32-key step is key
+//    4g+e of its first subtile (e < 4) or of its second (e >= 4), and the V^T
+//    fragment reads the same keys (two 8-byte LDS reads).
+// At the end the sink joins the denominator and lane l stores 4 consecutive
+// outputs of head l%16 per 16-dim tile.
+#include "mxfp4.h"
+
+namespace xk {
+namespace {
+
+constexpr int kAttnHeads = 64;              // heads per workgroup
+constexpr int kChunk = 64;                  // slots per chunk
+constexpr int kKPitch = kHeadDim + 8;       // bf16 per K-tile row (16-byte pad)
+constexpr int kVPitch = kChunk + 8;         // bf16 per V^T-tile row
+constexpr int kMaxAttnSlots = 2048;         // tokens resolved in LDS
+
+__device__ __forceinline__ float shfl_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float shfl_sum(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+__global__ __launch_bounds__(256) void sparse_attention_kernel(
+    const uint16_t* __restrict__ q, const uint32_t* __restrict__ kv_fp4, const uint8_t* __restrict__ kv_scale,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ sel_pos,
+    const int32_t* __restrict__ row_seq, const float* __restrict__ sink, float scale_log2,
+    float* __restrict__ out, int H, int k, int MB, int bs_log2) {
+  using Frag = bf16x8;
+  __shared__ __attribute__((aligned(16))) uint16_t kt[kChunk * kKPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kHeadDim * kVPitch];
+  __shared__ __attribute__((aligned(16))) float sbias[kChunk];
+  __shared__ int tok[kMaxAttnSlots];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int groups = H / kAttnHeads;
+  const int64_t r = blockIdx.x / groups;
+  const int head = (blockIdx.x % groups) * kAttnHeads + 16 * wave + c;  // this lane's head column
+
+  // 1. the row's slots -> cache tokens (-1: padded slot)
+  const int seq = row_seq ? row_seq[r] : int(r);
+  for (int j = tid; j < k; j += 256) {
+    const int p = sel_pos[r * k + j];
+    int t = -1;
+    if (p >= 0) {
+      const int blk = block_table[int64_t(seq) * MB + (p >> bs_log2)];
+      t = (blk << bs_log2) + (p & ((1 << bs_log2) - 1));
+    }
+    tok[j] = t;
+  }
+  // this wave's 16 heads as B fragments (column = head, K = d in [32s+8g, +8))
+  Frag qb[4];
+  const uint16_t* qrow = q + (r * H + head) * int64_t(kHeadDim);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qb[s] = *reinterpret_cast<const Frag*>(qrow + 32 * s + 8 * g);
+  __syncthreads();
+
+  // chunk loads: thread -> slot tid/4 of the chunk, dims [32*(tid%4), +32)
+  const int lslot = tid >> 2, quarter = tid & 3;
+  auto fetch = [&](int c0, u32x4& nib, uint32_t& sc, int& t) {
+    const int j = c0 + lslot;
+    t = j < k ? tok[j] : -1;
+    nib = u32x4{0u, 0u, 0u, 0u};
+    sc = 0u;
+    if (t >= 0) {
+      nib = reinterpret_cast<const u32x4*>(kv_fp4)[int64_t(t) * 4 + quarter];
+      sc = kv_scale[int64_t(t) * 4 + quarter];
+    }
+  };
+  u32x4 nib;
+  uint32_t sc;
+  int t;
+  fetch(0, nib, sc, t);
+
+  f32x4 o[8];  // O^T tile mt: dims 16mt + 4g + i of head c
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;  // running max (base-2 scaled) and sum of head c
+
+  for (int c0 = 0; c0 < k; c0 += kChunk) {
+    // 2. decode the chunk into the K and V^T tiles
+    {
+      u32x4 d[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) d[w] = t >= 0 ? decode8(nib[w], sc) : u32x4{0u, 0u, 0u, 0u};
+      uint16_t* krow = kt + lslot * kKPitch + 32 * quarter;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) reinterpret_cast<u32x4*>(krow)[w] = d[w];
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int dim = 32 * quarter + 8 * w + 2 * e;
+          vt[dim * kVPitch + lslot] = uint16_t(d[w][e] & 0xFFFFu);
+          vt[(dim + 1) * kVPitch + lslot] = uint16_t(d[w][e] >> 16);
+        }
+      if (quarter == 0) sbias[lslot] = t >= 0 ? 0.f : -INFINITY;
+    }
+    __syncthreads();
+    if (c0 + kChunk < k) fetch(c0 + kChunk, nib, sc, t);  // in flight during the MFMAs
+
+    // 3. S^T = K Q^T for this wave's heads
+    f32x4 sacc[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* arow = kt + (16 * st + c) * kKPitch + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const Frag*>(arow + 32 * s), qb[s],
+                                                            sacc[st], 0, 0, 0);
+    }
+    // 4. online softmax (base 2), head c
+    float x[4][4], cmax = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sbias[16 * st + 4 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[st][i] = fmaf(sacc[st][i], scale_log2, b4[i]);
+        cmax = fmaxf(cmax, x[st][i]);
+      }
+    }
+    cmax = shfl_max(cmax);
+    const float m_new = fmaxf(m, cmax);
+    const bool any = m_new > -INFINITY;
+    const float alpha = any ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+    float psum = 0.f;
+    Frag pb[2];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = any ? __builtin_amdgcn_exp2f(x[st][i] - m_new) : 0.f;
+        psum += p;
+        pb[st >> 1][4 * (st & 1) + i] = __bf16(p);
+      }
+    l = fmaf(l, alpha, shfl_sum(psum));
+    m = m_new;
+    // 5. O^T = O^T * alpha + V^T P^T
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const uint16_t* vrow = vt + (16 * mt + c) * kVPitch + 32 * ks + 4 * g;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        const Frag a = __builtin_bit_cast(Frag, u32x4{lo.x, lo.y, hi.x, hi.y});
+        o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ks], o[mt], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // the tiles are rewritten by the next chunk
+  }
+
+  // 6. the sink joins the denominator; store head c's outputs
+  const float s2 = sink ? sink[head] * 1.4426950408889634f : -INFINITY;
+  const float mf = fmaxf(m, s2);
+  float f = 0.f;
+  if (mf > -INFINITY) {
+    const float a = __builtin_amdgcn_exp2f(m - mf);
+    f = a / (l * a + __builtin_amdgcn_exp2f(s2 - mf));
+  }
+  float* orow = out + (r * H + head) * int64_t(kHeadDim);
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(orow + 16 * mt + 4 * g) = o[mt] * f;
+}
+
+}  // namespace
+
+hipError_t launch_sparse_attention(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
+                                   const int32_t* block_table, const int32_t* sel_pos, const int32_t* row_seq,
+                                   const float* sink, float scale, float* out, int R, int H, int k, int MB, int bs,
+                                   hipStream_t stream) {
+  const int bs_log2 = __builtin_ctz(unsigned(bs));
+  const float scale_log2 = float(double(scale) * 1.4426950408889634);  // softmax in base 2
+  hipLaunchKernelGGL(sparse_attention_kernel, dim3(unsigned(int64_t(R) * (H / kAttnHeads))), dim3(256), 0, stream,
+                     q, reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale, block_table, sel_pos, row_seq, sink,
+                     scale_log2, out, H, k, MB, bs_log2);
+  return hipGetLastError();
+}
+
+}  // namespace xk

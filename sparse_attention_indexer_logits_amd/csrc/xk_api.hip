@@ -1,6 +1,7 @@
 // C ABI of libxk: argument validation, device check and kernel dispatch.
 // Every check that needs no device runs before the first HIP call, so a bad
 // argument is reported without touching the GPU.
+#include <math.h>
 #include <string.h>
 
 #include <map>
@@ -236,4 +237,33 @@ XK_EXPORT xk_status xk_mxfp4_paged_gather(const uint8_t* kv_fp4, const uint8_t* 
   return launched(xk::launch_gather(kv_fp4, kv_scale, block_table, sel_pos, row_seq, out, R, k,
                                     MB, bs, static_cast<hipStream_t>(stream)),
                   "xk_mxfp4_paged_gather launch");
+}
+
+XK_EXPORT xk_status xk_sparse_attention_mxfp4(const void* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
+                                              const int32_t* block_table, const int32_t* sel_pos,
+                                              const int32_t* row_seq, const float* sink, float scale, float* out,
+                                              int R, int H, int k, int S, int MB, int NB, int bs, int D,
+                                              void* stream) {
+  if (!q || !kv_fp4 || !kv_scale || !block_table || !sel_pos || !out)
+    return fail(XK_ERR_INVALID_ARGUMENT, "null q, kv_fp4, kv_scale, block_table, sel_pos or out");
+  if (R < 1 || H < 1 || k < 1 || S < 1 || MB < 1 || NB < 1 || bs < 1 || D < 1)
+    return fail(XK_ERR_INVALID_ARGUMENT, "R, H, k, S, MB, NB, bs, D must be >= 1");
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+    return fail(XK_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (D != xk::kHeadDim) return fail(XK_ERR_UNSUPPORTED, "only D=128 is implemented");
+  if (H % 64 != 0) return fail(XK_ERR_UNSUPPORTED, "H must be a multiple of 64");
+  if (k > 2048) return fail(XK_ERR_UNSUPPORTED, "k above 2048");
+  if ((bs & (bs - 1)) != 0) return fail(XK_ERR_UNSUPPORTED, "block size must be a power of two");
+  if (!row_seq && R > S) return fail(XK_ERR_INVALID_ARGUMENT, "row_seq NULL needs R <= S");
+  if (int64_t(NB) * bs > (int64_t(1) << 31) - 1)
+    return fail(XK_ERR_UNSUPPORTED, "NB*bs (cache tokens) above 2^31-1");
+  if (int64_t(R) * (H / 64) > (int64_t(1) << 31) - 1) return fail(XK_ERR_UNSUPPORTED, "R*H/64 above 2^31-1");
+  if (!aligned(q, 16) || !aligned(kv_fp4, 16) || !aligned(out, 16))
+    return fail(XK_ERR_INVALID_ARGUMENT, "q, kv_fp4 and out must be 16-byte aligned");
+  xk_status s = check_device();
+  if (s != XK_OK) return s;
+  return launched(xk::launch_sparse_attention(static_cast<const uint16_t*>(q), kv_fp4, kv_scale, block_table,
+                                              sel_pos, row_seq, sink, scale, out, R, H, k, MB, bs,
+                                              static_cast<hipStream_t>(stream)),
+                  "xk_sparse_attention_mxfp4 launch");
 }

@@ -89,6 +89,10 @@ hipError_t launch_logits_topk(const void* q, const float* q_scale, const void* k
                               const float* k_scale, const float* w, const int32_t* limit,
                               int32_t* idx, int B, int T, int K, int ktop, bool fp8, void* workspace,
                               hipStream_t stream);
+hipError_t launch_sparse_attention(const uint16_t* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
+                                   const int32_t* block_table, const int32_t* sel_pos, const int32_t* row_seq,
+                                   const float* sink, float scale, float* out, int R, int H, int k, int MB, int bs,
+                                   hipStream_t stream);
 hipError_t launch_gather(const uint8_t* kv_fp4, const uint8_t* kv_scale,
                          const int32_t* block_table, const int32_t* sel_pos,
                          const int32_t* row_seq, uint16_t* out, int R, int k, int MB,

@@ -29,6 +29,7 @@ def test_header_declares_the_three_operations():
     names = declared_functions()
     for n in ("xk_indexer_logits", "xk_indexer_logits_paged", "xk_indexer_topk",
               "xk_indexer_logits_topk", "xk_indexer_logits_topk_workspace_size",
+              "xk_sparse_attention_mxfp4",
               "xk_mxfp4_paged_gather", "xk_indexer_topk_workspace_size", "xk_quant_fp8_rows",
               "xk_mxfp4_cache_write", "xk_status_string", "xk_last_error"):
         assert n in names
@@ -120,6 +121,25 @@ def test_topk_workspace_is_host_only(lib):
 ])
 def test_logits_topk_validation(lib, args, status, needle):
     assert lib.xk_indexer_logits_topk(*args, None) == status
+    assert needle in lib.xk_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    # (q, kv_fp4, kv_scale, block_table, sel_pos, row_seq, sink, scale, out,
+    #  R, H, k, S, MB, NB, bs, D)
+    ((None, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 1, 64, 4, 1, 1, 1, 64, 128), 1, "null"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, None, 1, 64, 4, 1, 1, 1, 64, 128), 1, "null"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 1, 64, 0, 1, 1, 1, 64, 128), 1, ">= 1"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, float("nan"), FAKE, 1, 64, 4, 1, 1, 1, 64, 128), 1, "finite"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 1, 64, 4, 1, 1, 1, 64, 64), 2, "D=128"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 1, 32, 4, 1, 1, 1, 64, 128), 2, "multiple of 64"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 1, 64, 4096, 1, 1, 1, 64, 128), 2, "2048"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 1, 64, 4, 1, 1, 1, 48, 128), 2, "power of two"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 3, 64, 4, 2, 1, 1, 64, 128), 1, "R <= S"),
+    ((FAKE, FAKE + 4, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 1, 64, 4, 1, 1, 1, 64, 128), 1, "aligned"),
+])
+def test_sparse_attention_validation(lib, args, status, needle):
+    assert lib.xk_sparse_attention_mxfp4(*args, None) == status
     assert needle in lib.xk_last_error().decode()
 
 

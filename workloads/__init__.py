@@ -27,7 +27,7 @@ BLOCK_SIZE = 64   # paged-cache tokens per block
 FP8_E4M3_MAX = 448.0
 
 # order in which child streams are spawned; never reorder (changes every input)
-_STREAMS = ("q", "k", "w", "lens", "fp4", "scale", "table", "ff", "neg", "kc4", "kcs")
+_STREAMS = ("q", "k", "w", "lens", "fp4", "scale", "table", "ff", "neg", "kc4", "kcs", "aq", "sink")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -237,6 +237,23 @@ def custom(name="custom", seed=123, B=1, T=4, K=300, topk=16, dtype="bf16",
                               causal_offset=causal_offset, len_range=len_range,
                               n_ff=n_ff, n_neg=n_neg, scale_lo=scale_lo, scale_hi=scale_hi,
                               kcache=kcache, kscale_lo=kscale_lo, kscale_hi=kscale_hi))
+
+
+ATTN_HEADS = 64
+ATTN_Q_SIGMA = 2.0 ** -7   # scores of a few units against the configs' mxfp4 rows
+
+
+@functools.lru_cache(maxsize=2)
+def attention_inputs(cfg: Config, heads: int = ATTN_HEADS, q_sigma: float = ATTN_Q_SIGMA) -> dict:
+    """Inputs of the sparse attention that consumes a config's selection:
+    q [rows, heads, 128] bf16 bits ~ N(0, q_sigma^2), a sink logit per head
+    ~ N(0, 1), and the softmax scale 1/sqrt(128). With the configs' group
+    scales (E8M0 bytes 118..136) a cache row has an rms of a few hundred, so
+    q_sigma = 2^-7 gives scores of a few units."""
+    s = _streams(cfg.seed)
+    q = _to_bf16_bits(_normal(s["aq"], (cfg.rows, heads, D_INDEX)) * np.float32(q_sigma))
+    sink = _normal(s["sink"], (heads,))
+    return {"q": q, "sink": sink, "scale": float(1.0 / np.sqrt(D_INDEX))}
 
 
 def apply_forced_negatives(idx: np.ndarray, neg_slots) -> np.ndarray:
