@@ -712,24 +712,31 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ l
 }
 
 // Append the entries u of a chunk with take(u) to the LDS list ckey / cj
-// (key_at / j_at are evaluated for taken entries only): one ballot and one
-// LDS atomic per wave and entry index. The list order depends on the
-// atomics, which nothing downstream relies on.
+// (key_at / j_at are evaluated for taken entries only). The wave takes all
+// U ballots first and claims room for all its entries with one LDS atomic,
+// so the per-entry-index chain is only SALU counting. The list order
+// depends on the atomics, which nothing downstream relies on.
 template <int BLOCK, int CAP, int U, typename KeyAt, typename JAt, typename Take>
 __device__ __forceinline__ void append_list(TopkShared<BLOCK, CAP>& sh, KeyAt key_at, JAt j_at,
                                             Take take_it) {
   const int lane = lane_id();
+  bool take[U];
+  uint64_t mask[U];
+  int total = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const bool take = take_it(u);
-    const uint64_t m = __ballot(take);
-    if (m == 0) continue;
-    const int leader = __ffsll((unsigned long long)m) - 1;
-    int base = 0;
-    if (lane == leader) base = atomicAdd(&sh.ccount, __popcll(m));
-    base = __builtin_amdgcn_readlane(base, leader);
-    if (take) {
-      const int pos = base + prefix_in_wave(m);
+    take[u] = take_it(u);
+    mask[u] = __ballot(take[u]);
+    total += __popcll(mask[u]);
+  }
+  if (total == 0) return;  // uniform
+  int base = 0;
+  if (lane == 0) base = atomicAdd(&sh.ccount, total);
+  base = __builtin_amdgcn_readlane(base, 0);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (take[u]) {
+      const int pos = base + prefix_in_wave(mask[u]);
       if (pos < CAP) {
         sh.ckey[pos] = key_at(u);
         sh.cj[pos] = j_at(u);
@@ -737,6 +744,7 @@ __device__ __forceinline__ void append_list(TopkShared<BLOCK, CAP>& sh, KeyAt ke
         sh.overflow = 1;
       }
     }
+    base += __popcll(mask[u]);
   }
 }
 
