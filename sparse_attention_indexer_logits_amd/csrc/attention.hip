@@ -36,7 +36,8 @@ namespace {
 constexpr int kAttnHeads = 64;              // heads per workgroup
 constexpr int kChunk = 64;                  // slots per chunk
 constexpr int kKPitch = kHeadDim + 8;       // bf16 per K-tile row (16-byte pad)
-constexpr int kVPitch = kChunk + 8;         // bf16 per V^T-tile row
+constexpr int kVPitch = kChunk + 4;         // bf16 per V^T-tile row: 34 dwords, so the 8-byte
+                                            // fragment reads of 16 rows hit 16 distinct bank pairs
 constexpr int kMaxAttnSlots = 2048;         // tokens resolved in LDS
 
 __device__ __forceinline__ float shfl_max(float v) {
@@ -83,8 +84,9 @@ __global__ __launch_bounds__(256) void sparse_attention_kernel(
   for (int s = 0; s < 4; ++s) qb[s] = *reinterpret_cast<const Frag*>(qrow + 32 * s + 8 * g);
   __syncthreads();
 
-  // chunk loads: thread -> slot tid/4 of the chunk, dims [32*(tid%4), +32)
-  const int lslot = tid >> 2, quarter = tid & 3;
+  // chunk loads: thread -> slot tid%64 of the chunk, dims [32*(tid/64), +32): a
+  // wave's transposed writes then cover 64 consecutive slots of one dim
+  const int lslot = tid & 63, quarter = tid >> 6;
   auto fetch = [&](int c0, u32x4& nib, uint32_t& sc, int& t) {
     const int j = c0 + lslot;
     t = j < k ? tok[j] : -1;
