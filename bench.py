@@ -11,11 +11,12 @@ dominant kernel. Prefill configs also time the fused step
 config times the sparse attention that consumes the selection under
 `consumer` (not part of the step).
 
-Steps are replayed from HIP graphs (one captured step per input copy), so the
-timed loop measures the GPU rather than Python's launch cost; before timing,
-two replays are checked bit for bit against an eager step, and
-`ms_per_step_eager` reports eager launches too. A kernel's duration is
-timed with HIP events on the launch stream around replays of a graph of 20
+Steps are replayed from HIP graphs: one graph holds a round of steps, one
+per input copy, so the timed loop measures the GPU rather than Python's or
+the graph launch's cost; before timing, replays are checked bit for bit
+against an eager step, and `ms_per_step_eager` reports eager launches too.
+A kernel's duration is timed with HIP events on the launch stream around
+replays of a graph of 20
 back-to-back launches of that kernel alone (rotating the same input
 copies), so no launch gap is counted.
 
@@ -256,6 +257,43 @@ def producers(args):
     print(json.dumps(line), flush=True)
 
 
+def step_graphs(torch, steps, run):
+    """One captured graph per step (input copy) and one holding a round of
+    all of them in order."""
+    graphs = []
+    for s in steps:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(s)
+        graphs.append(g)
+    round_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(round_graph):
+        for s in steps:
+            run(s)
+    torch.cuda.synchronize()
+    return graphs, round_graph
+
+
+def time_steps(torch, graphs, round_graph, n_steps, warmup):
+    """Wall ms per step over exactly n_steps steps: whole rounds from the round
+    graph (one launch per len(graphs) steps), the rest from single-step
+    graphs; warm-up the same way, untimed."""
+    n = len(graphs)
+
+    def run(count):
+        for _ in range(count // n):
+            round_graph.replay()
+        for i in range(count % n):
+            graphs[i].replay()
+
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(n_steps)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / n_steps
+
+
 def _graph_us(torch, launches, reps):
     """Average duration of one launch in a graph of back-to-back launches,
     timed with events on the launch stream."""
@@ -289,20 +327,8 @@ def fused_timing(args, cfg, steps, n_sets, eager_out, ms):
     torch.cuda.synchronize()
     if not (torch.equal(base.idx, eager_out[1]) and torch.equal(base.gathered, eager_out[2])):
         raise RuntimeError("fused logits -> top-k differs from the three-kernel step")
-    graphs = []
-    for s in steps:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            s.run_fused()
-        graphs.append(g)
-    for i in range(args.warmup):
-        graphs[i % n_sets].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % n_sets].replay()
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    graphs, round_graph = step_graphs(torch, steps, lambda s: s.run_fused())
+    ms_step = time_steps(torch, graphs, round_graph, args.steps, args.warmup)
     if not (torch.equal(base.idx, eager_out[1]) and torch.equal(base.gathered, eager_out[2])):
         raise RuntimeError("fused graph replays differ from the three-kernel step")
     n_in_graph = 20
@@ -442,31 +468,18 @@ def main():
     torch.cuda.synchronize()
     ms_step_eager = (time.perf_counter() - t0) * 1e3 / n_eager
 
-    # one HIP graph per input copy holds a whole step (three kernels)
-    graphs = []
-    for s in steps:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            s()
-        graphs.append(g)
-    torch.cuda.synchronize()
+    # one HIP graph per input copy holds a whole step (three kernels), and one
+    # graph holds a round of n_sets steps (one per input copy)
+    graphs, round_graph = step_graphs(torch, steps, lambda s: s())
     for rep in range(2):   # replays must reproduce the eager outputs bit for bit
-        graphs[0].replay()
-        torch.cuda.synchronize()
-        if not all(torch.equal(a, b) for a, b in zip(base.outputs(), eager_out)):
-            raise RuntimeError("graph replay differs from the eager step")
-        steps[0]()          # eager work between replays
-        torch.cuda.synchronize()
-
-    for i in range(args.warmup):
-        graphs[i % n_sets].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % n_sets].replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
+        for g in (graphs[0], round_graph):
+            g.replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(a, b) for a, b in zip(base.outputs(), eager_out)):
+                raise RuntimeError("graph replay differs from the eager step")
+            steps[0]()          # eager work between replays
+            torch.cuda.synchronize()
+    ms_step = time_steps(torch, graphs, round_graph, args.steps, args.warmup)
 
     # per-kernel durations: a graph of back-to-back launches of one kernel,
     # rotating the input copies, timed with events on the launch stream
