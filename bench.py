@@ -16,9 +16,8 @@ per input copy, so the timed loop measures the GPU rather than Python's or
 the graph launch's cost; before timing, replays are checked bit for bit
 against an eager step, and `ms_per_step_eager` reports eager launches too.
 A kernel's duration is timed with HIP events on the launch stream around
-replays of a graph of 20
-back-to-back launches of that kernel alone (rotating the same input
-copies), so no launch gap is counted.
+replays of a graph of 20 back-to-back launches of that kernel alone
+(rotating the same input copies), so no launch gap is counted.
 
 Inputs are resident in HBM before timing starts. Several identical copies of
 q/k/w are rotated across steps so that a decode-sized working set cannot be
