@@ -52,7 +52,8 @@ __device__ __forceinline__ int clamp_limit(const int32_t* limit, int64_t bt, int
 // the 16-byte pieces of d named by Mma16::dofs), 16 KB in flight per wave;
 // 64 keys (four subtiles) make one coalesced 256-byte store. No LDS traffic
 // and no barrier inside the key loop.
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 2;    // dense keys: two waves x a 256- or 384-key chunk
+constexpr int kPagedWaves = 4;  // paged keys: four waves (the paged kernel below)
 constexpr int kDecGroup = 64;  // keys per store: four 16-key subtiles
 
 template <bool FP8>
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void logits_decode_kernel(
 constexpr int kPagedTab = 72;  // staged table entries per workgroup (chunk / 16 + 1)
 
 template <bool MXFP4, int kRing = 8>  // kRing: subtiles in flight per wave
-__global__ __launch_bounds__(kDecWaves * 64, 2) void logits_paged_kernel(
+__global__ __launch_bounds__(kPagedWaves * 64, 2) void logits_paged_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ kcs,
     const int32_t* __restrict__ block_table, const float* __restrict__ w,
@@ -253,12 +254,12 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void logits_paged_kernel(
   const int j_end = min(j_begin + keys_per_wg, K);
   float* orow = out + bt * K;
 
-  for (int j = max(j_begin, lim + 1) + int(threadIdx.x); j < j_end; j += kDecWaves * 64)
+  for (int j = max(j_begin, lim + 1) + int(threadIdx.x); j < j_end; j += kPagedWaves * 64)
     orow[j] = -INFINITY;
   const int c_end = min(j_end, lim + 1);
   if (c_end <= j_begin) return;  // uniform over the workgroup
 
-  const int per_wave = keys_per_wg / kDecWaves;
+  const int per_wave = keys_per_wg / kPagedWaves;
   const int w_begin = j_begin + wave * per_wave;
   const int w_end = max(w_begin, min(w_begin + per_wave, c_end));
   const int tab0 = j_begin >> bs_log2;                      // first staged page index
@@ -266,12 +267,12 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void logits_paged_kernel(
   const auto ors = make_rsrc(orow + w_begin, (w_end - w_begin) * 4);
 
   // q chunks, head weights (times the q scale) and the chunk's table entries
-  constexpr int kQLoads = kHeads * kLanesPerRow / (kDecWaves * 64);
+  constexpr int kQLoads = kHeads * kLanesPerRow / (kPagedWaves * 64);
   const uint8_t* qsrc = q + bt * (kHeads * kQRow);
   u32x4 qv[kQLoads];
 #pragma unroll
   for (int i = 0; i < kQLoads; ++i) {
-    const int c = int(threadIdx.x) + kDecWaves * 64 * i;
+    const int c = int(threadIdx.x) + kPagedWaves * 64 * i;
     qv[i] = *reinterpret_cast<const u32x4*>(qsrc + (c / kLanesPerRow) * kQRow + (c % kLanesPerRow) * 16);
   }
   float wv = 0.f;
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void logits_paged_kernel(
   if (int(threadIdx.x) < n_tab) tv = block_table[b * MB + tab0 + int(threadIdx.x)];
 #pragma unroll
   for (int i = 0; i < kQLoads; ++i) {
-    const int c = int(threadIdx.x) + kDecWaves * 64 * i;
+    const int c = int(threadIdx.x) + kPagedWaves * 64 * i;
     *reinterpret_cast<u32x4*>(q_lds + (c / kLanesPerRow) * kPitch + (c % kLanesPerRow) * 16) = qv[i];
   }
   if (threadIdx.x < kHeads) w_lds[threadIdx.x] = wv;
@@ -600,8 +601,8 @@ hipError_t launch_logits_paged(const void* q, const float* q_scale, const float*
   // measured on the Flash and Pro decode shapes)
   const int64_t rows = int64_t(B) * T;
   const int64_t per = (int64_t(K) * rows + 2047) / 2048;
-  int kpw = int(std::min<int64_t>(std::max<int64_t>(per, 2 * kDecWaves * kDecGroup), 4 * kDecWaves * kDecGroup));
-  kpw = std::min(round_up(kpw, kDecWaves * kDecGroup), round_up(K, kDecWaves * kDecGroup));
+  int kpw = int(std::min<int64_t>(std::max<int64_t>(per, 2 * kPagedWaves * kDecGroup), 4 * kPagedWaves * kDecGroup));
+  kpw = std::min(round_up(kpw, kPagedWaves * kDecGroup), round_up(K, kPagedWaves * kDecGroup));
   const int nch = (K + kpw - 1) / kpw;
   int bs_log2 = 0;
   while ((1 << bs_log2) < bs) ++bs_log2;
@@ -610,10 +611,10 @@ hipError_t launch_logits_paged(const void* q, const float* q_scale, const float*
   const auto* kc = static_cast<const uint8_t*>(k_cache);
   const auto* ks = static_cast<const uint8_t*>(k_scale);
   if (mxfp4)
-    hipLaunchKernelGGL(logits_paged_kernel<true>, grid, dim3(kDecWaves * 64), 0, stream, q8, q_scale, kc, ks,
+    hipLaunchKernelGGL(logits_paged_kernel<true>, grid, dim3(kPagedWaves * 64), 0, stream, q8, q_scale, kc, ks,
                        block_table, w, limit, logits, T, K, MB, bs_log2, kpw, nch);
   else
-    hipLaunchKernelGGL(logits_paged_kernel<false>, grid, dim3(kDecWaves * 64), 0, stream, q8, q_scale, kc, ks,
+    hipLaunchKernelGGL(logits_paged_kernel<false>, grid, dim3(kPagedWaves * 64), 0, stream, q8, q_scale, kc, ks,
                        block_table, w, limit, logits, T, K, MB, bs_log2, kpw, nch);
   return hipGetLastError();
 }
@@ -624,10 +625,11 @@ hipError_t launch_logits(const void* q, const float* q_scale, const void* k,
   const auto* q8 = static_cast<const uint8_t*>(q);
   const auto* k8 = static_cast<const uint8_t*>(k);
   if (T < 8) {
-    // one query per workgroup; chunks of 512 or 768 keys (a multiple of four
+    // one query per workgroup; chunks of 256 or 384 keys (a multiple of two
     // waves x 64). Short chunks keep a workgroup's life short next to the
     // kernel's, so ragged rows balance across CUs (measured on the Flash
-    // and Pro decode shapes: 512 / 768 beat 1024 and 2048 there)
+    // and Pro decode shapes: two waves x 128 keys beat four x 128 by 2-3%,
+    // and beat 8 x 64, 8 x 128, 2 x 64 and 1 x 128)
     const int64_t rows = int64_t(B) * T;
     const int64_t per = (int64_t(K) * rows + 2047) / 2048;
     int kpw = int(std::min<int64_t>(std::max<int64_t>(per, 2 * kDecWaves * kDecGroup), 3 * kDecWaves * kDecGroup));
@@ -635,10 +637,10 @@ hipError_t launch_logits(const void* q, const float* q_scale, const void* k,
     const int nch = (K + kpw - 1) / kpw;
     const dim3 grid(unsigned(rows * nch));
     if (fp8)
-      hipLaunchKernelGGL(logits_decode_kernel<true>, grid, dim3(256), 0, stream, q8, q_scale, k8,
+      hipLaunchKernelGGL(logits_decode_kernel<true>, grid, dim3(kDecWaves * 64), 0, stream, q8, q_scale, k8,
                          k_scale, w, limit, logits, T, K, kpw, nch);
     else
-      hipLaunchKernelGGL(logits_decode_kernel<false>, grid, dim3(256), 0, stream, q8, q_scale, k8,
+      hipLaunchKernelGGL(logits_decode_kernel<false>, grid, dim3(kDecWaves * 64), 0, stream, q8, q_scale, k8,
                          k_scale, w, limit, logits, T, K, kpw, nch);
   } else {
     // One query per wave (64 VGPRs of A fragments): 4 waves for bf16 (three
