@@ -27,6 +27,8 @@ class IndexerStep:
         self.topk = topk
         self.kv_fp4, self.kv_scale = kv_fp4, kv_scale
         self.block_table, self.row_seq = block_table, row_seq
+        # the C arguments below hold raw pointers: every tensor they name stays referenced here
+        self.k_cache, self.k_cache_scale = k_cache, k_cache_scale
         lg, ix, ga = outputs if outputs is not None else (None, None, None)
         self.paged = k is None
         if self.paged:

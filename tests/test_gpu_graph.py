@@ -56,3 +56,32 @@ def test_graph_replays_match_eager(pipeline, name):
         ref = oracle.indexer_topk(step.logits.cpu().numpy().reshape(cfg.rows, cfg.K),
                                   x["limit"].reshape(-1), cfg.topk)
         assert np.array_equal(idx, ref)
+
+
+def test_paged_step_keeps_its_key_cache(pipeline):
+    """A paged-key step built from a key cache that nothing else references
+    (bench.py's per-copy clones) still reads that cache after the caller's
+    reference is gone and its old block could be handed out again: the step
+    holds every tensor its C arguments point to."""
+    name = "flash_decode_fp4"
+    x = workloads.inputs(name)
+    cfg = x["cfg"]
+    print(f"[graph] paged step lifetime, config={name}", flush=True)
+    d = workloads.to_device(x)
+
+    def paged(kc, outputs=None):
+        return pipeline(d["q"], None, d["w"], d["limit"], cfg.topk, d["kv_fp4"], d["kv_scale"],
+                        d["block_table"], d["row_seq"], d["q_scale"], None, outputs=outputs,
+                        k_cache=kc, k_cache_scale=d["kc_scale"], K=cfg.K)
+
+    base = paged(d["kc"])
+    base()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in base.outputs()]
+    other = paged(d["kc"].clone(), outputs=base.outputs())   # the only reference to the clone
+    junk = [torch.full_like(d["kc"], 0x77) for _ in range(3)]  # would take a freed block
+    other()
+    torch.cuda.synchronize()
+    del junk
+    for a, b in zip(base.outputs(), eager):
+        assert torch.equal(a, b), "a step on a copy of the key cache differs from the original's"
