@@ -6,7 +6,9 @@
 // selection): among the n = clamp(limit+1, 0, K) valid keys of a row, the
 // min(k, n) largest scores ordered by (score desc, j asc), then -1 padding.
 //
-// One workgroup per row. Rows up to 16384 keys are read from HBM once and
+// Many short rows (at least 1024 rows of at most 4096 keys, k <= 512) run
+// one wave per row (topk_wave_kernel, below); otherwise one workgroup per
+// row. Rows up to 16384 keys are read from HBM once and
 // stay in VGPRs (V values per thread, j = tid + BLOCK*v); longer rows keep a
 // 16384-key prefix in VGPRs and stream the rest once (topk_long_kernel).
 // Scores become order-preserving u32 keys (-0.0 folded to +0.0); key 0 marks
@@ -404,17 +406,19 @@ __device__ __forceinline__ bool finite_key(uint32_t key) {
 }
 
 // Bin of a key, linear in the score over the row's finite range [lo, hi]
-// (s = kBins / (hi - lo)); +-inf clamp to the end bins. Subtraction,
+// (s = NB / (hi - lo)); +-inf clamp to the end bins. Subtraction,
 // multiplication by s >= 0 and truncation all preserve order, so a larger
 // key never lands in a lower bin, which is all the selection relies on.
 // s = 0 (no finite range) sends every finite key to bin 0.
-struct ValueBins {
+template <int NB>
+struct LinearBins {
   float lo, s;
   __device__ __forceinline__ int operator()(uint32_t key) const {
     const float t = (key_value(key) - lo) * s;
-    return t >= float(kBins - 1) ? kBins - 1 : (t > 0.f ? int(t) : 0);
+    return t >= float(NB - 1) ? NB - 1 : (t > 0.f ? int(t) : 0);
   }
 };
+using ValueBins = LinearBins<kBins>;
 
 // Wave 0: turn the bin counts in hist into descending exclusive starts
 // (entries in higher bins) in place, and find the threshold bin b*: the bin holding the need-th largest entry, need =
@@ -711,6 +715,328 @@ __global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ l
   radix_topk<BLOCK, CAP>(sh, x, n, k, idx + row * k);
 }
 
+// ---------------------------------------------------------------------------
+// Many short rows (prefill under a causal limit): one wave per row and no
+// barrier on the common path. The row sits in V registers per lane (16-byte
+// loads, j = 256*i + 4*lane + c). A wave64 VALU instruction holds its SIMD
+// for four cycles and LDS atomics contend across the CU, so the wave first
+// narrows the row in registers:
+//  1. A bound tau with C(tau) = #{scores >= tau} >= min(k, n). The first
+//     probe is the normal quantile of the row's mean and variance at the
+//     wanted tail fraction; further probes are false position on the exact
+//     counts (one compare and add per entry and a wave sum), until C(tau) is
+//     a little above k. Every winner scores >= the k-th largest >= tau.
+//  2. The C(tau) candidates go to a wave-private LDS list (raw score bits
+//     and ~j), each lane's run placed by a wave prefix sum of the lanes'
+//     counts, with no atomics.
+//  3. The bucket path on the list: kWaveBins bins linear in the score over
+//     the candidates' range, a histogram and one descending scan in
+//     registers give the bin b* that holds the k-th largest; the entries of
+//     bins >= b* are scattered to their bins' slots through atomic cursors
+//     (issued back to back: lanes without an entry count into a private
+//     dummy) and ranked inside their bin by comparison, so the output does
+//     not depend on atomic order.
+// LDS operations of one wave complete in program order, so the phases need
+// no barrier. A row with more than kWaveCand candidates after the search
+// (scores crowded by heavy ties, infinities) is left to the radix path,
+// which the whole workgroup runs on it after one barrier, in the same LDS.
+constexpr int kWaveBins = 512;
+constexpr int kWaveCand = 896;   // candidate entries per wave
+constexpr int kWaveRows = 4;     // rows (waves) per workgroup
+constexpr int kWaveMaxK = 512;   // k for which the wave path is used
+constexpr int kWaveFallbackCap = 256;
+constexpr int kWaveSearchSteps = 6;
+
+struct WaveRowShared {
+  __attribute__((aligned(16))) uint32_t hist[kWaveBins + 64];  // + a dummy counter per lane
+  uint64_t cand[kWaveCand];  // the candidates, then the bin slots of the selection
+};
+constexpr size_t kWaveSmem = std::max(sizeof(WaveRowShared) * kWaveRows,
+                                      sizeof(TopkShared<64 * kWaveRows, kWaveFallbackCap>));
+
+__device__ __forceinline__ int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_incl_scan(v), 63); }
+
+// Sum over the wave, uniform result (butterflies in each row of 16 lanes,
+// then the four row sums read as scalars).
+__device__ __forceinline__ float wave_fsum(float v) {
+#define XK_ADD_DPP(C) v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), C, 0xF, 0xF, false));
+  XK_ADD_DPP(kDppQuadSwap1)
+  XK_ADD_DPP(kDppQuadSwap2)
+  XK_ADD_DPP(kDppHalfMirror)
+  XK_ADD_DPP(kDppRowMirror)
+#undef XK_ADD_DPP
+  const auto at = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+  return (at(0) + at(16)) + (at(32) + at(48));
+}
+
+// Upper-tail normal quantile: z with P(Z > z) = p, 0 < p < 1, by the
+// rational approximation of Abramowitz and Stegun (Handbook of Mathematical
+// Functions, formula 26.2.23; absolute error below 4.5e-4). It only seeds
+// the threshold search, so its accuracy affects speed, not results.
+__device__ __forceinline__ float normal_upper_quantile(float p) {
+  const bool upper = p <= 0.5f;
+  const float q = upper ? p : 1.f - p;
+  const float t = sqrtf(-2.f * __logf(q));
+  const float num = fmaf(fmaf(0.010328f, t, 0.802853f), t, 2.515517f);
+  const float den = fmaf(fmaf(fmaf(0.001308f, t, 0.189269f), t, 1.432788f), t, 1.f);
+  const float z = t - num / den;
+  return upper ? z : -z;
+}
+
+// Descending exclusive starts of the bins in place (entries in higher bins),
+// the threshold bin b* (holding the need-th largest entry, need = min(k,
+// entries)) and m, the entries in bins >= b*; b* = kWaveBins and m = 0 for
+// a row with no entry. Lane 0 holds the top bins.
+__device__ __forceinline__ void wave_scan_desc(uint32_t* hist, int k, int& bstar, int& m) {
+  constexpr int PER = kWaveBins / 64;
+  static_assert(PER % 4 == 0, "bins per lane");
+  const int lane = lane_id();
+  const int base = kWaveBins - (lane + 1) * PER;
+  uint32_t c[PER];
+#pragma unroll
+  for (int i = 0; i < PER / 4; ++i) {
+    const u32x4 q4 = *reinterpret_cast<const u32x4*>(&hist[base + 4 * i]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[4 * i + e] = q4[e];
+  }
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sum += int(c[i]);
+  const int incl = wave_incl_scan(sum);
+  const int need = min(k, __builtin_amdgcn_readlane(incl, 63));
+  int run = incl - sum, found = -1, upto = 0;
+#pragma unroll
+  for (int o = 0; o < PER; ++o) {
+    const int i = PER - 1 - o;
+    const int cnt = int(c[i]);
+    c[i] = uint32_t(run);
+    run += cnt;
+    if (found < 0 && run - cnt < need && run >= need) {
+      found = base + i;
+      upto = run;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER / 4; ++i)
+    *reinterpret_cast<u32x4*>(&hist[base + 4 * i]) = u32x4{c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]};
+  const uint64_t fm = __ballot(found >= 0);
+  if (fm == 0ull) {
+    bstar = kWaveBins;
+    m = 0;
+  } else {
+    const int src = __builtin_ctzll(fm);
+    bstar = __builtin_amdgcn_readlane(found, src);
+    m = __builtin_amdgcn_readlane(upto, src);
+  }
+}
+
+// One row by one wave; returns false, having written nothing, when the
+// row keeps more than kWaveCand candidates. K % 4 == 0 and the row 16-byte
+// aligned (the launcher checks).
+template <int V>
+__device__ __forceinline__ bool wave_row_topk(WaveRowShared& sh, const float* __restrict__ x, int n, int k,
+                                              int32_t* __restrict__ orow) {
+  constexpr int G = V / 4;                   // 16-byte loads per lane
+  constexpr int U = (kWaveCand + 63) / 64;   // list entries per lane
+  const int lane = lane_id();
+  const auto rs = make_rsrc(x, ((n + 3) & ~3) * 4);  // whole quads: reads stay inside the row
+  float xs[V];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rs, (256 * i + 4 * lane) * 4, 0, 0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) xs[4 * i + c] = __uint_as_float(r[c]);
+  }
+  // Every loop below runs over all G groups with a uniform test, so xs stays
+  // in registers: groups >= ng hold no entry and are skipped, and the one
+  // group straddling the row's end gets NaN past it (every comparison with
+  // it is false).
+  const int ng = (n + 255) >> 8, nfull = n >> 8;
+  float mn = INFINITY, mx = -INFINITY, s1 = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    if (i < nfull) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float v = xs[4 * i + c];
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+        s1 += v;
+        s2 = fmaf(v, v, s2);
+      }
+    } else if (i < ng) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool in = 256 * i + 4 * lane + c < n;
+        const float v = in ? xs[4 * i + c] : 0.f;
+        xs[4 * i + c] = in ? v : __builtin_nanf("");
+        if (in) {
+          mn = fminf(mn, v);
+          mx = fmaxf(mx, v);
+        }
+        s1 += v;
+        s2 = fmaf(v, v, s2);
+      }
+    }
+  }
+  auto count_lane = [&](float t) {
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      if (i < ng) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) cnt += xs[4 * i + c] >= t ? 1 : 0;
+      }
+    return cnt;
+  };
+  // 1. the bound tau (c = C(tau), mine = this lane's part of it)
+  const int need = min(k, n);
+  const int goal = min(need + (need >> 2) + 32, kWaveCand);
+  float tau = -INFINITY;
+  int c = n, mine = -1;
+  uint32_t kmn = order_key(mn), kmx = order_key(mx);
+  wave_min_max(kmn, kmx);
+  if (c > goal && finite_key(kmn) && finite_key(kmx) && kmn < kmx) {
+    float lo = key_value(kmn), hi = key_value(kmx);
+    int clo = n, chi = 1;  // estimates until measured; they only steer the probes
+    const float aim = float((need + goal) >> 1);
+    const float mean = wave_fsum(s1) / float(n);
+    const float var = fmaxf(wave_fsum(s2) / float(n) - mean * mean, 0.f);
+    float t = fmaf(sqrtf(var), normal_upper_quantile(aim / float(n)), mean);
+#pragma unroll 1
+    for (int step = 0; step < kWaveSearchSteps; ++step) {
+      if (step > 0 || !(t > lo && t < hi)) {
+        // false position on the count, kept inside [1/8, 7/8] of the bracket
+        float f = (float(clo) - aim) / float(max(clo - chi, 1));
+        f = fminf(fmaxf(f, 0.125f), 0.875f);
+        t = fmaf(f, hi, fmaf(-f, lo, lo));  // lo + f (hi - lo), no overflow
+        if (!(t > lo && t < hi)) break;     // the bracket cannot shrink
+      }
+      const int cl = count_lane(t);
+      const int ct = wave_sum(cl);
+      if (ct >= need) {
+        lo = t;
+        clo = ct;
+        tau = t;
+        c = ct;
+        mine = cl;
+        if (c <= goal) break;
+      } else {
+        hi = t;
+        chi = ct;
+      }
+    }
+  }
+  if (c > kWaveCand) return false;  // uniform
+  if (mine < 0) mine = count_lane(tau);  // uniform test (tau = -inf: the valid entries)
+  // 2. the candidates into the list, each lane's run from a wave prefix sum
+  {
+    int at = wave_incl_scan(mine) - mine;
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      if (i < ng) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (xs[4 * i + e] >= tau)
+            sh.cand[at++] = (uint64_t(__float_as_uint(xs[4 * i + e])) << 32) |
+                            uint64_t(~uint32_t(256 * i + 4 * lane + e));
+      }
+  }
+  // 3. bucket path on the list, held U entries per lane as key << 32 | ~j.
+  // The bins span [tau, row maximum] (the row's finite range without a
+  // search), which holds every finite candidate; infinities clamp to the end
+  // bins. The reads are unconditional (U * 64 == kWaveCand), so no load
+  // waits inside a branch.
+  static_assert(U * 64 == kWaveCand, "the list fills whole lane rows");
+  LinearBins<kWaveBins> bins{0.f, 0.f};
+  if (finite_key(kmn) && finite_key(kmx)) {
+    bins.lo = tau > -INFINITY ? tau : key_value(kmn);
+    const float range = key_value(kmx) - bins.lo;
+    bins.s = range > 0.f && range < INFINITY ? float(kWaveBins) / range : 0.f;
+  }
+  uint64_t ent[U];
+  int bin[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t e = sh.cand[64 * u + lane];
+    const float f = __uint_as_float(uint32_t(e >> 32));
+    const float t = (f - bins.lo) * bins.s;
+    ent[u] = (uint64_t(order_key(f)) << 32) | (e & 0xFFFFFFFFull);
+    bin[u] = 64 * u + lane < c ? (t >= float(kWaveBins - 1) ? kWaveBins - 1 : (t > 0.f ? int(t) : 0)) : -1;
+  }
+  static_assert(kWaveBins % 256 == 0, "clear with 16-byte stores");
+#pragma unroll
+  for (int i = 0; i < kWaveBins / 256; ++i)
+    *reinterpret_cast<u32x4*>(&sh.hist[256 * i + 4 * lane]) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (64 * u < c) atomicAdd(&sh.hist[bin[u] >= 0 ? bin[u] : kWaveBins + lane], 1u);  // uniform test
+  int bstar, m;
+  wave_scan_desc(sh.hist, k, bstar, m);
+  // scatter (the list is in registers, its LDS now holds the bin slots):
+  // hist[b] is bin b's cursor; afterwards its end, and hist[b + 1] its start
+  // (every bin above b* is full)
+  uint32_t pos[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    pos[u] = 64 * u < c ? atomicAdd(&sh.hist[bin[u] >= bstar ? bin[u] : kWaveBins + lane], 1u) : 0u;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (64 * u < c && bin[u] >= bstar) sh.cand[pos[u]] = ent[u];
+  // each lane ranks its own scattered entries inside their bins (pos now
+  // holds each bin's end, start its first slot)
+  int start[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int b = max(bin[u], 0);
+    pos[u] = sh.hist[b];
+    start[u] = b == kWaveBins - 1 ? 0 : int(sh.hist[b + 1]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (64 * u < c && bin[u] >= bstar) {
+      int rank = 0;
+      if (int(pos[u]) - start[u] > 1)  // a bin of one entry holds only this one
+        for (int q = start[u]; q < int(pos[u]); ++q) rank += sh.cand[q] > ent[u] ? 1 : 0;
+      if (start[u] + rank < k) orow[start[u] + rank] = int32_t(~uint32_t(ent[u] & 0xFFFFFFFFull));
+    }
+  }
+  for (int p = m + lane; p < k; p += 64) orow[p] = -1;
+  return true;
+}
+
+// kWaveRows rows per workgroup, last to first (the longest rows first under
+// a causal limit); rows the wave path gives back are finished by the
+// workgroup's radix path.
+template <int V>
+__global__ __launch_bounds__(64 * kWaveRows, 4) void topk_wave_kernel(const float* __restrict__ logits,
+                                                                   const int32_t* __restrict__ limit,
+                                                                   int32_t* __restrict__ idx, int R, int K,
+                                                                   int k) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kWaveSmem];
+  __shared__ int redo[kWaveRows];
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  const int64_t row = int64_t(R) - 1 - (int64_t(blockIdx.x) * kWaveRows + wave);
+  int n = 0;
+  bool done = true;
+  if (row >= 0) {
+    n = limit ? max(0, min(limit[row], K - 1) + 1) : K;
+    n = __builtin_amdgcn_readfirstlane(n);
+    done = wave_row_topk<V>(reinterpret_cast<WaveRowShared*>(smem)[wave], logits + row * K, n, k, idx + row * k);
+  }
+  if (lane_id() == 0) redo[wave] = done ? -1 : n;
+  __syncthreads();
+  auto& sh = *reinterpret_cast<TopkShared<64 * kWaveRows, kWaveFallbackCap>*>(smem);
+#pragma unroll 1
+  for (int w = 0; w < kWaveRows; ++w) {
+    const int nw = redo[w];  // uniform over the workgroup
+    if (nw < 0) continue;
+    const int64_t rw = int64_t(R) - 1 - (int64_t(blockIdx.x) * kWaveRows + w);
+    radix_topk<64 * kWaveRows, kWaveFallbackCap>(sh, logits + rw * K, nw, k, idx + rw * k);
+    __syncthreads();
+  }
+}
+
 // Append the entries u of a chunk with take(u) to the LDS list ckey / cj
 // (key_at / j_at are evaluated for taken entries only). The wave takes all
 // U ballots first and claims room for all its entries with one LDS atomic,
@@ -966,10 +1292,25 @@ hipError_t launch_one(const float* logits, const int32_t* limit, int32_t* idx, i
   return hipGetLastError();
 }
 
+template <int V>
+hipError_t launch_wave(const float* logits, const int32_t* limit, int32_t* idx, int R, int K, int k,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL(topk_wave_kernel<V>, dim3(unsigned((R + kWaveRows - 1) / kWaveRows)), dim3(64 * kWaveRows),
+                     0, stream, logits, limit, idx, R, K, k);
+  return hipGetLastError();
+}
+
+constexpr int kWaveMinRows = 1024;  // fewer rows leave most SIMDs idle: a workgroup per row instead
+
 }  // namespace
 
 hipError_t launch_topk(const float* logits, const int32_t* limit, int32_t* idx, int R, int K,
                        int k, hipStream_t stream) {
+  const bool wave_path = R >= kWaveMinRows && k <= kWaveMaxK && K % 4 == 0 &&
+                         reinterpret_cast<uintptr_t>(logits) % 16 == 0;
+  if (wave_path && K <= 1024) return launch_wave<16>(logits, limit, idx, R, K, k, stream);
+  if (wave_path && K <= 2048) return launch_wave<32>(logits, limit, idx, R, K, k, stream);
+  if (wave_path && K <= 4096) return launch_wave<64>(logits, limit, idx, R, K, k, stream);
   if (K <= 256 * 4) return launch_one<256, 4, 256>(logits, limit, idx, R, K, k, stream);
   if (K <= 256 * 16) return launch_one<256, 16, 256>(logits, limit, idx, R, K, k, stream);
   if (K <= 1024 * 8) return launch_one<1024, 8, 1024>(logits, limit, idx, R, K, k, stream);
