@@ -40,10 +40,12 @@ __global__ __launch_bounds__(256) void mxfp4_gather_kernel(
   const int64_t s = slot0 + lane;
   int tok = -1;
   if (lane < 4 * STEPS && s < n_slots) {
+    // the row's sequence does not depend on sel_pos: both loads go out
+    // together, leaving two dependent hops (table, then data)
+    const int64_t row = s / k;
+    const int seq = row_seq ? row_seq[row] : int(row);
     const int p = sel_pos[s];
     if (p >= 0) {
-      const int64_t row = s / k;
-      const int seq = row_seq ? row_seq[row] : int(row);
       const int blk = block_table[int64_t(seq) * MB + (p >> bs_log2)];
       tok = (blk << bs_log2) + (p & ((1 << bs_log2) - 1));
     }
