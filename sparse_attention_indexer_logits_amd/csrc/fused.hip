@@ -25,6 +25,7 @@ constexpr int kMaxSlots = 16384;     // candidate slots per row (the select kern
 constexpr int kMinKeysPerIndex = 16;  // K / k below this: filtering keeps most keys
 constexpr int kMinQueryBlocks = 256;  // one workgroup per CU at least
 constexpr int kMaxRecomputeBlocks = 64;
+constexpr int kMaxRowKeys = 1 << 22;  // one chunk's key bytes stay in a buffer descriptor's range
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -37,7 +38,8 @@ FusedPlan plan_fused(int B, int T, int K, int k, bool fp8) {
   const int QB = fp8 ? 8 : 4;  // queries per workgroup of the prefill kernel
   p.nqb = (T + QB - 1) / QB;
   const int64_t qblocks = int64_t(p.nqb) * B;
-  p.fused = T >= 8 && qblocks >= kMinQueryBlocks && int64_t(K) >= int64_t(kMinKeysPerIndex) * k;
+  p.fused = T >= 8 && qblocks >= kMinQueryBlocks && int64_t(K) >= int64_t(kMinKeysPerIndex) * k &&
+            K <= kMaxRowKeys;
   if (!p.fused) {
     p.off_logits = 0;
     p.bytes = align256(size_t(R) * size_t(K) * 4);

@@ -384,9 +384,16 @@ __global__ __launch_bounds__(kPagedWaves * 64, 2) void logits_paged_kernel(
 }
 
 // prefill grid: 1-D over (query blocks, longest causal rows first) x B x
-// (key chunks). NW waves x QW queries per workgroup share double-buffered
-// 64-key LDS tiles; the next tile's global loads are issued before this
-// tile's MFMAs and stored to LDS after them, one barrier per tile.
+// (key chunks). NW waves, one query each, share 64-key tiles that the
+// buffer unit writes straight into LDS (buffer_load ... lds, 16 bytes per
+// lane): three tile buffers rotate, so while a tile is scored the next one
+// has landed and the one after it is in flight, with one barrier per tile
+// and no tile data passing through registers. The LDS rows are unpadded;
+// each 16-byte piece is stored at its index XOR a row-dependent mask, so a
+// fragment read (16 keys x one 16-byte piece) still hits 16 distinct
+// 16-byte bank groups. Within a tile the next subtile's B fragments are
+// read before the current subtile's MFMAs, and a subtile's ReLU/weight
+// epilogue is issued alongside the next subtile's MFMAs.
 //
 // With NL > 0 the kernel writes no logits: it is the first half of the
 // fused logits -> top-k path, one query per wave. Each lane keeps the NL
@@ -400,6 +407,9 @@ __global__ __launch_bounds__(kPagedWaves * 64, 2) void logits_paged_kernel(
 // (entries past it are dropped); the selection kernel then has the row
 // recomputed.
 constexpr int kPrefillTile = 64;
+// keys per prefill workgroup chunk are capped so that a chunk's key bytes
+// fit a buffer descriptor's 32-bit range
+constexpr int kPrefillMaxChunk = 1 << 22;
 
 // minimum over the wave, uniform result (DPP butterflies in each row of 16
 // lanes, then the four rows read as scalars)
@@ -415,7 +425,30 @@ __device__ __forceinline__ float wave_min(float v) {
   return fminf(fminf(lane_v(0), lane_v(16)), fminf(lane_v(32), lane_v(48)));
 }
 
-template <bool FP8, int QW, int NW, int NL>
+// waits until at most N vector-memory operations of this wave are
+// outstanding, then joins the workgroup barrier; the asm's memory clobber
+// keeps the compiler from moving memory accesses across it
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// N loads of 16 bytes per lane from `rs` (at this lane's offsets) straight
+// into LDS: load i fills the 1 KB at dst + i*1024, lane l its 16 bytes at l*16.
+// (The 16-byte form is a gfx950 instruction that the host pass's view of the
+// device target lacks, so the host pass sees an empty body.)
+template <int N>
+__device__ __forceinline__ void lds_load_1k(__amdgpu_buffer_rsrc_t rs, uint8_t* dst, const int (&voff)[N]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
+                                             voff[i], 0, 0, 0);
+#endif
+}
+
+template <bool FP8, int NW, int NL>
 __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ k, const float* __restrict__ k_scale,
@@ -423,16 +456,22 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
     float* __restrict__ out, CandidateOut co, int B, int T, int K, int keys_per_wg, int n_chunks,
     int n_qblocks) {
   using M = Mma16<FP8>;
+  using Frag = typename M::Frag;
   constexpr bool kCand = NL > 0;
-  static_assert(!kCand || QW == 1, "the candidate epilogue keeps one query per wave");
-  constexpr int QB = QW * NW;  // queries per workgroup
-  constexpr int kRowBytes = kHeadDim * M::kElemBytes;
-  constexpr int kPitch = kRowBytes + 16;  // 16-byte pad: conflict-free fragment reads
-  constexpr int kChunks = kRowBytes / 16;
-  constexpr int kThreads = NW * 64;
-  constexpr int kPer = kPrefillTile * kChunks / kThreads;  // 16-byte pieces per thread per tile
-  static_assert(kPer >= 1 && kPrefillTile * kChunks % kThreads == 0, "tile split");
-  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kPrefillTile * kPitch];
+  constexpr int QB = NW;  // queries per workgroup, one per wave
+  constexpr int kRowBytes = kHeadDim * M::kElemBytes;        // 256 (bf16) or 128 (fp8)
+  constexpr int kTileBytes = kPrefillTile * kRowBytes;
+  constexpr int kDma = kTileBytes / (NW * 64 * 16);           // 16-byte LDS loads per lane per tile
+  static_assert(kDma >= 1 && kTileBytes % (NW * 64 * 16) == 0, "tile split");
+  // vector-memory operations a wave issues in a step after the next tile's
+  // loads: the following tile's loads, the score store and (fp8) the key
+  // scales
+  constexpr int kAfter = kDma + 1 + (FP8 ? 1 : 0);
+  // three tile buffers as separate arrays, so the compiler can tell the
+  // buffer being read from the ones being written
+  __shared__ __attribute__((aligned(16))) uint8_t tile0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tile1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tile2[kTileBytes];
 
   // the wave index in a scalar register: per-wave values derived from it
   // (rows, buffer descriptors) then stay scalar
@@ -452,62 +491,71 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
   const int j_end = min(j_begin + keys_per_wg, K);
   const int c_end = min(j_end, blk_lim + 1);
 
-  int q_end[QW];
-  int64_t bt[QW];
-  bool qvalid[QW];
-#pragma unroll
-  for (int qi = 0; qi < QW; ++qi) {
-    const int t = qb * QB + QW * wave + qi;
-    qvalid[qi] = t < T;
-    bt[qi] = b * T + (qvalid[qi] ? t : 0);
-    const int lim = qvalid[qi] ? clamp_limit(limit, bt[qi], K) : -1;
-    q_end[qi] = min(j_end, lim + 1);
-    if (!kCand && qvalid[qi]) {
-      float* orow = out + bt[qi] * K;
-      for (int j = max(j_begin, lim + 1) + lane; j < j_end; j += 64) orow[j] = -INFINITY;
-    }
+  const int t_q = qb * QB + wave;
+  const bool qvalid = t_q < T;
+  const int64_t bt = b * T + (qvalid ? t_q : 0);
+  const int lim = qvalid ? clamp_limit(limit, bt, K) : -1;
+  const int q_end = min(j_end, lim + 1);
+  if (!kCand && qvalid) {
+    float* orow = out + bt * K;
+    for (int j = max(j_begin, lim + 1) + lane; j < j_end; j += 64) orow[j] = -INFINITY;
   }
   if (kCand && blockIdx.x == 0 && threadIdx.x < 2) co.ctrl[threadIdx.x] = 0;  // queue counters
   if (c_end <= j_begin) {  // uniform over the workgroup
-    if (kCand && qvalid[0] && lane == 0) co.count[bt[0] * n_chunks + chunk] = 0;
+    if (kCand && qvalid && lane == 0) co.count[bt * n_chunks + chunk] = 0;
     return;
   }
 
-  const uint8_t* kseq = k + b * int64_t(K) * kRowBytes;
-  const float* skseq = FP8 ? k_scale + b * int64_t(K) : nullptr;
-  // Two tiles in flight through registers: at the start of tile t the free
-  // register buffer starts loading tile t+2; at its end the other buffer,
-  // holding tile t+1 (issued at the start of tile t-1), goes to LDS. Loads
-  // clamp to the last key and stores go through range-checked buffers, so
-  // the loop has no data-dependent memory branch and the waits stay exact.
-  u32x4 pre[2][kPer];
-  float skp[2];  // fp8: key scale of key (tile start + lane)
-  auto gload = [&](int j0, u32x4 (&dst)[kPer], float& sk) {
+  // the chunk's scored keys: loads at or past c_end read 0 without a memory
+  // access (those keys' scores are never stored)
+  const int n_tiles = (c_end - j_begin + kPrefillTile - 1) / kPrefillTile;
+  const int valid_bytes = (c_end - j_begin) * kRowBytes;
+  const uint8_t* kchunk = k + (b * int64_t(K) + j_begin) * kRowBytes;
+  const auto srs = make_rsrc(FP8 ? k_scale + b * int64_t(K) + j_begin : nullptr, FP8 ? (c_end - j_begin) * 4 : 0);
+  // piece p of LDS row `row` holds the row's 16-byte piece p ^ swz(row);
+  // bf16 rows (16 pieces, 256 B) XOR with row % 16, fp8 rows (8 pieces,
+  // 128 B, two rows per 256 B) with (row / 2) % 8
+  auto swz = [](int row) { return FP8 ? (row >> 1) & 7 : row & 15; };
+  constexpr int kPieces = kRowBytes / 16;
+  // this lane's source offset (within a tile) for each of its LDS loads;
+  // load i of wave w fills LDS bytes [(w*kDma + i)*1024, +1024), lane l
+  // the 16 bytes at l*16 of that range
+  int voff[kDma];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = int(threadIdx.x) + kThreads * i;
-      const int row = min(j0 + c / kChunks, K - 1);
-      dst[i] = *reinterpret_cast<const u32x4*>(kseq + int64_t(row) * kRowBytes + (c % kChunks) * 16);
-    }
-    if constexpr (FP8) sk = skseq[min(j0 + lane, K - 1)];
-  };
-  auto lds_put = [&](uint8_t* dst, const u32x4 (&src)[kPer]) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = int(threadIdx.x) + kThreads * i;
-      *reinterpret_cast<u32x4*>(dst + (c / kChunks) * kPitch + (c % kChunks) * 16) = src[i];
-    }
-  };
-  // logits: this chunk's outputs of each query, up to its limit; candidates:
-  // the (row, chunk) region
-  __amdgpu_buffer_rsrc_t ors[QW];
-#pragma unroll
-  for (int qi = 0; qi < QW; ++qi) {
-    if constexpr (kCand)
-      ors[qi] = make_rsrc(co.cand + (bt[qi] * n_chunks + chunk) * int64_t(co.capc), co.capc * 8);
-    else
-      ors[qi] = make_rsrc(out + bt[qi] * K + j_begin, max(0, q_end[qi] - j_begin) * 4);
+  for (int i = 0; i < kDma; ++i) {
+    const int o = (wave * kDma + i) * 1024 + lane * 16;
+    const int row = o / kRowBytes, p = (o % kRowBytes) / 16;
+    voff[i] = row * kRowBytes + (p ^ swz(row)) * 16;
   }
+  auto dma = [&](uint8_t* dst, int tix) {
+    const int off = tix * kTileBytes;  // scalar
+    lds_load_1k<kDma>(make_rsrc(kchunk + off, max(0, valid_bytes - off)), dst + wave * kDma * 1024, voff);
+  };
+  // LDS offsets (within a subtile) of this lane's fragment pieces: key r of
+  // the subtile, pieces named by Mma16::dofs
+  constexpr int kRd = FP8 ? 2 : M::kSteps;
+  int rd[kRd];
+#pragma unroll
+  for (int i = 0; i < kRd; ++i) {
+    const int piece = FP8 ? 2 * g + i : (M::dofs(i, g) * M::kElemBytes) / 16;
+    rd[i] = r * kRowBytes + ((piece ^ swz(r)) % kPieces) * 16;
+  }
+  auto frag_load = [&](const uint8_t* buf, int st, Frag (&f)[M::kSteps]) {
+    const uint8_t* base = buf + st * 16 * kRowBytes;
+    if constexpr (FP8) {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(base + rd[0]);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(base + rd[1]);
+      f[0] = Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+#pragma unroll
+      for (int s = 0; s < M::kSteps; ++s) f[s] = M::load(base + rd[s]);
+    }
+  };
+
+  // logits: this query's outputs of the chunk, up to its limit;
+  // candidates: the (row, chunk) region
+  const auto ors = kCand ? make_rsrc(co.cand + (bt * n_chunks + chunk) * int64_t(co.capc), co.capc * 8)
+                         : make_rsrc(out + bt * K + j_begin, max(0, q_end - j_begin) * 4);
   float best[kCand ? NL : 1];  // descending; -inf until the lane has seen NL keys
 #pragma unroll
   for (int i = 0; i < (kCand ? NL : 1); ++i) best[i] = -INFINITY;
@@ -515,77 +563,74 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
   int cnt = 0;            // candidates this wave has emitted (uniform)
 
   // q fragments and head weights are loaded before the key tiles: memory
-  // waits count in issue order, so waiting for them (at their first use,
-  // inside the loop) must not also wait for tiles in flight
-  Query16<FP8> qr[QW];
-#pragma unroll
-  for (int qi = 0; qi < QW; ++qi) {
-    if (qvalid[qi])
-      qr[qi].load(q + bt[qi] * (kHeads * kRowBytes), w + bt[qi] * kHeads,
-                  FP8 ? q_scale + bt[qi] * kHeads : nullptr, lane);
-    else
-      qr[qi].zero();
-  }
-  gload(j_begin, pre[0], skp[0]);
-  gload(j_begin + kPrefillTile, pre[1], skp[1]);
-  lds_put(tile[0], pre[0]);
-  __syncthreads();
+  // waits count in issue order, so waiting for them (at their first use)
+  // must not also wait for tiles in flight
+  Query16<FP8> qr;
+  if (qvalid)
+    qr.load(q + bt * (kHeads * kRowBytes), w + bt * kHeads, FP8 ? q_scale + bt * kHeads : nullptr, lane);
+  else
+    qr.zero();
+  dma(tile0, 0);
+  dma(tile1, 1);
+  wait_vm_barrier<kDma>();  // tile 0 has landed (this wave's part), then all waves' parts
 
-  // tile at j0 in tile[cur]; `fill` (free) starts loading the tile two
-  // ahead, `hold` (the next tile, issued a step earlier) goes to LDS at the
-  // end. The same memory operations run every step: refills past the chunk
-  // read the last key again and stores past a query's limit (or, for
-  // candidates, of keys that do not qualify) are dropped.
-  auto step = [&](int j0, int cur, u32x4 (&fill)[kPer], float& sk_fill, const u32x4 (&hold)[kPer]) {
-    const float sk = sk_fill;  // this tile's key scales, loaded with it
-    gload(j0 + 2 * kPrefillTile, fill, sk_fill);
-    float p[QW][4];
+  // score tile tix (in `cur`) after starting tile tix + 2 (into `nxt`,
+  // the buffer every wave finished reading before the last barrier)
+  auto step = [&](const uint8_t* cur, uint8_t* nxt, int tix) {
+    if (kCand && (tix & 7) == 6) tau = fmaxf(tau, wave_min(best[kCand ? NL - 1 : 0]));
+    const int j0 = j_begin + tix * kPrefillTile;
+    float sk = 1.f;  // fp8: scale of key j0 + lane
+    if constexpr (FP8)
+      sk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, (tix * kPrefillTile + lane) * 4, 0, 0));
+    dma(nxt, tix + 2);
+    Frag bf[2][M::kSteps];
+    f32x4 acc[2][4];
+    float p[4];
+    frag_load(cur, 0, bf[0]);
+    qr.mma(bf[0], acc[0]);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      typename M::Frag bf[M::kSteps];
-      const uint8_t* lrow = tile[cur] + (16 * st + r) * kPitch;
-#pragma unroll
-      for (int s = 0; s < M::kSteps; ++s) bf[s] = M::load(lrow + M::dofs(s, g) * M::kElemBytes);
-#pragma unroll
-      for (int qi = 0; qi < QW; ++qi) p[qi][st] = qr[qi].partial(bf);
-    }
-#pragma unroll
-    for (int qi = 0; qi < QW; ++qi) {
-      const float tot = subtile_total(p[qi], lane);
-      const float sc = FP8 ? tot * sk : tot;
-      if constexpr (kCand) {
-        const int j = j0 + lane;
-        const bool valid = j < q_end[qi];
-        const float sv = valid ? sc : -INFINITY;
-#pragma unroll
-        for (int i = NL - 1; i > 0; --i) best[i] = __builtin_amdgcn_fmed3f(best[i], best[i - 1], sv);
-        best[0] = fmaxf(best[0], sv);
-        const bool pass = valid && sc >= tau;
-        const uint64_t m = __ballot(pass);
-        const int rank = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{order_key(sc), uint32_t(j)}, ors[qi],
-                                              pass ? (cnt + rank) * 8 : co.capc * 8, 0, 0);
-        cnt += __popcll(m);
-      } else {
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors[qi],
-                                              (j0 - j_begin + lane) * 4, 0, 0);
+      if (st < 3) {
+        frag_load(cur, st + 1, bf[(st + 1) & 1]);
+        qr.mma(bf[(st + 1) & 1], acc[(st + 1) & 1]);
       }
+      p[st] = qr.epilogue(acc[st & 1]);
     }
-    lds_put(tile[cur ^ 1], hold);
-    __syncthreads();
+    const float tot = subtile_total(p, lane);
+    const float sc = FP8 ? tot * sk : tot;
+    if constexpr (kCand) {
+      const int j = j0 + lane;
+      const bool valid = j < q_end;
+      const float sv = valid ? sc : -INFINITY;
+#pragma unroll
+      for (int i = NL - 1; i > 0; --i) best[i] = __builtin_amdgcn_fmed3f(best[i], best[i - 1], sv);
+      best[0] = fmaxf(best[0], sv);
+      const bool pass = valid && sc >= tau;
+      const uint64_t m = __ballot(pass);
+      const int rank = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{order_key(sc), uint32_t(j)}, ors,
+                                            pass ? (cnt + rank) * 8 : co.capc * 8, 0, 0);
+      cnt += __popcll(m);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors,
+                                            (tix * kPrefillTile + lane) * 4, 0, 0);
+    }
+    // tile tix + 1 has landed: this wave's part (only tile tix + 2's loads,
+    // the store and the scale load may still be outstanding), then all waves'
+    wait_vm_barrier<kAfter>();
   };
-  // Both steps of an iteration always run (an odd last tile is followed by
-  // one redundant tile whose stores are all dropped): with no loop exit
-  // between a refill and its use, the compiler cannot sink the refill next
-  // to that use, which would expose its latency. Candidates: every fourth
-  // iteration the wave raises tau to its lists' minimum.
-  int it = 0;
-  for (int j0 = j_begin; j0 < c_end; j0 += 2 * kPrefillTile, ++it) {
-    if (kCand && (it & 3) == 3) tau = fmaxf(tau, wave_min(best[kCand ? NL - 1 : 0]));
-    step(j0, 0, pre[0], skp[0], pre[1]);
-    step(j0 + kPrefillTile, 1, pre[1], skp[1], pre[0]);
+  // Candidates: every eighth tile the wave raises tau to its lists' minimum.
+  for (int tix = 0;;) {
+    step(tile0, tile2, tix);
+    if (++tix >= n_tiles) break;
+    step(tile1, tile0, tix);
+    if (++tix >= n_tiles) break;
+    step(tile2, tile1, tix);
+    if (++tix >= n_tiles) break;
   }
-  if (kCand && qvalid[0] && lane == 0) co.count[bt[0] * n_chunks + chunk] = cnt;
+  // no LDS load may still be in flight when the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0);
+  if (kCand && qvalid && lane == 0) co.count[bt * n_chunks + chunk] = cnt;
 }
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -652,15 +697,16 @@ hipError_t launch_logits(const void* q, const float* q_scale, const void* k,
     const int64_t qblocks = int64_t(nqb) * B;
     // key chunks re-read the block's q, so split keys only when there are
     // fewer than ~1024 query blocks
-    const int nkc = int(std::max<int64_t>(1, (1024 + qblocks - 1) / qblocks));
+    const int nkc = int(std::max<int64_t>({1, (1024 + qblocks - 1) / qblocks,
+                                           (int64_t(K) + kPrefillMaxChunk - 1) / kPrefillMaxChunk}));
     const int kpw = round_up((K + nkc - 1) / nkc, kPrefillTile);
     const int nch = (K + kpw - 1) / kpw;
     const dim3 grid(unsigned(int64_t(nch) * qblocks));
     if (fp8)
-      hipLaunchKernelGGL((logits_prefill_kernel<true, 1, 8, 0>), grid, dim3(8 * 64), 0, stream, q8,
+      hipLaunchKernelGGL((logits_prefill_kernel<true, 8, 0>), grid, dim3(8 * 64), 0, stream, q8,
                          q_scale, k8, k_scale, w, limit, logits, CandidateOut{}, B, T, K, kpw, nch, nqb);
     else
-      hipLaunchKernelGGL((logits_prefill_kernel<false, 1, 4, 0>), grid, dim3(4 * 64), 0, stream, q8,
+      hipLaunchKernelGGL((logits_prefill_kernel<false, 4, 0>), grid, dim3(4 * 64), 0, stream, q8,
                          q_scale, k8, k_scale, w, limit, logits, CandidateOut{}, B, T, K, kpw, nch, nqb);
   }
   return hipGetLastError();
@@ -677,7 +723,7 @@ hipError_t launch_logits_candidates(const void* q, const float* q_scale, const v
     constexpr bool F = decltype(fp8_tag)::value;
     constexpr int NL = decltype(nl_tag)::value;
     constexpr int NW = F ? 8 : 4;
-    hipLaunchKernelGGL((logits_prefill_kernel<F, 1, NW, NL>), grid, dim3(NW * 64), 0, stream, q8, q_scale,
+    hipLaunchKernelGGL((logits_prefill_kernel<F, NW, NL>), grid, dim3(NW * 64), 0, stream, q8, q_scale,
                        k8, k_scale, w, limit, nullptr, co, B, T, K, p.kpw, p.nch, p.nqb);
   };
   using T4 = std::integral_constant<int, 4>;

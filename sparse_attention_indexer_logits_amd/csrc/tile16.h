@@ -14,8 +14,8 @@ namespace xk {
 // across the four M-tiles. That keeps the per-query state small (16 head
 // weights + 16 accumulators per lane) so a wave can own QW queries and each
 // B fragment read from LDS feeds 4*QW MFMAs. After the four 16-key subtiles
-// of a 64-key tile, a 3-shuffle butterfly leaves lane l with the full score
-// of key l, so stores are 64 consecutive floats.
+// of a 64-key tile, three lane swaps and adds leave lane l with the full
+// score of key l, so stores are 64 consecutive floats.
 template <bool FP8>
 struct Mma16;
 
@@ -77,15 +77,19 @@ struct Query16 {
       for (int i = 0; i < 4; ++i) wr[mt][i] = 0.f;
     }
   }
-  // this lane's 16-head partial score of key (lane % 16) of a 16-key subtile
-  __device__ float partial(const typename M::Frag (&b)[M::kSteps]) const {
-    f32x4 acc[4];
+  // the four M-tiles' accumulators of a 16-key subtile (steps outermost, so
+  // consecutive MFMAs are independent)
+  __device__ void mma(const typename M::Frag (&b)[M::kSteps], f32x4 (&acc)[4]) const {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < M::kSteps; ++s) acc[mt] = M::mma(a[mt][s], b[s], acc[mt]);
-    }
+    for (int s = 0; s < M::kSteps; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt] = M::mma(a[mt][s], b[s], acc[mt]);
+  }
+  // this lane's 16-head partial score (ReLU, head weight, sum) of key
+  // (lane % 16) from the subtile's accumulators
+  __device__ float epilogue(const f32x4 (&acc)[4]) const {
     float p0 = 0.f, p1 = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -96,20 +100,30 @@ struct Query16 {
     }
     return p0 + p1;
   }
+  // this lane's 16-head partial score of key (lane % 16) of a 16-key subtile
+  __device__ float partial(const typename M::Frag (&b)[M::kSteps]) const {
+    f32x4 acc[4];
+    mma(b, acc);
+    return epilogue(acc);
+  }
 };
 
 // p[st] = this lane's partial for key 16*st + lane%16; returns the full score
-// of key `lane` (sum over the four lane groups, routed by a butterfly).
+// of key `lane` (sum over the four lane groups).
 __device__ __forceinline__ float subtile_total(const float (&p)[4], int lane) {
-  const bool up32 = lane >= 32, up16 = (lane & 16) != 0;
-  // xor 32: lower half keeps subtiles 0,1; upper half keeps 2,3
-  const float k0 = up32 ? p[2] : p[0], k1 = up32 ? p[3] : p[1];
-  const float s0 = up32 ? p[0] : p[2], s1 = up32 ? p[1] : p[3];
-  const float a0 = k0 + __shfl_xor(s0, 32);
-  const float a1 = k1 + __shfl_xor(s1, 32);
-  // xor 16: even groups keep the first, odd groups the second
-  const float keep = up16 ? a1 : a0, send = up16 ? a0 : a1;
-  return keep + __shfl_xor(send, 16);
+  // v_permlane32_swap: lanes 32-63 of the first operand trade places with
+  // lanes 0-31 of the second. After swapping (p0, p2) the lower half holds
+  // subtile 0 of both halves and the upper half subtile 2 of both, so one add
+  // sums each key over the two halves (likewise p1, p3).
+  const auto x02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
+  const auto x13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
+  const float a0 = __uint_as_float(x02[0]) + __uint_as_float(x02[1]);
+  const float a1 = __uint_as_float(x13[0]) + __uint_as_float(x13[1]);
+  // v_permlane16_swap does the same for 16-lane groups within each half:
+  // even groups end with a0 of both groups, odd groups with a1
+  const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
+  (void)lane;
+  return __uint_as_float(y[0]) + __uint_as_float(y[1]);
 }
 
 }  // namespace xk
