@@ -410,6 +410,7 @@ constexpr int kPrefillTile = 64;
 // keys per prefill workgroup chunk are capped so that a chunk's key bytes
 // fit a buffer descriptor's 32-bit range
 constexpr int kPrefillMaxChunk = 1 << 22;
+constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 
 // minimum over the wave, uniform result (DPP butterflies in each row of 16
 // lanes, then the four rows read as scalars)
@@ -477,10 +478,16 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
   // (rows, buffer descriptors) then stay scalar
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r = lane & 15;
-  const int chunk = int(blockIdx.x % n_chunks);
-  const int rest = int(blockIdx.x / n_chunks);
-  const int64_t b = rest % B;
-  const int qb = n_qblocks - 1 - rest / B;  // longest causal rows first
+  // Workgroup i runs on XCD i % 8. Eight consecutive workgroups take the
+  // same key chunk of eight consecutive (sequence, query block) units, so
+  // every XCD gets an equal share of each chunk; units run longest causal
+  // rows first.
+  const int x8 = int(blockIdx.x % kXcds), grp = int(blockIdx.x / kXcds);
+  const int chunk = grp % n_chunks;
+  const int unit = (grp / n_chunks) * kXcds + x8;
+  if (unit >= n_qblocks * B) return;  // uniform: the grid is rounded up to whole groups
+  const int64_t b = unit % B;
+  const int qb = n_qblocks - 1 - unit / B;
   int blk_lim = -1;
 #pragma unroll
   for (int i = 0; i < QB; ++i) {
@@ -634,6 +641,7 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
 }
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
+int64_t round_up64(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 }  // namespace
 
@@ -701,7 +709,7 @@ hipError_t launch_logits(const void* q, const float* q_scale, const void* k,
                                            (int64_t(K) + kPrefillMaxChunk - 1) / kPrefillMaxChunk}));
     const int kpw = round_up((K + nkc - 1) / nkc, kPrefillTile);
     const int nch = (K + kpw - 1) / kpw;
-    const dim3 grid(unsigned(int64_t(nch) * qblocks));
+    const dim3 grid(unsigned(int64_t(nch) * round_up64(qblocks, kXcds)));
     if (fp8)
       hipLaunchKernelGGL((logits_prefill_kernel<true, 8, 0>), grid, dim3(8 * 64), 0, stream, q8,
                          q_scale, k8, k_scale, w, limit, logits, CandidateOut{}, B, T, K, kpw, nch, nqb);
@@ -718,7 +726,7 @@ hipError_t launch_logits_candidates(const void* q, const float* q_scale, const v
                                     bool fp8, hipStream_t stream) {
   const auto* q8 = static_cast<const uint8_t*>(q);
   const auto* k8 = static_cast<const uint8_t*>(k);
-  const dim3 grid(unsigned(int64_t(p.nch) * p.nqb * B));
+  const dim3 grid(unsigned(int64_t(p.nch) * round_up64(int64_t(p.nqb) * B, kXcds)));
   auto go = [&](auto fp8_tag, auto nl_tag) {
     constexpr bool F = decltype(fp8_tag)::value;
     constexpr int NL = decltype(nl_tag)::value;
