@@ -454,8 +454,7 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ k, const float* __restrict__ k_scale,
     const float* __restrict__ w, const int32_t* __restrict__ limit,
-    float* __restrict__ out, CandidateOut co, int B, int T, int K, int keys_per_wg, int n_chunks,
-    int n_qblocks) {
+    float* __restrict__ out, CandidateOut co, int B, int T, int K, int n_chunks, int n_qblocks) {
   using M = Mma16<FP8>;
   using Frag = typename M::Frag;
   constexpr bool kCand = NL > 0;
@@ -494,8 +493,16 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
     const int ti = qb * QB + i;
     if (ti < T) blk_lim = max(blk_lim, clamp_limit(limit, b * T + ti, K));
   }
-  const int j_begin = chunk * keys_per_wg;
-  const int j_end = min(j_begin + keys_per_wg, K);
+  // The block's own scored range [0, row_end) is split into n_chunks parts
+  // of equal tile counts: under a causal limit the parts shrink with the
+  // row, so no workgroup is left with an empty fixed key range and long and
+  // short rows are cut alike. The last part also covers the keys past the
+  // block's limit (their -inf fill).
+  const int row_end = min(K, blk_lim + 1);
+  const int nt_all = (max(row_end, 0) + kPrefillTile - 1) / kPrefillTile;
+  const int t_lo = int(int64_t(nt_all) * chunk / n_chunks), t_hi = int(int64_t(nt_all) * (chunk + 1) / n_chunks);
+  const int j_begin = t_lo * kPrefillTile;
+  const int j_end = chunk == n_chunks - 1 ? K : min(K, t_hi * kPrefillTile);
   const int c_end = min(j_end, blk_lim + 1);
 
   const int t_q = qb * QB + wave;
@@ -703,19 +710,20 @@ hipError_t launch_logits(const void* q, const float* q_scale, const void* k,
     const int QB = fp8 ? 8 : 4;
     const int nqb = (T + QB - 1) / QB;
     const int64_t qblocks = int64_t(nqb) * B;
-    // key chunks re-read the block's q, so split keys only when there are
-    // fewer than ~1024 query blocks
-    const int nkc = int(std::max<int64_t>({1, (1024 + qblocks - 1) / qblocks,
+    // every block's row in at least two parts (under a causal limit rows
+    // of 1 to K/64 tiles then give workgroups of half those sizes, which
+    // balance better; both parts of a block run on one XCD, so its second q
+    // read hits that XCD's L2); more parts only when there are fewer than
+    // ~1024 query blocks, since each part re-reads q
+    const int nch = int(std::max<int64_t>({2, (1024 + qblocks - 1) / qblocks,
                                            (int64_t(K) + kPrefillMaxChunk - 1) / kPrefillMaxChunk}));
-    const int kpw = round_up((K + nkc - 1) / nkc, kPrefillTile);
-    const int nch = (K + kpw - 1) / kpw;
     const dim3 grid(unsigned(int64_t(nch) * round_up64(qblocks, kXcds)));
     if (fp8)
       hipLaunchKernelGGL((logits_prefill_kernel<true, 8, 0>), grid, dim3(8 * 64), 0, stream, q8,
-                         q_scale, k8, k_scale, w, limit, logits, CandidateOut{}, B, T, K, kpw, nch, nqb);
+                         q_scale, k8, k_scale, w, limit, logits, CandidateOut{}, B, T, K, nch, nqb);
     else
       hipLaunchKernelGGL((logits_prefill_kernel<false, 4, 0>), grid, dim3(4 * 64), 0, stream, q8,
-                         q_scale, k8, k_scale, w, limit, logits, CandidateOut{}, B, T, K, kpw, nch, nqb);
+                         q_scale, k8, k_scale, w, limit, logits, CandidateOut{}, B, T, K, nch, nqb);
   }
   return hipGetLastError();
 }
@@ -732,7 +740,7 @@ hipError_t launch_logits_candidates(const void* q, const float* q_scale, const v
     constexpr int NL = decltype(nl_tag)::value;
     constexpr int NW = F ? 8 : 4;
     hipLaunchKernelGGL((logits_prefill_kernel<F, NW, NL>), grid, dim3(NW * 64), 0, stream, q8, q_scale,
-                       k8, k_scale, w, limit, nullptr, co, B, T, K, p.kpw, p.nch, p.nqb);
+                       k8, k_scale, w, limit, nullptr, co, B, T, K, p.nch, p.nqb);
   };
   using T4 = std::integral_constant<int, 4>;
   using T8 = std::integral_constant<int, 8>;
