@@ -11,8 +11,6 @@
 // consecutive lanes write one 256-byte row, so stores are fully coalesced.
 // The store stream (256 B per slot) is ~80% of the bytes, so the kernel is
 // HBM-write bound; output uses non-temporal stores.
-#include <type_traits>
-
 #include "mxfp4.h"
 
 namespace xk {
@@ -22,9 +20,7 @@ namespace {
 // and resolves it to a physical token (two dependent loads for the whole
 // wave); then STEPS steps each cover 4 slots x 16 pieces: the token index is
 // broadcast from its lane, all steps' nibble/scale loads are issued
-// together, and each step ends in one contiguous 1 KB store. Large outputs
-// use STEPS = 16 (fewer, longer waves); small ones fewer steps so there are
-// still thousands of waves.
+// together, and each step ends in one contiguous 1 KB store.
 template <int STEPS>
 __global__ __launch_bounds__(256) void mxfp4_gather_kernel(
     const uint32_t* __restrict__ kv_fp4,   // [NB*bs, 16] dwords (64 B per token)
@@ -32,6 +28,7 @@ __global__ __launch_bounds__(256) void mxfp4_gather_kernel(
     const int32_t* __restrict__ block_table, int MB,
     const int32_t* __restrict__ sel_pos, const int32_t* __restrict__ row_seq,
     u32x4* __restrict__ out, int64_t n_slots, int k, int bs_log2) {
+  static_assert(4 * STEPS <= 64, "one lane resolves each slot of the wave");
   const int lane = threadIdx.x & 63;
   const int64_t slot0 = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * (4 * STEPS);
   if (slot0 >= n_slots) return;  // uniform per wave
@@ -82,21 +79,18 @@ hipError_t launch_gather(const uint8_t* kv_fp4, const uint8_t* kv_scale,
                          int bs, hipStream_t stream) {
   const int64_t n_slots = int64_t(R) * k;
   const int bs_log2 = __builtin_ctz(unsigned(bs));
-  auto go = [&](auto steps_tag) {
-    constexpr int STEPS = decltype(steps_tag)::value;
-    const int64_t per_block = 4 * 4 * STEPS;  // 4 waves x 4*STEPS slots
-    const int64_t blocks = (n_slots + per_block - 1) / per_block;
-    hipLaunchKernelGGL(mxfp4_gather_kernel<STEPS>, dim3(unsigned(blocks)), dim3(256), 0, stream,
-                       reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale, block_table, MB,
-                       sel_pos, row_seq, reinterpret_cast<u32x4*>(out), n_slots, k, bs_log2);
-  };
-  // aim for >= 4096 waves: 4*STEPS slots per wave
-  if (n_slots >= 4096 * 64)
-    go(std::integral_constant<int, 16>{});
-  else if (n_slots >= 4096 * 16)
-    go(std::integral_constant<int, 4>{});
-  else
-    go(std::integral_constant<int, 1>{});
+  // Two steps (8 slots) per wave at every size: measured against 1, 4, 8
+  // and 16 steps, 2 gave the shortest gathers on the Flash and long prefill
+  // shapes (2M slots: 90 us against 106 us for 16 steps) and matched the best
+  // on the decode shapes. Shorter waves keep more independent
+  // sel_pos -> table -> data chains in flight; a single step leaves most
+  // lanes of the resolving load idle.
+  constexpr int kSteps = 2;
+  constexpr int64_t per_block = 4 * 4 * kSteps;  // 4 waves x 4*kSteps slots
+  const int64_t blocks = (n_slots + per_block - 1) / per_block;
+  hipLaunchKernelGGL(mxfp4_gather_kernel<kSteps>, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                     reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale, block_table, MB, sel_pos, row_seq,
+                     reinterpret_cast<u32x4*>(out), n_slots, k, bs_log2);
   return hipGetLastError();
 }
 
