@@ -37,8 +37,9 @@ def _rows(seed, N):
     return x
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-@pytest.mark.parametrize("N", [1, 7, 1000, 98304])
+# (1 << 20) + 3 rows: the launch shape for many rows (four passes per wave), ragged
+@pytest.mark.parametrize("dtype,N", [(d, n) for d in ("fp32", "bf16") for n in (1, 7, 1000, 98304)]
+                         + [("fp32", (1 << 20) + 3)])
 def test_quant_fp8_rows(xk, dtype, N):
     x = _rows(N, N)
     xt = torch.from_numpy(x).cuda()
@@ -55,8 +56,9 @@ def test_quant_fp8_rows(xk, dtype, N):
     assert np.array_equal(out.cpu().numpy(), codes)
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-@pytest.mark.parametrize("N,NB,bs", [(5, 2, 16), (300, 8, 64), (98304, 1536, 64)])
+@pytest.mark.parametrize("dtype,N,NB,bs", [(d, n, nb, bs) for d in ("fp32", "bf16")
+                                           for n, nb, bs in ((5, 2, 16), (300, 8, 64), (98304, 1536, 64))]
+                         + [("bf16", (1 << 20) + 3, 16400, 64)])
 def test_mxfp4_cache_write(xk, dtype, N, NB, bs):
     rng = np.random.default_rng(N)
     x = _rows(N + 1, N)
