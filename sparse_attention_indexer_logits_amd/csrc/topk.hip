@@ -1052,7 +1052,7 @@ __device__ __forceinline__ void append_list(TopkShared<BLOCK, CAP>& sh, KeyAt ke
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     take[u] = take_it(u);
-    mask[u] = __ballot(take[u]);
+    mask[u] = __builtin_amdgcn_ballot_w64(take[u]);  // the compare's own lane mask
     total += __popcll(mask[u]);
   }
   if (total == 0) return;  // uniform
@@ -1129,10 +1129,16 @@ __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const 
   // monotone in the score, so one float compare per key, and only joining
   // keys are converted)
   const float tau_f = key_value(sh.tau);
+  // A load past the row's end reads 0.0, which passes only when tau_f <= 0:
+  // the range test is needed only for such a bound on the last chunk.
   stream_chunks<BLOCK, U, NBUF>(rs, prefix, n, first, second, [&](const float (&c)[U], int base) {
-    append_list<BLOCK, CAP, U>(
-        sh, [&](int u) { return order_key(c[u]); }, [&](int u) { return uint32_t(base + BLOCK * u + tid); },
-        [&](int u) { return base + BLOCK * u + tid < n && c[u] >= tau_f; });
+    auto key_of = [&](int u) { return order_key(c[u]); };
+    auto j_of = [&](int u) { return uint32_t(base + BLOCK * u + tid); };
+    if (tau_f > 0.f || base + BLOCK * U <= n)  // uniform
+      append_list<BLOCK, CAP, U>(sh, key_of, j_of, [&](int u) { return c[u] >= tau_f; });
+    else
+      append_list<BLOCK, CAP, U>(sh, key_of, j_of,
+                                 [&](int u) { return base + BLOCK * u + tid < n && c[u] >= tau_f; });
   });
   __syncthreads();
   if (!sh.overflow) {
