@@ -603,12 +603,31 @@ __device__ __forceinline__ float load_score(__amdgpu_buffer_rsrc_t rs, int j) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, j * 4, 0, 0));
 }
 
-// Loads of the chunk of BLOCK*U entries starting at base (this thread's
-// entries base + BLOCK*u + tid).
-template <int BLOCK, int U>
+// Entry u of this thread in the chunk of BLOCK*U entries starting at base:
+// base + BLOCK*u + tid, or with Q4 (16-byte loads: 4 consecutive entries per
+// load) base + 4*BLOCK*(u/4) + 4*tid + u%4.
+template <int BLOCK, bool Q4>
+__device__ __forceinline__ int chunk_j(int base, int u) {
+  return Q4 ? base + 4 * BLOCK * (u >> 2) + 4 * int(threadIdx.x) + (u & 3) : base + BLOCK * u + int(threadIdx.x);
+}
+
+// Loads of the chunk of BLOCK*U entries starting at base (entry u at
+// chunk_j). Q4 needs the row 16-byte aligned, base a multiple of 4 and rs
+// covering whole quads.
+template <int BLOCK, int U, bool Q4 = false>
 __device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t rs, int base, float (&c)[U]) {
+  if constexpr (Q4) {
+    static_assert(U % 4 == 0, "whole quads");
 #pragma unroll
-  for (int u = 0; u < U; ++u) c[u] = load_score(rs, base + BLOCK * u + int(threadIdx.x));
+    for (int i = 0; i < U / 4; ++i) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, chunk_j<BLOCK, true>(base, 4 * i) * 4, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[4 * i + e] = __uint_as_float(v[e]);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) c[u] = load_score(rs, chunk_j<BLOCK, false>(base, u));
+  }
 }
 
 // g(scores, base) over chunks of entries [j_lo, j_hi) of the row streamed
@@ -621,7 +640,7 @@ __device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t rs, int base, 
 // three chunks unconditionally (entries past j_hi are masked): with no exit
 // between a load and its use, the compiler issues the loads where they
 // stand instead of next to their use.
-template <int BLOCK, int U, int NBUF, typename G>
+template <int BLOCK, int U, int NBUF, bool Q4, typename G>
 __device__ __forceinline__ void stream_chunks(__amdgpu_buffer_rsrc_t rs, int j_lo, int j_hi, float (&c0)[U],
                                               float (&c1)[U], G g) {
   static_assert(NBUF == 2 || NBUF == 3, "two or three buffers");
@@ -629,19 +648,19 @@ __device__ __forceinline__ void stream_chunks(__amdgpu_buffer_rsrc_t rs, int j_l
   if constexpr (NBUF == 3) {
     float c2[U];
     for (int base = j_lo; base < j_hi; base += 3 * C) {
-      load_chunk<BLOCK, U>(rs, base + 2 * C, c2);
+      load_chunk<BLOCK, U, Q4>(rs, base + 2 * C, c2);
       g(c0, base);
-      load_chunk<BLOCK, U>(rs, base + 3 * C, c0);
+      load_chunk<BLOCK, U, Q4>(rs, base + 3 * C, c0);
       g(c1, base + C);
-      load_chunk<BLOCK, U>(rs, base + 4 * C, c1);
+      load_chunk<BLOCK, U, Q4>(rs, base + 4 * C, c1);
       g(c2, base + 2 * C);
     }
   } else {  // c1 unused: one chunk in flight while one is processed
     float nxt[U];
     for (int base = j_lo; base < j_hi; base += 2 * C) {
-      load_chunk<BLOCK, U>(rs, base + C, nxt);
+      load_chunk<BLOCK, U, Q4>(rs, base + C, nxt);
       g(c0, base);
-      load_chunk<BLOCK, U>(rs, base + 2 * C, c0);
+      load_chunk<BLOCK, U, Q4>(rs, base + 2 * C, c0);
       g(nxt, base + C);
     }
   }
@@ -1082,27 +1101,32 @@ __device__ __forceinline__ void append_list(TopkShared<BLOCK, CAP>& sh, KeyAt ke
 // >= b* and the keys >= tau of the rest of the row (streamed once) form an
 // LDS candidate list, from which the winners are selected exactly. If the list runs out of room (scores
 // crowded into b*), the row falls back to multi-pass streaming selection.
-template <int BLOCK, int V, int CAP, int NBUF>
+template <int BLOCK, int V, int CAP, int NBUF, bool Q4 = false>
 __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const float* __restrict__ x, int n,
                                               int k, int32_t* __restrict__ orow) {
   constexpr int U = 16;           // streamed entries per thread per chunk
   constexpr int L = CAP / BLOCK;  // list entries per thread
   static_assert(CAP % BLOCK == 0, "list spread evenly over the block");
+  static_assert(!Q4 || V % 4 == 0, "whole quads");
   const int tid = threadIdx.x;
   const int prefix = min(n, BLOCK * V);
-  const auto rs = row_rsrc(x, n);
+  // Q4: whole quads, so a 16-byte load never straddles the range's end (the
+  // entries of the last quad past n are row data, masked by index below)
+  const auto rs = Q4 ? make_rsrc(x, ((n + 3) & ~3) * 4) : row_rsrc(x, n);
   float raw[V];
-  load_chunk<BLOCK, V>(rs, 0, raw);
+  load_chunk<BLOCK, V, Q4>(rs, 0, raw);
   float first[U], second[U];  // the streamed part's first chunks, in flight during the prefix's threshold
-  load_chunk<BLOCK, U>(rs, prefix, first);
-  if constexpr (NBUF == 3) load_chunk<BLOCK, U>(rs, prefix + BLOCK * U, second);
+  load_chunk<BLOCK, U, Q4>(rs, prefix, first);
+  if constexpr (NBUF == 3) load_chunk<BLOCK, U, Q4>(rs, prefix + BLOCK * U, second);
   uint32_t key[V];
 #pragma unroll
-  for (int v = 0; v < V; ++v) key[v] = tid + BLOCK * v < prefix ? order_key(raw[v]) : 0u;
+  for (int v = 0; v < V; ++v) key[v] = chunk_j<BLOCK, Q4>(0, v) < prefix ? order_key(raw[v]) : 0u;
   auto key_at = [&](int v) { return key[v]; };
-  auto j_at = [&](int v) { return uint32_t(tid + BLOCK * v); };
+  auto j_at = [&](int v) { return uint32_t(chunk_j<BLOCK, Q4>(0, v)); };
   if (n <= prefix) {
-    if (!bucket_topk<BLOCK, CAP, V>(sh, key_at, j_at, k, orow, (n + BLOCK - 1) / BLOCK))
+    // entries u >= nu lie past n for every thread
+    const int nu = Q4 ? 4 * ((n + 4 * BLOCK - 1) / (4 * BLOCK)) : (n + BLOCK - 1) / BLOCK;
+    if (!bucket_topk<BLOCK, CAP, V>(sh, key_at, j_at, k, orow, nu))
       radix_topk<BLOCK, CAP>(sh, x, n, k, orow);
     return;
   }
@@ -1129,16 +1153,17 @@ __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const 
   // monotone in the score, so one float compare per key, and only joining
   // keys are converted)
   const float tau_f = key_value(sh.tau);
-  // A load past the row's end reads 0.0, which passes only when tau_f <= 0:
-  // the range test is needed only for such a bound on the last chunk.
-  stream_chunks<BLOCK, U, NBUF>(rs, prefix, n, first, second, [&](const float (&c)[U], int base) {
+  // Only the last chunk needs the range test: past the range a load reads
+  // 0.0, which can pass only when tau_f <= 0, and with Q4 the rest of the
+  // last quad holds row data.
+  stream_chunks<BLOCK, U, NBUF, Q4>(rs, prefix, n, first, second, [&](const float (&c)[U], int base) {
     auto key_of = [&](int u) { return order_key(c[u]); };
-    auto j_of = [&](int u) { return uint32_t(base + BLOCK * u + tid); };
-    if (tau_f > 0.f || base + BLOCK * U <= n)  // uniform
+    auto j_of = [&](int u) { return uint32_t(chunk_j<BLOCK, Q4>(base, u)); };
+    if (base + BLOCK * U <= n || (!Q4 && tau_f > 0.f))  // uniform
       append_list<BLOCK, CAP, U>(sh, key_of, j_of, [&](int u) { return c[u] >= tau_f; });
     else
       append_list<BLOCK, CAP, U>(sh, key_of, j_of,
-                                 [&](int u) { return base + BLOCK * u + tid < n && c[u] >= tau_f; });
+                                 [&](int u) { return chunk_j<BLOCK, Q4>(base, u) < n && c[u] >= tau_f; });
   });
   __syncthreads();
   if (!sh.overflow) {
@@ -1161,14 +1186,14 @@ __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const 
   radix_topk<BLOCK, CAP>(sh, x, n, k, orow);
 }
 
-template <int BLOCK, int V, int CAP, int NBUF = 2>
+template <int BLOCK, int V, int CAP, int NBUF = 2, bool Q4 = false>
 __global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restrict__ logits,
                                                           const int32_t* __restrict__ limit,
                                                           int32_t* __restrict__ idx, int K, int k) {
   __shared__ TopkShared<BLOCK, CAP> sh;
   const int64_t row = blockIdx.x;
   const int n = limit ? max(0, min(limit[row], K - 1) + 1) : K;
-  long_row_topk<BLOCK, V, CAP, NBUF>(sh, logits + row * K, n, k, idx + row * k);
+  long_row_topk<BLOCK, V, CAP, NBUF, Q4>(sh, logits + row * K, n, k, idx + row * k);
 }
 
 // ---------------------------------------------------------------------------
@@ -1321,8 +1346,13 @@ hipError_t launch_topk(const float* logits, const int32_t* limit, int32_t* idx, 
   if (K <= 256 * 16) return launch_one<256, 16, 256>(logits, limit, idx, R, K, k, stream);
   if (K <= 1024 * 8) return launch_one<1024, 8, 1024>(logits, limit, idx, R, K, k, stream);
   if (K <= 1024 * 16) return launch_one<1024, 16, 1024>(logits, limit, idx, R, K, k, stream);
-  hipLaunchKernelGGL((topk_long_kernel<1024, 16, 8192>), dim3(unsigned(R)), dim3(1024), 0, stream,
-                     logits, limit, idx, K, k);
+  // 16-byte loads when every row starts 16-byte aligned
+  if (K % 4 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0)
+    hipLaunchKernelGGL((topk_long_kernel<1024, 16, 8192, 2, true>), dim3(unsigned(R)), dim3(1024), 0, stream,
+                       logits, limit, idx, K, k);
+  else
+    hipLaunchKernelGGL((topk_long_kernel<1024, 16, 8192>), dim3(unsigned(R)), dim3(1024), 0, stream,
+                       logits, limit, idx, K, k);
   return hipGetLastError();
 }
 
