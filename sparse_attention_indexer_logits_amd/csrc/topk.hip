@@ -1064,30 +1064,30 @@ __global__ __launch_bounds__(64 * kWaveRows, 4) void topk_wave_kernel(const floa
 template <int BLOCK, int CAP, int U, typename KeyAt, typename JAt, typename Take>
 __device__ __forceinline__ void append_list(TopkShared<BLOCK, CAP>& sh, KeyAt key_at, JAt j_at,
                                             Take take_it) {
-  const int lane = lane_id();
-  bool take[U];
   uint64_t mask[U];
   int total = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    take[u] = take_it(u);
-    mask[u] = __builtin_amdgcn_ballot_w64(take[u]);  // the compare's own lane mask
+    mask[u] = __builtin_amdgcn_ballot_w64(take_it(u));  // the compare's own lane mask
     total += __popcll(mask[u]);
   }
   if (total == 0) return;  // uniform
   int base = 0;
-  if (lane == 0) base = atomicAdd(&sh.ccount, total);
+  if (lane_id() == 0) base = atomicAdd(&sh.ccount, total);
   base = __builtin_amdgcn_readlane(base, 0);
+  if (base + total > CAP) {  // uniform: the list is full, the row goes to the radix path
+    if (lane_id() == 0) sh.overflow = 1;
+    return;
+  }
+  // take_it is evaluated again rather than kept: U lane masks held as
+  // booleans would not fit the scalar registers
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (take[u]) {
-      const int pos = base + prefix_in_wave(mask[u]);
-      if (pos < CAP) {
-        sh.ckey[pos] = key_at(u);
-        sh.cj[pos] = j_at(u);
-      } else {
-        sh.overflow = 1;
-      }
+    if (take_it(u)) {
+      const int pos = base + int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask[u] >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo(uint32_t(mask[u]), 0u)));
+      sh.ckey[pos] = key_at(u);
+      sh.cj[pos] = j_at(u);
     }
     base += __popcll(mask[u]);
   }
@@ -1140,8 +1140,11 @@ __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const 
   const int bstar = sh.digit;
   // prefix keys in bins >= b* join the list; tau, the smallest of them, is
   // at most the prefix's k-th largest key
+  // The list holds raw score bits until the stream ends (one dense pass then
+  // turns them into order keys), so the stream's masked writes carry no
+  // conversion.
   uint32_t mn = 0xFFFFFFFFu, unused = 0u;
-  append_list<BLOCK, CAP, V>(sh, key_at, j_at, [&](int v) {
+  append_list<BLOCK, CAP, V>(sh, [&](int v) { return __float_as_uint(key_value(key[v])); }, j_at, [&](int v) {
     const bool t = bin[v] >= bstar;
     if (t) mn = min(mn, key[v]);
     return t;
@@ -1157,7 +1160,7 @@ __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const 
   // 0.0, which can pass only when tau_f <= 0, and with Q4 the rest of the
   // last quad holds row data.
   stream_chunks<BLOCK, U, NBUF, Q4>(rs, prefix, n, first, second, [&](const float (&c)[U], int base) {
-    auto key_of = [&](int u) { return order_key(c[u]); };
+    auto key_of = [&](int u) { return __float_as_uint(c[u]); };
     auto j_of = [&](int u) { return uint32_t(chunk_j<BLOCK, Q4>(base, u)); };
     if (base + BLOCK * U <= n || (!Q4 && tau_f > 0.f))  // uniform
       append_list<BLOCK, CAP, U>(sh, key_of, j_of, [&](int u) { return c[u] >= tau_f; });
@@ -1168,6 +1171,8 @@ __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const 
   __syncthreads();
   if (!sh.overflow) {
     const int nc = sh.ccount;
+    for (int i = tid; i < nc; i += BLOCK) sh.ckey[i] = order_key(__uint_as_float(sh.ckey[i]));
+    __syncthreads();
     uint32_t lkey[L], lj[L];
 #pragma unroll
     for (int u = 0; u < L; ++u) {
