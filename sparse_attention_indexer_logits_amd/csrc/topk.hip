@@ -56,10 +56,6 @@ constexpr int kBins = 2048;  // 11-bit digits
 
 __device__ __forceinline__ int lane_id() { return int(threadIdx.x & 63); }
 
-__device__ __forceinline__ int prefix_in_wave(uint64_t mask) {
-  return __popcll(mask & ((uint64_t(1) << lane_id()) - 1));
-}
-
 // DPP controls (GFX9 encoding).
 constexpr int kDppQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kDppQuadSwap2 = 0x4E;    // quad_perm [2,3,0,1]
@@ -118,6 +114,7 @@ struct TopkShared {
   uint32_t cj[CAP];
   int wsel[BLOCK / 64], wcand[BLOCK / 64];
   uint32_t wlo[BLOCK / 64], whi[BLOCK / 64];  // per-wave finite key range
+  int wtot[BLOCK / 64];                        // per-wave bin totals of the block scan
   int digit, above, at;
   int ccount;    // candidate list: entries claimed so far
   int overflow;  // 1 if the candidate list ran out of room
@@ -420,32 +417,41 @@ struct LinearBins {
 };
 using ValueBins = LinearBins<kBins>;
 
-// Wave 0: turn the bin counts in hist into descending exclusive starts
-// (entries in higher bins) in place, and find the threshold bin b*: the bin holding the need-th largest entry, need =
-// min(k, entries). Leaves sh.digit = b* and sh.at = entries in bins >= b*
-// (b* = kBins and 0 when there are no entries).
+// Turn the bin counts in hist into descending exclusive starts (entries in
+// higher bins) in place, and find the threshold bin b*: the bin holding the
+// need-th largest entry, need = min(k, entries). Leaves sh.digit = b* and
+// sh.at = entries in bins >= b* (b* = kBins and 0 when there are no
+// entries). Run by the whole block (every thread calls it): thread t holds
+// kBins/BLOCK consecutive bins, thread 0 the top ones; a wave prefix sum, one
+// barrier and the totals of the waves above give each thread its first
+// start. Exactly one thread holds b*.
 template <int BLOCK, int CAP>
-__device__ __forceinline__ void scan_desc(TopkShared<BLOCK, CAP>& sh, int k) {
-  constexpr int PER = kBins / 64;
-  const int lane = lane_id();
-  const int base = kBins - (lane + 1) * PER;  // lane 0 holds the top bins
+__device__ __forceinline__ void scan_desc_block(TopkShared<BLOCK, CAP>& sh, int k) {
+  constexpr int NW = BLOCK / 64;
+  constexpr int PER = kBins / BLOCK;
+  static_assert(PER >= 1 && kBins % BLOCK == 0, "bins per thread");
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int base = kBins - (tid + 1) * PER;  // thread 0 holds the top bins
   uint32_t c[PER];
 #pragma unroll
-  for (int i = 0; i < PER / 4; ++i) {
-    const u32x4 q4 = *reinterpret_cast<const u32x4*>(&sh.hist[base + 4 * i]);
-    c[4 * i] = q4[0];
-    c[4 * i + 1] = q4[1];
-    c[4 * i + 2] = q4[2];
-    c[4 * i + 3] = q4[3];
-  }
+  for (int i = 0; i < PER; ++i) c[i] = sh.hist[base + i];
   int sum = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) sum += int(c[i]);
   const int incl = wave_incl_scan(sum);
-  const int need = min(k, __builtin_amdgcn_readlane(incl, 63));
-  int run = incl - sum, found = -1, upto = 0;
+  if (lane_id() == 63) sh.wtot[wave] = incl;
+  __syncthreads();
+  int above = 0, total = 0;
 #pragma unroll
-  for (int o = 0; o < PER; ++o) {  // descending bin order within the lane
+  for (int w = 0; w < NW; ++w) {
+    const int t = sh.wtot[w];
+    above += w < wave ? t : 0;
+    total += t;
+  }
+  const int need = min(k, total);
+  int run = above + incl - sum, found = -1, upto = 0;
+#pragma unroll
+  for (int o = 0; o < PER; ++o) {  // descending bin order within the thread
     const int i = PER - 1 - o;
     const int cnt = int(c[i]);
     c[i] = uint32_t(run);
@@ -456,15 +462,12 @@ __device__ __forceinline__ void scan_desc(TopkShared<BLOCK, CAP>& sh, int k) {
     }
   }
 #pragma unroll
-  for (int i = 0; i < PER / 4; ++i) {
-    *reinterpret_cast<u32x4*>(&sh.hist[base + 4 * i]) =
-        u32x4{c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]};
-  }
+  for (int i = 0; i < PER; ++i) sh.hist[base + i] = c[i];
   if (found >= 0) {
     sh.digit = found;
     sh.at = upto;
   }
-  if (need == 0 && lane == 0) {
+  if (need == 0 && tid == 0) {
     sh.digit = kBins;
     sh.at = 0;
   }
@@ -521,7 +524,7 @@ __device__ __forceinline__ ValueBins bucket_threshold(TopkShared<BLOCK, CAP>& sh
     }
   }
   __syncthreads();
-  if (threadIdx.x < 64) scan_desc(sh, k);
+  scan_desc_block(sh, k);
   __syncthreads();
   return bins;
 }
