@@ -27,10 +27,18 @@ __global__ __launch_bounds__(256) void mxfp4_gather_kernel(
     const uint8_t* __restrict__ kv_scale,  // [NB*bs, 4]
     const int32_t* __restrict__ block_table, int MB,
     const int32_t* __restrict__ sel_pos, const int32_t* __restrict__ row_seq,
-    u32x4* __restrict__ out, int64_t n_slots, int k, int bs_log2) {
+    u32x4* __restrict__ out, int64_t n_slots, int k, int bs_log2, int bpr) {
   static_assert(4 * STEPS <= 64, "one lane resolves each slot of the wave");
   const int lane = threadIdx.x & 63;
-  const int64_t slot0 = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * (4 * STEPS);
+  // bpr > 0 (a row is bpr whole workgroups): the workgroups of row r run on
+  // XCD r % 8 (workgroup i runs on XCD i % 8), where the top-k wrote that
+  // row's sel_pos, so those loads hit the XCD's L2
+  int64_t blk = blockIdx.x;
+  if (bpr > 0) {
+    const int64_t m = blockIdx.x / 8;
+    blk = ((m / bpr) * 8 + blockIdx.x % 8) * bpr + m % bpr;
+  }
+  const int64_t slot0 = (blk * 4 + (threadIdx.x >> 6)) * (4 * STEPS);
   if (slot0 >= n_slots) return;  // uniform per wave
 
   // 1. this lane's slot -> physical token (-1: padded slot or past the end)
@@ -87,10 +95,13 @@ hipError_t launch_gather(const uint8_t* kv_fp4, const uint8_t* kv_scale,
   // lanes of the resolving load idle.
   constexpr int kSteps = 2;
   constexpr int64_t per_block = 4 * 4 * kSteps;  // 4 waves x 4*kSteps slots
-  const int64_t blocks = (n_slots + per_block - 1) / per_block;
+  // rows of whole workgroups go to XCDs by row (the grid rounded up to eight
+  // rows); otherwise workgroups take consecutive slots
+  const int bpr = k % per_block == 0 ? int(k / per_block) : 0;
+  const int64_t blocks = bpr ? (int64_t(R) + 7) / 8 * 8 * bpr : (n_slots + per_block - 1) / per_block;
   hipLaunchKernelGGL(mxfp4_gather_kernel<kSteps>, dim3(unsigned(blocks)), dim3(256), 0, stream,
                      reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale, block_table, MB, sel_pos, row_seq,
-                     reinterpret_cast<u32x4*>(out), n_slots, k, bs_log2);
+                     reinterpret_cast<u32x4*>(out), n_slots, k, bs_log2, bpr);
   return hipGetLastError();
 }
 

@@ -719,10 +719,15 @@ __device__ __forceinline__ void radix_topk(TopkShared<BLOCK, CAP>& sh, const flo
 template <int BLOCK, int V, int CAP>
 __global__ __launch_bounds__(BLOCK) void topk_kernel(const float* __restrict__ logits,
                                                      const int32_t* __restrict__ limit,
-                                                     int32_t* __restrict__ idx, int K, int k) {
+                                                     int32_t* __restrict__ idx, int R, int K, int k) {
   __shared__ TopkShared<BLOCK, CAP> sh;
   const int tid = threadIdx.x;
-  const int64_t row = int64_t(gridDim.x) - 1 - blockIdx.x;
+  // Row r runs on XCD r % 8 (workgroup i runs on XCD i % 8), where the
+  // gather of its selection runs too, so the indices it reads are in that
+  // XCD's L2; groups of eight rows go last to first (the longest rows first
+  // under a causal limit). The grid is R rounded up to whole groups.
+  const int64_t row = (int64_t(gridDim.x / 8) - 1 - blockIdx.x / 8) * 8 + blockIdx.x % 8;
+  if (row >= R) return;  // uniform
   const float* x = logits + row * K;
   float raw[V];  // issued before the limit arrives; keys past it are masked below
   load_chunk<BLOCK, V>(row_rsrc(x, K), 0, raw);
@@ -1326,8 +1331,8 @@ __global__ __launch_bounds__(kRecBlock) void fused_recompute_kernel(
 template <int BLOCK, int V, int CAP>
 hipError_t launch_one(const float* logits, const int32_t* limit, int32_t* idx, int R, int K, int k,
                       hipStream_t stream) {
-  hipLaunchKernelGGL((topk_kernel<BLOCK, V, CAP>), dim3(unsigned(R)), dim3(BLOCK), 0, stream,
-                     logits, limit, idx, K, k);
+  hipLaunchKernelGGL((topk_kernel<BLOCK, V, CAP>), dim3(unsigned((R + 7) / 8 * 8)), dim3(BLOCK), 0, stream,
+                     logits, limit, idx, R, K, k);
   return hipGetLastError();
 }
 
