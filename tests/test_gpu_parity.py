@@ -290,16 +290,20 @@ def test_gather_golden_bytes_and_scales(xk):
     assert np.array_equal(g, o)
 
 
+# k = 33: workgroups take consecutive slots; k = 64, 96: rows of whole workgroups, grouped by
+# XCD, with 5 rows (not a multiple of 8)
+@pytest.mark.parametrize("k", [33, 64, 96])
 @pytest.mark.parametrize("bs", [1, 16, 64, 256])
-def test_gather_block_sizes_and_identity_rows(xk, bs):
-    rng = np.random.default_rng(bs)
+def test_gather_block_sizes_and_identity_rows(xk, bs, k):
+    print(f"[parity] gather bs={bs} k={k}", flush=True)
+    rng = np.random.default_rng(bs * 1000 + k)
     S, MB = 5, 7
     NB = S * MB
     fp4 = rng.integers(0, 256, size=(NB, bs, 64), dtype=np.uint8)
     sc = rng.integers(110, 145, size=(NB, bs, 4), dtype=np.uint8)
     sc[rng.random(sc.shape) < 0.05] = 0xFF
     table = rng.permutation(NB).astype(np.int32).reshape(S, MB)
-    R, k = S, 33
+    R = S
     sel = rng.integers(-2, MB * bs, size=(R, k)).astype(np.int32)
     d = {"kv_fp4": torch.from_numpy(fp4).cuda(), "kv_scale": torch.from_numpy(sc).cuda(),
          "block_table": torch.from_numpy(table).cuda(), "row_seq": None}
