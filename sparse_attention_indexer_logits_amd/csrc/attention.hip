@@ -49,6 +49,7 @@ __device__ __forceinline__ float shfl_sum(float v) {
   return v + __shfl_xor(v, 32);
 }
 
+template <bool SPLIT>
 __global__ __launch_bounds__(256) void sparse_attention_kernel(
     const uint16_t* __restrict__ q, const uint32_t* __restrict__ kv_fp4, const uint8_t* __restrict__ kv_scale,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ sel_pos,
@@ -62,9 +63,14 @@ __global__ __launch_bounds__(256) void sparse_attention_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
-  const int groups = H / kAttnHeads;
+  // SPLIT: the workgroup takes 16 heads and its four waves split every chunk's
+  // keys (wave w keys 16w..16w+15), each wave running its own online softmax;
+  // the four partial states are merged at the end. Otherwise each wave takes
+  // 16 of the workgroup's 64 heads over all keys.
+  constexpr int kHeadsPerWg = SPLIT ? 16 : kAttnHeads;
+  const int groups = H / kHeadsPerWg;
   const int64_t r = blockIdx.x / groups;
-  const int head = (blockIdx.x % groups) * kAttnHeads + 16 * wave + c;  // this lane's head column
+  const int head = (blockIdx.x % groups) * kHeadsPerWg + (SPLIT ? 0 : 16 * wave) + c;  // this lane's head column
 
   // 1. the row's slots -> cache tokens (-1: padded slot)
   const int seq = row_seq ? row_seq[r] : int(r);
@@ -129,22 +135,24 @@ __global__ __launch_bounds__(256) void sparse_attention_kernel(
     __syncthreads();
     if (c0 + kChunk < k) fetch(c0 + kChunk, nib, sc, t);  // in flight during the MFMAs
 
-    // 3. S^T = K Q^T for this wave's heads
-    f32x4 sacc[4];
+    // 3. S^T = K Q^T for this wave's heads (SPLIT: of this wave's 16 keys)
+    constexpr int NST = SPLIT ? 1 : 4;  // 16-key subtiles per wave
+    f32x4 sacc[NST];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int st = 0; st < NST; ++st) {
+      const int key0 = 16 * (SPLIT ? wave : st);
       sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* arow = kt + (16 * st + c) * kKPitch + 8 * g;
+      const uint16_t* arow = kt + (key0 + c) * kKPitch + 8 * g;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const Frag*>(arow + 32 * s), qb[s],
                                                             sacc[st], 0, 0, 0);
     }
     // 4. online softmax (base 2), head c
-    float x[4][4], cmax = -INFINITY;
+    float x[NST][4], cmax = -INFINITY;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sbias[16 * st + 4 * g]);
+    for (int st = 0; st < NST; ++st) {
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sbias[16 * (SPLIT ? wave : st) + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         x[st][i] = fmaf(sacc[st][i], scale_log2, b4[i]);
@@ -157,33 +165,86 @@ __global__ __launch_bounds__(256) void sparse_attention_kernel(
     const float alpha = any ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
     float psum = 0.f;
     Frag pb[2];
+    s16x4 pq;  // SPLIT: this lane's probabilities (bf16 bits) of keys 4g..4g+3 of the wave's subtile
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+    for (int st = 0; st < NST; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p = any ? __builtin_amdgcn_exp2f(x[st][i] - m_new) : 0.f;
         psum += p;
-        pb[st >> 1][4 * (st & 1) + i] = __bf16(p);
+        if constexpr (SPLIT)
+          pq[i] = __builtin_bit_cast(short, __bf16(p));
+        else
+          pb[st >> 1][4 * (st & 1) + i] = __bf16(p);
       }
     l = fmaf(l, alpha, shfl_sum(psum));
     m = m_new;
     // 5. O^T = O^T * alpha + V^T P^T
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    if constexpr (SPLIT) {
+      // one 16-key step on v_mfma_f32_16x16x16_bf16: a lane group's K slots
+      // are keys 4g..4g+3 of the wave's subtile on both operands
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        const uint16_t* vrow = vt + (16 * mt + c) * kVPitch + 32 * ks + 4 * g;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-        const Frag a = __builtin_bit_cast(Frag, u32x4{lo.x, lo.y, hi.x, hi.y});
-        o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ks], o[mt], 0, 0, 0);
+        const uint2 v = *reinterpret_cast<const uint2*>(vt + (16 * mt + c) * kVPitch + 16 * wave + 4 * g);
+        o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v), pq, o[mt], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const uint16_t* vrow = vt + (16 * mt + c) * kVPitch + 32 * ks + 4 * g;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+          const Frag a = __builtin_bit_cast(Frag, u32x4{lo.x, lo.y, hi.x, hi.y});
+          o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ks], o[mt], 0, 0, 0);
+        }
       }
     }
     __syncthreads();  // the tiles are rewritten by the next chunk
   }
 
+  if constexpr (SPLIT) {
+    // 6'. merge the four waves' states of the 16 heads, then the sink
+    __shared__ float cm[4][16], cl[4][16];
+    __shared__ __attribute__((aligned(16))) float co[4][16][kHeadDim];
+    if (g == 0) {
+      cm[wave][c] = m;
+      cl[wave][c] = l;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(&co[wave][c][16 * mt + 4 * g]) = o[mt];
+    __syncthreads();
+    const int hc = tid >> 4, d0 = 8 * (tid & 15);  // 16 threads per head, 8 dims each
+    float mw[4], mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      mw[w] = cm[w][hc];
+      mm = fmaxf(mm, mw[w]);
+    }
+    float lsum = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = mw[w] > -INFINITY ? __builtin_amdgcn_exp2f(mw[w] - mm) : 0.f;
+      lsum = fmaf(cl[w][hc], a, lsum);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(co[w][hc][d0 + e], a, acc[e]);
+    }
+    const int hd = (blockIdx.x % groups) * kHeadsPerWg + hc;
+    const float s2 = sink ? sink[hd] * 1.4426950408889634f : -INFINITY;
+    const float mf = fmaxf(mm, s2);
+    float f = 0.f;
+    if (mf > -INFINITY) {
+      const float a = __builtin_amdgcn_exp2f(mm - mf);
+      f = a / (lsum * a + __builtin_amdgcn_exp2f(s2 - mf));
+    }
+    float* orow = out + (r * H + hd) * int64_t(kHeadDim) + d0;
+    *reinterpret_cast<f32x4*>(orow) = f32x4{acc[0], acc[1], acc[2], acc[3]} * f;
+    *reinterpret_cast<f32x4*>(orow + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]} * f;
+    return;
+  }
   // 6. the sink joins the denominator; store head c's outputs
   const float s2 = sink ? sink[head] * 1.4426950408889634f : -INFINITY;
   const float mf = fmaxf(m, s2);
@@ -205,9 +266,16 @@ hipError_t launch_sparse_attention(const uint16_t* q, const uint8_t* kv_fp4, con
                                    hipStream_t stream) {
   const int bs_log2 = __builtin_ctz(unsigned(bs));
   const float scale_log2 = float(double(scale) * 1.4426950408889634);  // softmax in base 2
-  hipLaunchKernelGGL(sparse_attention_kernel, dim3(unsigned(int64_t(R) * (H / kAttnHeads))), dim3(256), 0, stream,
-                     q, reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale, block_table, sel_pos, row_seq, sink,
-                     scale_log2, out, H, k, MB, bs_log2);
+  // Fewer (row, 64-head) workgroups than CUs (decode): 16 heads per workgroup
+  // with the keys split across its waves, four times the workgroups.
+  if (int64_t(R) * (H / kAttnHeads) < 256)
+    hipLaunchKernelGGL(sparse_attention_kernel<true>, dim3(unsigned(int64_t(R) * (H / 16))), dim3(256), 0, stream,
+                       q, reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale, block_table, sel_pos, row_seq, sink,
+                       scale_log2, out, H, k, MB, bs_log2);
+  else
+    hipLaunchKernelGGL(sparse_attention_kernel<false>, dim3(unsigned(int64_t(R) * (H / kAttnHeads))), dim3(256), 0,
+                       stream, q, reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale, block_table, sel_pos, row_seq,
+                       sink, scale_log2, out, H, k, MB, bs_log2);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ constexpr int kHeadDim = 128;  // DeepSeek-V4 index_head_dim
 constexpr int kMaxTopk = 2048;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;  // four bf16 bit patterns
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
