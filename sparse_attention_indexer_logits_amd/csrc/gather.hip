@@ -31,8 +31,9 @@ __global__ __launch_bounds__(256) void mxfp4_gather_kernel(
   static_assert(4 * STEPS <= 64, "one lane resolves each slot of the wave");
   const int lane = threadIdx.x & 63;
   // bpr > 0 (a row is bpr whole workgroups): the workgroups of row r run on
-  // XCD r % 8 (workgroup i runs on XCD i % 8), where the top-k wrote that
-  // row's sel_pos, so those loads hit the XCD's L2
+  // XCD r % 8 (workgroup i runs on XCD i % 8). The one-workgroup-per-row
+  // top-k kernels run row r there too, so the row's sel_pos loads hit that
+  // XCD's L2 (a placement for speed only; any sel_pos gives the same output)
   int64_t blk = blockIdx.x;
   if (bpr > 0) {
     const int64_t m = blockIdx.x / 8;
