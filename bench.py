@@ -2,28 +2,33 @@
 
 A step is one pass of the whole path over one batch of synthetic input:
     xk_indexer_logits -> xk_indexer_topk -> xk_mxfp4_paged_gather
-Prints ONE JSON line. `value` is the indexer-logits throughput of the whole
-step (algorithmic logits FLOPs / step wall time), `topk_gather_GBps` the
-algorithmic bytes of top-k + gather over their kernel time; `stages` has every
-kernel's average duration against its roof, and `roofline` repeats the
-dominant kernel. Prefill configs also time the fused step
-(xk_indexer_logits_topk -> gather, no score matrix) under `fused`, and every
-config times the sparse attention that consumes the selection under
-`consumer` (not part of the step).
+Prints ONE JSON line. The headline workload is the long-context fp8 chunked
+prefill (T=2048 queries at causal offset 96256 against K=98304 OCP-e4m3
+keys, top-1024), the largest single-GPU shape. `value` is the indexer-logits
+throughput of the whole step (algorithmic logits FLOPs / step wall time),
+`topk_gather_GBps` the algorithmic bytes of top-k + gather over their kernel
+time; `stages` has every kernel's average duration against its roof (plus
+per-dispatch percentiles, warm and after a 512 MiB cache flush), and
+`roofline` repeats the dominant kernel. Prefill configs also time the fused
+step (xk_indexer_logits_topk -> gather, no score matrix) under `fused`, and
+the sparse attention that consumes the selection under `consumer` (not part
+of the step). `other_configs` gives the stage table of the Flash decode,
+Flash prefill and Pro decode workloads measured in the same run.
 
 Steps are replayed from HIP graphs: one graph holds a round of steps, one
 per input copy, so the timed loop measures the GPU rather than Python's or
 the graph launch's cost; before timing, replays are checked bit for bit
 against an eager step, and `ms_per_step_eager` reports eager launches too.
-A kernel's duration is timed with HIP events on the launch stream around
-replays of a graph of 20 back-to-back launches of that kernel alone
-(rotating the same input copies), so no launch gap is counted.
+A kernel's average duration is timed with HIP events on the launch stream
+around replays of a graph of 20 back-to-back launches of that kernel alone
+(rotating the input copies), so no launch gap is counted.
 
 Inputs are resident in HBM before timing starts. Several identical copies of
 q/k/w are rotated across steps so that a decode-sized working set cannot be
 served from the 256 MB last-level cache instead of HBM.
 
-    python bench.py [--steps K] [--warmup W] [--config flash_decode]
+    python bench.py [--steps K] [--warmup W] [--config long_fp8_prefill]
+    python bench.py --kernel logits [--config C] [--steps N]   (one stage only, for profilers)
 """
 from __future__ import annotations
 
@@ -43,7 +48,9 @@ sys.path.insert(0, ROOT)
 METRIC = "indexer logits TFLOP/s & top-k+mxfp4 gather GB/s, % of MI355X roofline"
 PEAK = {"hbm": 8000.0, "mfma_bf16": 2500.0, "mfma_fp8": 5000.0}   # GB/s, TFLOP/s (dense)
 FLOP_PER_PAIR = 2 * 64 * 128
-DEFAULT_CONFIG = "flash_decode"
+DEFAULT_CONFIG = "long_fp8_prefill"
+EXTRA_CONFIGS = "flash_decode,flash_prefill,pro_decode"
+FLUSH_BYTES = 512 << 20   # written before each cold dispatch: twice the 256 MB last-level cache
 
 
 def algorithmic_work(x, sel_pos=None):
@@ -104,14 +111,24 @@ def measured_traffic(config, kernel_stage):
     return vals.get(kernel_stage)
 
 
+def host_cores():
+    """Threads the numpy oracle runs on (its BLAS pool; the rest of numpy is
+    single-threaded) next to the host's cores: those this process may run
+    on, and the machine's count."""
+    affinity = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        blas = 1
+    return {"threads_used": int(min(blas, affinity)), "blas_threads": int(blas), "affinity": affinity,
+            "cpu_count": os.cpu_count()}
+
+
 def cpu_baseline(x, work, budget_s):
     """The oracle as it stands, on a bounded sample of the step's query rows."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    cores = host_cores()
     cfg = x["cfg"]
     R = cfg.rows
     order = np.random.default_rng(0).permutation(R)
@@ -149,8 +166,10 @@ def cpu_baseline(x, work, budget_s):
         step_s = total / reps
         sample = (f"{reps} whole steps ({R} query rows each: logits + top-k + gather, float64 "
                   f"numpy), {total:.1f} s")
-    return {"value": work["logits_flops"] / step_s / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle", "sample": sample, "ms_per_step": step_s * 1e3}
+    return {"value": work["logits_flops"] / step_s / 1e12, "unit": "TFLOP/s", "cores": cores["threads_used"],
+            "host_cores": cores["affinity"], "host_cpu_count": cores["cpu_count"],
+            "blas_threads": cores["blas_threads"], "kind": "oracle", "sample": sample,
+            "ms_per_step": step_s * 1e3}
 
 
 def producers(args):
@@ -234,11 +253,7 @@ def producers(args):
         "stages": stages, "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-        except Exception:
-            cores = 1
+        cores = host_cores()
         n = min(nk, 65536)
         xs = kx[:n].float().numpy()
         t0 = time.perf_counter()
@@ -248,7 +263,8 @@ def producers(args):
         oracle.mxfp4_encode_rows(xs)
         t_e = time.perf_counter() - t0
         step_s = (nq + nk) * t_q / n + nk * t_e / n
-        line["cpu_baseline"] = {"value": total_bytes / step_s / 1e9, "unit": "GB/s", "cores": int(cores),
+        line["cpu_baseline"] = {"value": total_bytes / step_s / 1e9, "unit": "GB/s", "cores": cores["threads_used"],
+                                "host_cores": cores["affinity"], "host_cpu_count": cores["cpu_count"],
                                 "kind": "oracle",
                                 "sample": f"{n} k rows quantized to fp8 ({t_q:.1f} s) and encoded to mxfp4 "
                                           f"({t_e:.1f} s), numpy, scaled to the step's q and k rows",
@@ -391,46 +407,40 @@ def copy_calibration(nbytes=1 << 30, reps=4):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default=DEFAULT_CONFIG)
-    ap.add_argument("--sets", type=int, default=0, help="input copies rotated across steps (0=auto)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a 1 GiB device copy (PMC byte-counter calibration)")
-    ap.add_argument("--producers", action="store_true",
-                    help="time the input producers (fp8 row quantizer for q and k, mxfp4 cache "
-                         "writer for k) on the config's shapes instead of the step")
-    args = ap.parse_args()
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.producers:
-        if args.gpus != 1:
-            print("bench.py measures one GPU only", file=sys.stderr)
-            sys.exit(2)
-        producers(args)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the indexer path here "
-              "is built and timed on a single MI355X.", file=sys.stderr)
-        sys.exit(2)
+def dispatch_us(torch, launches, flush=None):
+    """Duration of each launch, timed alone with an event pair on the launch
+    stream: p10/p50/p90 and mean in microseconds. With `flush` (a device
+    buffer) the buffer is overwritten before each launch, so the launch
+    starts with caches holding none of its inputs."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    vals = []
+    for i, f in enumerate(launches):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        e0.record()
+        f()
+        e1.record()
+        e1.synchronize()
+        vals.append(e0.elapsed_time(e1) * 1e3)
+    v = np.asarray(vals)
+    return {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)),
+            "p90": float(np.percentile(v, 90)), "mean": float(v.mean()), "n": int(v.size)}
 
+
+def setup(config, n_sets=0):
+    """Inputs of a config on the device and its IndexerSteps (one per input
+    copy, all writing the same outputs), after one checked eager step."""
     import torch
     import workloads
-    import sparse_attention_indexer_logits_amd as xk
     from sparse_attention_indexer_logits_amd.pipeline import IndexerStep
 
-    x = workloads.inputs(args.config)
+    x = workloads.inputs(config)
     cfg = x["cfg"]
     d = workloads.to_device(x)
     in_bytes = sum(t.numel() * t.element_size() for key, t in d.items()
                    if key in ("q", "k", "w", "kc") and t is not None)
-    n_sets = args.sets or int(min(16, max(1, -(-512 * 2 ** 20 // in_bytes))))
+    n_sets = n_sets or int(min(16, max(1, -(-512 * 2 ** 20 // in_bytes))))
+
     def make_step(q, k, w, kc, outputs=None):
         return IndexerStep(q, k, w, d["limit"], cfg.topk, d["kv_fp4"], d["kv_scale"],
                            d["block_table"], d["row_seq"], d["q_scale"], d["k_scale"],
@@ -442,7 +452,6 @@ def main():
         steps.append(make_step(d["q"].clone(), None if d["k"] is None else d["k"].clone(),
                                d["w"].clone(), None if d.get("kc") is None else d["kc"].clone(),
                                outputs=base.outputs()))
-
     # one checked pass: top-k indices must be valid positions before the gather reads them
     base.run_logits()
     base.run_topk()
@@ -453,7 +462,34 @@ def main():
         raise RuntimeError("top-k produced out-of-range indices; not running the gather")
     base.run_gather()
     torch.cuda.synchronize()
-    work = algorithmic_work(x, sel)
+    return x, d, steps, algorithmic_work(x, sel)
+
+
+def stage_entry(name, us, work, cfg):
+    """A kernel's average duration against its roof."""
+    sec = us / 1e6
+    if name == "logits" and cfg.T >= 8:
+        peak = PEAK["mfma_fp8" if cfg.dtype == "fp8" else "mfma_bf16"]
+        ach = work["logits_flops"] / sec / 1e12
+        return {"bound": "mfma", "us": us, "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                "frac": ach / peak, "frac_of_bf16_peak": ach / PEAK["mfma_bf16"],
+                "flops": work["logits_flops"]}
+    nbytes = work[f"{name}_bytes"]
+    ach = nbytes / sec / 1e9
+    return {"bound": "hbm", "us": us, "achieved": ach, "peak": PEAK["hbm"], "unit": "GB/s",
+            "frac": ach / PEAK["hbm"], "bytes": nbytes}
+
+
+def measure(args, config, full):
+    """The step of one config: graph-replayed wall time per step, each
+    kernel's average and per-dispatch durations; with `full`, also the
+    fused step, the consumer and the CPU oracle baseline."""
+    import torch
+
+    x, d, steps, work = setup(config, args.sets)
+    cfg = x["cfg"]
+    n_sets = len(steps)
+    base = steps[0]
     eager_out = [t.clone() for t in base.outputs()]
 
     for i in range(args.warmup):
@@ -480,76 +516,151 @@ def main():
             torch.cuda.synchronize()
     ms_step = time_steps(torch, graphs, round_graph, args.steps, args.warmup)
 
-    # per-kernel durations: a graph of back-to-back launches of one kernel,
+    # average durations: a graph of back-to-back launches of one kernel,
     # rotating the input copies, timed with events on the launch stream
     n_in_graph = 20
-    ms = {}
-    for name in ("logits", "topk", "gather"):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n_in_graph):
-                getattr(steps[i % n_sets], "run_" + name)()
-        g.replay()
-        torch.cuda.synchronize()
-        reps = max(1, args.steps // n_in_graph)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms[name] = e0.elapsed_time(e1) / (reps * n_in_graph)
-
-    fused = fused_timing(args, cfg, steps, n_sets, eager_out, ms) if cfg.T >= 8 and cfg.kcache is None else None
-    consumer = consumer_timing(args, x, d, steps, n_sets)
-
-    prefill = cfg.T >= 8
-    mfma_peak = PEAK["mfma_fp8" if cfg.dtype == "fp8" else "mfma_bf16"]
     stages = {}
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
     for name in ("logits", "topk", "gather"):
-        sec = ms[name] / 1e3
-        if name == "logits" and prefill:
-            ach = work["logits_flops"] / sec / 1e12
-            stages[name] = {"bound": "mfma", "us": ms[name] * 1e3, "achieved": ach,
-                            "peak": mfma_peak, "unit": "TFLOP/s", "frac": ach / mfma_peak,
-                            "frac_of_bf16_peak": ach / PEAK["mfma_bf16"]}
-        else:
-            nbytes = work[f"{name}_bytes"]
-            ach = nbytes / sec / 1e9
-            stages[name] = {"bound": "hbm", "us": ms[name] * 1e3, "achieved": ach,
-                            "peak": PEAK["hbm"], "unit": "GB/s", "frac": ach / PEAK["hbm"],
-                            "bytes": nbytes}
-    dom = max(stages, key=lambda s: stages[s]["us"])
-    roof = {k: stages[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
-    roof["kernel"] = dom
-    roof["traffic"] = measured_traffic(args.config, dom)
+        us = _graph_us(torch, [getattr(steps[i % n_sets], "run_" + name) for i in range(n_in_graph)],
+                       max(1, args.steps // n_in_graph))
+        st = stage_entry(name, us, work, cfg)
+        # each dispatch alone: warm (inputs as the step leaves them) and cold
+        # (512 MiB written first, so no cache holds the inputs)
+        n_disp = max(10, min(50, args.steps))
+        st["dispatch_warm_us"] = dispatch_us(torch, [getattr(steps[i % n_sets], "run_" + name)
+                                                     for i in range(n_disp)])
+        st["dispatch_cold_us"] = dispatch_us(torch, [getattr(steps[i % n_sets], "run_" + name)
+                                                     for i in range(n_disp)], flush)
+        stages[name] = st
+    del flush
+    if not all(torch.equal(a, b) for a, b in zip(base.outputs(), eager_out)):
+        raise RuntimeError("timed launches changed the step's outputs")
 
     tg_bytes = work["topk_bytes"] + work["gather_bytes"]
-    tg_gbps = tg_bytes / ((ms["topk"] + ms["gather"]) / 1e3) / 1e9
-    value = work["logits_flops"] / (ms_step / 1e3) / 1e12
+    tg_gbps = tg_bytes / ((stages["topk"]["us"] + stages["gather"]["us"]) / 1e6) / 1e9
+    out = {"ms_per_step": ms_step, "ms_per_step_eager": ms_step_eager, "stages": stages,
+           "topk_gather_GBps": tg_gbps, "topk_gather_frac_hbm": tg_gbps / PEAK["hbm"],
+           "logits_kernel_TFLOPs": work["logits_flops"] / (stages["logits"]["us"] / 1e6) / 1e12,
+           "value_TFLOPs": work["logits_flops"] / (ms_step / 1e3) / 1e12,
+           "input_copies_rotated": n_sets, "work": work}
+    if full:
+        ms = {k: v["us"] / 1e3 for k, v in stages.items()}
+        if cfg.T >= 8 and cfg.kcache is None:
+            fused = fused_timing(args, cfg, steps, n_sets, eager_out, ms)
+            fused["value"] = work["logits_flops"] / (fused["ms_per_step"] / 1e3) / 1e12
+            out["fused"] = fused
+        out["consumer"] = consumer_timing(args, x, d, steps, n_sets)
+    del graphs, round_graph, steps
+    return x, out
+
+
+def kernel_only(args):
+    """One stage launched --steps times back to back (eagerly), after the
+    checked step: a short program for counter runs of one kernel."""
+    import torch
+    x, d, steps, work = setup(args.config, 1)
+    s = steps[0]
+    if args.kernel == "logits_topk":
+        s.enable_fused()
+    if args.kernel == "consumer":
+        consumer_timing(args, x, d, steps, 1)
+        torch.cuda.synchronize()
+    else:
+        f = getattr(s, "run_" + args.kernel)
+        for _ in range(args.steps):
+            f()
+        torch.cuda.synchronize()
+    print(json.dumps({"kernel": args.kernel, "config": args.config, "launches": args.steps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--extra-configs", default=None,
+                    help="comma-separated configs whose stage tables join the line (default: the "
+                         f"decode and Flash prefill workloads with the default --config, none otherwise)")
+    ap.add_argument("--sets", type=int, default=0, help="input copies rotated across steps (0=auto)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (PMC byte-counter calibration)")
+    ap.add_argument("--producers", action="store_true",
+                    help="time the input producers (fp8 row quantizer for q and k, mxfp4 cache "
+                         "writer for k) on the config's shapes instead of the step")
+    ap.add_argument("--kernel", choices=("logits", "topk", "gather", "logits_topk", "consumer"),
+                    help="only launch this stage --steps times (for profiler counter runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the indexer path here "
+              "is built and timed on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.producers:
+        producers(args)
+        return
+    if args.kernel:
+        kernel_only(args)
+        return
+
+    import torch
+
+    x, res = measure(args, args.config, full=True)
+    cfg = x["cfg"]
+    stages = res["stages"]
+    dom = max(stages, key=lambda s: stages[s]["us"])
+    roof = {k: stages[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    if "frac_of_bf16_peak" in stages[dom]:
+        roof["frac_of_bf16_peak"] = stages[dom]["frac_of_bf16_peak"]
+    roof["kernel"] = dom
+    roof["traffic"] = measured_traffic(args.config, dom)
+    roof["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     line = {
-        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
-        "ms_per_step_eager": ms_step_eager, "launch": "hip_graph",
+        "metric": METRIC, "value": res["value_TFLOPs"], "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+        "ms_per_step_eager": res["ms_per_step_eager"], "launch": "hip_graph",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic: seeded numpy PCG64 inputs with the DeepSeek-V4 indexer shapes",
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "K": cfg.K, "H": 64, "D": 128,
                    "topk": cfg.topk, "qk_dtype": cfg.dtype, "limit": "causal"
                    if cfg.causal_offset is not None else "per-sequence length",
+                   "causal_offset": cfg.causal_offset,
                    "cache": "mxfp4 E2M1+E8M0, block 64",
                    "keys": "dense" if cfg.kcache is None else f"paged {cfg.kcache} cache, block 64",
-                   "input_copies_rotated": n_sets},
-        "topk_gather_GBps": tg_gbps, "topk_gather_frac_hbm": tg_gbps / PEAK["hbm"],
-        "logits_kernel_TFLOPs": work["logits_flops"] / (ms["logits"] / 1e3) / 1e12,
-        "stages": stages, "roofline": roof, "work": work,
+                   "input_copies_rotated": res["input_copies_rotated"]},
+        "topk_gather_GBps": res["topk_gather_GBps"], "topk_gather_frac_hbm": res["topk_gather_frac_hbm"],
+        "logits_kernel_TFLOPs": res["logits_kernel_TFLOPs"],
+        "stages": stages, "roofline": roof, "work": res["work"],
     }
-    if fused is not None:
-        fused["value"] = work["logits_flops"] / (fused["ms_per_step"] / 1e3) / 1e12
-        line["fused"] = fused
-    line["consumer"] = consumer
+    for k in ("fused", "consumer"):
+        if k in res:
+            line[k] = res[k]
+    extra = args.extra_configs
+    if extra is None:
+        extra = EXTRA_CONFIGS if args.config == DEFAULT_CONFIG else ""
+    others = {}
+    for name in [c for c in extra.split(",") if c and c != args.config]:
+        torch.cuda.empty_cache()
+        xo, ro = measure(args, name, full=False)
+        others[name] = {"ms_per_step": ro["ms_per_step"], "value_TFLOPs": ro["value_TFLOPs"],
+                        "topk_gather_GBps": ro["topk_gather_GBps"],
+                        "topk_gather_frac_hbm": ro["topk_gather_frac_hbm"],
+                        "input_copies_rotated": ro["input_copies_rotated"],
+                        "stages": ro["stages"], "work": ro["work"]}
+        for st, v in others[name]["stages"].items():
+            v["traffic"] = measured_traffic(name, st)
+        print(f"[bench] {name}: " + ", ".join(f"{st} {v['us']:.1f} us ({100 * v['frac']:.1f}%)"
+                                              for st, v in ro["stages"].items()), file=sys.stderr, flush=True)
+    if others:
+        line["other_configs"] = others
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(x, work, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(x, res["work"], args.cpu_budget)
     print(json.dumps(line), flush=True)
 
 
