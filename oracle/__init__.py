@@ -15,7 +15,7 @@ Pins (what checks the oracle against something other than itself) live in
 """
 from .formats import (bf16_bits_to_f64, e4m3_to_f64, e2m1_to_f64, e8m0_to_f64,
                       f64_to_bf16_bits)
-from .indexer import (indexer_logits, logits_entry, indexer_topk, topk_row, mxfp4_paged_gather,
+from .indexer import (indexer_logits, indexer_topk, topk_row, mxfp4_paged_gather,
                       paged_keys, indexer_logits_paged)
 from .quant import (e4m3_encode, e2m1_encode, quant_fp8_rows, mxfp4_encode_rows,
                     mxfp4_cache_write)
@@ -23,7 +23,7 @@ from .attention import sparse_attention
 
 __all__ = [
     "bf16_bits_to_f64", "e4m3_to_f64", "e2m1_to_f64", "e8m0_to_f64", "f64_to_bf16_bits",
-    "indexer_logits", "logits_entry", "indexer_topk", "topk_row", "mxfp4_paged_gather",
+    "indexer_logits", "indexer_topk", "topk_row", "mxfp4_paged_gather",
     "paged_keys", "indexer_logits_paged",
     "e4m3_encode", "e2m1_encode", "quant_fp8_rows", "mxfp4_encode_rows", "mxfp4_cache_write",
     "sparse_attention",

@@ -49,12 +49,6 @@ def dequant_k(k, k_scale, dtype):
     return e4m3_to_f64(k) * np.asarray(k_scale, dtype=np.float64)[..., None]
 
 
-def logits_entry(q_hat_th, k_hat_j, w_th):
-    """One score [P27]: sum over heads of w * relu(q_h . k), float64, scalar."""
-    dots = q_hat_th @ k_hat_j                  # [H]: q[t,h,:] . k[j,:]
-    return float(np.sum(w_th * np.maximum(dots, 0.0)))
-
-
 def indexer_logits(q, k, w, limit=None, q_scale=None, k_scale=None, dtype="bf16",
                    rows=None):
     """Indexer logits [B,T,K] float32 [P27].

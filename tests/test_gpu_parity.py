@@ -110,8 +110,11 @@ def assert_sel_pos_in_range(sel, x):
 
 
 # ----------------------------------------------------------------------------- configs
+# logits rows checked against the oracle (None: every row); the top-k is
+# checked on every row of every config (the oracle's selection on the GPU's
+# own logits costs a sort per row)
 CONFIG_SAMPLES = {"tiny": None, "flash_decode": None, "flash_prefill": None,
-                  "pro_decode": None, "long_fp8_prefill": 24}
+                  "pro_decode": None, "long_fp8_prefill": 128}
 
 
 @pytest.mark.parametrize("name", list(CONFIG_SAMPLES))
@@ -133,7 +136,7 @@ def test_config_chain(xk, name):
     g_idx = run_topk(xk, g_logits, d["limit"].reshape(-1), cfg.topk).cpu().numpy()
     assert not np.any(g_idx == SENT_I32)
     L2 = g_np.reshape(cfg.rows, cfg.K)
-    check_topk(g_idx, L2, lim_flat, cfg.topk, rows, name)
+    check_topk(g_idx, L2, lim_flat, cfg.topk, np.arange(cfg.rows), name)
     # selection against the oracle's own logits (P3-style Jaccard report)
     o_log = oracle.indexer_logits(x["q"], x["k"], x["w"], x["limit"], x["q_scale"], x["k_scale"],
                                   cfg.dtype, rows=[(int(r) // cfg.T, int(r) % cfg.T)

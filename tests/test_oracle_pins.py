@@ -198,18 +198,6 @@ def test_logits_invariants():
     np.testing.assert_allclose(neg[0], exp_neg.astype(np.float32), rtol=1e-6, atol=1e-5)
 
 
-def test_logits_entry_matches_row():
-    rng = np.random.default_rng(15)
-    q = _rand_bf16(rng, (1, 2, 64, 128))
-    k = _rand_bf16(rng, (1, 10, 128))
-    w = (rng.standard_normal((1, 2, 64)) / 8).astype(np.float32)
-    full = oracle.indexer_logits(q, k, w)
-    qh, kh = oracle.bf16_bits_to_f64(q), oracle.bf16_bits_to_f64(k)
-    for t in range(2):
-        for j in range(10):
-            assert np.float32(oracle.logits_entry(qh[0, t], kh[0, j], w[0, t].astype(np.float64))) == full[0, t, j]
-
-
 def test_logits_fp8_agrees_with_bf16_on_shared_values():
     """Values representable in both e4m3 and bf16 give the same scores (scale 1)."""
     rng = np.random.default_rng(16)
