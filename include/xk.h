@@ -80,8 +80,11 @@ typedef enum {
  *   logits   [B,T,K]    fp32 output; every element is written
  *   B, T, K >= 1; H must be 64 and D 128 (the DeepSeek-V4 indexer:
  *   index_n_heads 64, index_head_dim 128), else XK_ERR_UNSUPPORTED.
- * Accumulation is fp32 (MFMA); results match a float64 evaluation to
- * ~1e-6 of max|logit|.
+ * Dot products accumulate in fp32 (MFMA). bf16: the ReLU, weights and head
+ * sum run in fp32, so results match a float64 evaluation to ~1e-6 of
+ * max|logit|. fp8: each head's ReLU'd score and weight are rounded to f16
+ * before the fp32 head sum (relative error ~2^-10 per term, well inside
+ * the e4m3 inputs' own 2^-4), so results match to ~1e-3 of max|logit|.
  */
 xk_status xk_indexer_logits(const void* q, const float* q_scale,
                             const void* k, const float* k_scale,

@@ -16,17 +16,19 @@
 // The dequant scales of fp8 inputs are positive, so relu(sq*sk*x) =
 // sq*sk*relu(x): sq folds into the head weight and sk multiplies the
 // finished score. fp8 operands use the f8f6f4 MFMAs with OCP e4m3 on both
-// sides and unit block scales.
+// sides; the A block scale 2^-25 brings every e4m3 score into (-1, 1), so the
+// ReLU, the rounding to f16 and the weighted head sum take one clamped
+// packed convert and one v_dot2_f32_f16 per two heads (tile16.h).
 //
-// Two kernels, both on 16x16 tiles (v_mfma_f32_16x16x32_bf16 /
-// v_mfma_scale_f32_16x16x128_f8f6f4; a lane holds 16 heads of one key, so
-// per-query state is small):
-//  * decode  (few queries, long rows; HBM bound). A workgroup owns one query
-//    and a key chunk; each wave streams its own keys with B fragments loaded
-//    from HBM straight into registers, 16 KB of keys in flight.
+// Two kernels:
+//  * decode  (few queries, long rows; HBM bound; 16x16 tiles). A workgroup
+//    owns one query and a key chunk; each wave streams its own keys with B
+//    fragments loaded from HBM straight into registers, 16 KB in flight.
 //  * prefill (many queries; MFMA bound). A workgroup owns 4 (bf16) or 8
-//    (fp8) queries, one per wave, and a key chunk; double-buffered 64-key
-//    LDS tiles are shared by all its waves.
+//    (fp8) queries, one per wave, and a key chunk; three rotating LDS key
+//    tiles (64 bf16 or 128 fp8 keys) are shared by all its waves. bf16 runs
+//    on 16x16 tiles, fp8 on 32x32 tiles (v_mfma_scale_f32_32x32x64_f8f6f4),
+//    whose longer MFMAs leave more issue slots to the epilogue's VALU work.
 // Causal tiles that lie wholly past a query's limit are skipped and filled
 // with -inf.
 #include <math.h>
@@ -149,36 +151,21 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void logits_decode_kernel(
   }
   if (threadIdx.x < kHeads) w_lds[threadIdx.x] = wv;
   __syncthreads();
-  Frag a[4][M::kSteps];  // [M-tile][step]
-  float wr[4][4];        // head 16*mt + 4*g + i
+  // the query's A fragments and head weights, in the form every scoring
+  // kernel uses (Query16), so a key's score has the same bits here as in the
+  // prefill kernel
+  Query16<FP8> qr;
+  float wf[4][4];  // head 16*mt + 4*g + i
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
     for (int s = 0; s < M::kSteps; ++s)
-      a[mt][s] = M::load(q_lds + (16 * mt + r) * kPitch + M::dofs(s, g) * M::kElemBytes);
+      qr.a[mt][s] = M::load(q_lds + (16 * mt + r) * kPitch + M::dofs(s, g) * M::kElemBytes);
     const f32x4 w4 = *reinterpret_cast<const f32x4*>(&w_lds[16 * mt + 4 * g]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wr[mt][i] = w4[i];
+    for (int i = 0; i < 4; ++i) wf[mt][i] = w4[i];
   }
-  // this lane's 16-head partial score of key (subtile start + r)
-  auto partial = [&](const Frag (&bf)[M::kSteps]) {
-    f32x4 acc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < M::kSteps; ++s) acc[mt] = M::mma(a[mt][s], bf[s], acc[mt]);
-    }
-    float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      p0 = fmaf(wr[mt][0], fmaxf(acc[mt][0], 0.f), p0);
-      p1 = fmaf(wr[mt][1], fmaxf(acc[mt][1], 0.f), p1);
-      p0 = fmaf(wr[mt][2], fmaxf(acc[mt][2], 0.f), p0);
-      p1 = fmaf(wr[mt][3], fmaxf(acc[mt][3], 0.f), p1);
-    }
-    return p0 + p1;
-  };
+  qr.set_weights(wf);
 
   for (int j0 = 0; j0 < n_keys; j0 += 16 * kDecRing) {
 #pragma unroll
@@ -188,7 +175,7 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void logits_decode_kernel(
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const int slot = 4 * grp + st;
-        p[st] = partial(buf[slot]);
+        p[st] = qr.partial(buf[slot]);
         gload(jg + 16 * st + 16 * kDecRing, buf[slot]);  // the slot's next subtile
         // keep the refill here: sunk to the end of the loop, all refills
         // would be waited for together and the ring would not overlap
@@ -197,7 +184,7 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void logits_decode_kernel(
       const float s_key = sk[grp];
       sk[grp] = sload(jg + 16 * kDecRing);
       const float tot = subtile_total(p, lane);
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, FP8 ? tot * s_key : tot), ors,
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, qr.finish(tot, s_key)), ors,
                                             (jg + lane) * 4, 0, 0);
     }
   }
@@ -406,7 +393,8 @@ __global__ __launch_bounds__(kPagedWaves * 64, 2) void logits_paged_kernel(
 // included. The count written at the end may exceed the region's capacity
 // (entries past it are dropped); the selection kernel then has the row
 // recomputed.
-constexpr int kPrefillTile = 64;
+constexpr int kPrefillTile = 64;     // bf16 keys per LDS tile
+constexpr int kPrefillTileFp8 = 128;  // fp8 keys per LDS tile (16 KB, one barrier per two 64-key groups)
 // keys per prefill workgroup chunk are capped so that a chunk's key bytes
 // fit a buffer descriptor's 32-bit range
 constexpr int kPrefillMaxChunk = 1 << 22;
@@ -450,7 +438,10 @@ __device__ __forceinline__ void lds_load_1k(__amdgpu_buffer_rsrc_t rs, uint8_t* 
 }
 
 template <bool FP8, int NW, int NL>
-__global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
+// The second bound is the minimum number of waves per SIMD: fp8 workgroups
+// of 8 waves need 4 (128 VGPRs) for two workgroups per CU; bf16 workgroups
+// of 4 waves run three per CU.
+__global__ __launch_bounds__(NW * 64, FP8 ? 4 : 3) void logits_prefill_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const uint8_t* __restrict__ k, const float* __restrict__ k_scale,
     const float* __restrict__ w, const int32_t* __restrict__ limit,
@@ -460,13 +451,16 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
   constexpr bool kCand = NL > 0;
   constexpr int QB = NW;  // queries per workgroup, one per wave
   constexpr int kRowBytes = kHeadDim * M::kElemBytes;        // 256 (bf16) or 128 (fp8)
-  constexpr int kTileBytes = kPrefillTile * kRowBytes;
+  constexpr int kTile = FP8 ? kPrefillTileFp8 : kPrefillTile;  // keys per LDS tile
+  constexpr int kGroups = kTile / 64;                          // 64-key score groups per tile
+  constexpr int kTileBytes = kTile * kRowBytes;
   constexpr int kDma = kTileBytes / (NW * 64 * 16);           // 16-byte LDS loads per lane per tile
   static_assert(kDma >= 1 && kTileBytes % (NW * 64 * 16) == 0, "tile split");
   // vector-memory operations a wave issues in a step after the next tile's
-  // loads: the following tile's loads, the score store and (fp8) the key
+  // loads: the following tile's loads, the score stores and (fp8) the key
   // scales
-  constexpr int kAfter = kDma + 1 + (FP8 ? 1 : 0);
+  constexpr int kAfter = kDma + kGroups + (FP8 ? kGroups : 0);
+  constexpr int kTauEvery = 512 / kTile;  // candidates: tiles between bound updates
   // three tile buffers as separate arrays, so the compiler can tell the
   // buffer being read from the ones being written
   __shared__ __attribute__((aligned(16))) uint8_t tile0[kTileBytes];
@@ -499,10 +493,10 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
   // short rows are cut alike. The last part also covers the keys past the
   // block's limit (their -inf fill).
   const int row_end = min(K, blk_lim + 1);
-  const int nt_all = (max(row_end, 0) + kPrefillTile - 1) / kPrefillTile;
+  const int nt_all = (max(row_end, 0) + kTile - 1) / kTile;
   const int t_lo = int(int64_t(nt_all) * chunk / n_chunks), t_hi = int(int64_t(nt_all) * (chunk + 1) / n_chunks);
-  const int j_begin = t_lo * kPrefillTile;
-  const int j_end = chunk == n_chunks - 1 ? K : min(K, t_hi * kPrefillTile);
+  const int j_begin = t_lo * kTile;
+  const int j_end = chunk == n_chunks - 1 ? K : min(K, t_hi * kTile);
   const int c_end = min(j_end, blk_lim + 1);
 
   const int t_q = qb * QB + wave;
@@ -522,14 +516,19 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
 
   // the chunk's scored keys: loads at or past c_end read 0 without a memory
   // access (those keys' scores are never stored)
-  const int n_tiles = (c_end - j_begin + kPrefillTile - 1) / kPrefillTile;
+  const int n_tiles = (c_end - j_begin + kTile - 1) / kTile;
   const int valid_bytes = (c_end - j_begin) * kRowBytes;
   const uint8_t* kchunk = k + (b * int64_t(K) + j_begin) * kRowBytes;
   const auto srs = make_rsrc(FP8 ? k_scale + b * int64_t(K) + j_begin : nullptr, FP8 ? (c_end - j_begin) * 4 : 0);
-  // piece p of LDS row `row` holds the row's 16-byte piece p ^ swz(row);
-  // bf16 rows (16 pieces, 256 B) XOR with row % 16, fp8 rows (8 pieces,
-  // 128 B, two rows per 256 B) with (row / 2) % 8
-  auto swz = [](int row) { return FP8 ? (row >> 1) & 7 : row & 15; };
+  // piece p of LDS row `row` holds the row's 16-byte piece p ^ swz(row).
+  // A 16-byte LDS read is served 32 lanes at a time over 128 four-byte
+  // banks (512 B), so the 32 (row, piece) pairs one half-wave reads must
+  // fall in distinct 16-byte slots modulo 512 B:
+  //  bf16 rows (16 pieces, 256 B; 16 rows x one piece per read): XOR with
+  //  row % 16;
+  //  fp8 rows (8 pieces, 128 B; 32 consecutive rows x one piece per read,
+  //  rows r, r+4, ..., r+28 sharing a slot set): XOR with (row / 4) % 8.
+  auto swz = [](int row) { return FP8 ? (row >> 2) & 7 : row & 15; };
   constexpr int kPieces = kRowBytes / 16;
   // this lane's source offset (within a tile) for each of its LDS loads;
   // load i of wave w fills LDS bytes [(w*kDma + i)*1024, +1024), lane l
@@ -545,24 +544,30 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
     const int off = tix * kTileBytes;  // scalar
     lds_load_1k<kDma>(make_rsrc(kchunk + off, max(0, valid_bytes - off)), dst + wave * kDma * 1024, voff);
   };
-  // LDS offsets (within a subtile) of this lane's fragment pieces: key r of
-  // the subtile, pieces named by Mma16::dofs
-  constexpr int kRd = FP8 ? 2 : M::kSteps;
+  // LDS offsets of this lane's fragment pieces.
+  //  bf16 (16x16 tiles): key r of a 16-key subtile, pieces named by Mma16::dofs.
+  //  fp8 (32x32 tiles): key l % 32 of a 32-key block, bytes [64s + 32g, +32)
+  //  of step s (g = l / 32): pieces 4s + 2g and 4s + 2g + 1.
+  constexpr int kRd = FP8 ? 4 : M::kSteps;
   int rd[kRd];
 #pragma unroll
   for (int i = 0; i < kRd; ++i) {
-    const int piece = FP8 ? 2 * g + i : (M::dofs(i, g) * M::kElemBytes) / 16;
-    rd[i] = r * kRowBytes + ((piece ^ swz(r)) % kPieces) * 16;
+    const int row = FP8 ? (lane & 31) : r;
+    const int piece = FP8 ? 4 * (i >> 1) + 2 * (lane >> 5) + (i & 1) : (M::dofs(i, g) * M::kElemBytes) / 16;
+    rd[i] = row * kRowBytes + ((piece ^ swz(row)) % kPieces) * 16;
   }
-  auto frag_load = [&](const uint8_t* buf, int st, Frag (&f)[M::kSteps]) {
+  auto frag_load = [&](const uint8_t* buf, int st, Frag (&f)[M::kSteps]) {  // bf16 subtile st
     const uint8_t* base = buf + st * 16 * kRowBytes;
-    if constexpr (FP8) {
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(base + rd[0]);
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(base + rd[1]);
-      f[0] = Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    } else {
 #pragma unroll
-      for (int s = 0; s < M::kSteps; ++s) f[s] = M::load(base + rd[s]);
+    for (int s = 0; s < M::kSteps; ++s) f[s] = M::load(base + rd[s]);
+  };
+  auto frag32 = [&](const uint8_t* buf, int blk, i32x8 (&f)[2]) {  // fp8 32-key block blk
+    const uint8_t* base = buf + blk * 32 * kRowBytes;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(base + rd[2 * s]);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(base + rd[2 * s + 1]);
+      f[s] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };
 
@@ -579,7 +584,7 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
   // q fragments and head weights are loaded before the key tiles: memory
   // waits count in issue order, so waiting for them (at their first use)
   // must not also wait for tiles in flight
-  Query16<FP8> qr;
+  std::conditional_t<FP8, Query32, Query16<false>> qr;
   if (qvalid)
     qr.load(q + bt * (kHeads * kRowBytes), w + bt * kHeads, FP8 ? q_scale + bt * kHeads : nullptr, lane);
   else
@@ -591,43 +596,62 @@ __global__ __launch_bounds__(NW * 64, 2) void logits_prefill_kernel(
   // score tile tix (in `cur`) after starting tile tix + 2 (into `nxt`,
   // the buffer every wave finished reading before the last barrier)
   auto step = [&](const uint8_t* cur, uint8_t* nxt, int tix) {
-    if (kCand && (tix & 7) == 6) tau = fmaxf(tau, wave_min(best[kCand ? NL - 1 : 0]));
-    const int j0 = j_begin + tix * kPrefillTile;
-    float sk = 1.f;  // fp8: scale of key j0 + lane
-    if constexpr (FP8)
-      sk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, (tix * kPrefillTile + lane) * 4, 0, 0));
+    if (kCand && (tix % kTauEvery) == kTauEvery - 2) tau = fmaxf(tau, wave_min(best[kCand ? NL - 1 : 0]));
+    float sk[kGroups];  // fp8: scale of key (group start + lane)
+#pragma unroll
+    for (int h = 0; h < kGroups; ++h)
+      sk[h] = FP8 ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  srs, (tix * kTile + 64 * h + lane) * 4, 0, 0))
+                  : 1.f;
+    // the scale loads stay ahead of the tile loads: waiting for them then
+    // leaves the tile loads in flight
+    __builtin_amdgcn_sched_barrier(0);
     dma(nxt, tix + 2);
-    Frag bf[2][M::kSteps];
-    f32x4 acc[2][4];
-    float p[4];
-    frag_load(cur, 0, bf[0]);
-    qr.mma(bf[0], acc[0]);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      if (st < 3) {
-        frag_load(cur, st + 1, bf[(st + 1) & 1]);
-        qr.mma(bf[(st + 1) & 1], acc[(st + 1) & 1]);
+    for (int h = 0; h < kGroups; ++h) {
+      const uint8_t* grp = cur + h * 64 * kRowBytes;
+      float tot;
+      if constexpr (FP8) {
+        i32x8 bf[2][2];  // [block][step]
+        frag32(grp, 0, bf[0]);
+        frag32(grp, 1, bf[1]);
+        const float p0 = qr.partial(bf[0]);
+        const float p1 = qr.partial(bf[1]);
+        tot = tile_total32(p0, p1);
+      } else {
+        Frag bf[2][M::kSteps];
+        f32x4 acc[2][4];
+        float p[4];
+        frag_load(grp, 0, bf[0]);
+        qr.mma(bf[0], acc[0]);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          if (st < 3) {
+            frag_load(grp, st + 1, bf[(st + 1) & 1]);
+            qr.mma(bf[(st + 1) & 1], acc[(st + 1) & 1]);
+          }
+          p[st] = qr.epilogue(acc[st & 1]);
+        }
+        tot = subtile_total(p, lane);
       }
-      p[st] = qr.epilogue(acc[st & 1]);
-    }
-    const float tot = subtile_total(p, lane);
-    const float sc = FP8 ? tot * sk : tot;
-    if constexpr (kCand) {
-      const int j = j0 + lane;
-      const bool valid = j < q_end;
-      const float sv = valid ? sc : -INFINITY;
+      const float sc = qr.finish(tot, sk[h]);
+      const int jo = tix * kTile + 64 * h + lane;  // this lane's key, relative to j_begin
+      if constexpr (kCand) {
+        const int j = j_begin + jo;
+        const bool valid = j < q_end;
+        const float sv = valid ? sc : -INFINITY;
 #pragma unroll
-      for (int i = NL - 1; i > 0; --i) best[i] = __builtin_amdgcn_fmed3f(best[i], best[i - 1], sv);
-      best[0] = fmaxf(best[0], sv);
-      const bool pass = valid && sc >= tau;
-      const uint64_t m = __ballot(pass);
-      const int rank = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2{order_key(sc), uint32_t(j)}, ors,
-                                            pass ? (cnt + rank) * 8 : co.capc * 8, 0, 0);
-      cnt += __popcll(m);
-    } else {
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors,
-                                            (tix * kPrefillTile + lane) * 4, 0, 0);
+        for (int i = NL - 1; i > 0; --i) best[i] = __builtin_amdgcn_fmed3f(best[i], best[i - 1], sv);
+        best[0] = fmaxf(best[0], sv);
+        const bool pass = valid && sc >= tau;
+        const uint64_t m = __ballot(pass);
+        const int rank = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{order_key(sc), uint32_t(j)}, ors,
+                                              pass ? (cnt + rank) * 8 : co.capc * 8, 0, 0);
+        cnt += __popcll(m);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, jo * 4, 0, 0);
+      }
     }
     // tile tix + 1 has landed: this wave's part (only tile tix + 2's loads,
     // the store and the scale load may still be outstanding), then all waves'

@@ -1267,35 +1267,46 @@ __device__ __attribute__((noinline)) void score_row(const uint8_t* __restrict__ 
   constexpr int kRowBytes = kHeadDim * M::kElemBytes;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r = lane & 15;
-  Query16<FP8> qr;
+  // fp8 scores on 32x32 tiles, bf16 on 16x16 tiles: the prefill kernel's forms
+  std::conditional_t<FP8, Query32, Query16<false>> qr;
   qr.load(q + row * (kHeads * kRowBytes), w + row * kHeads, FP8 ? q_scale + row * kHeads : nullptr, lane);
   const auto krs = make_rsrc(kmat + b * int64_t(K) * kRowBytes, n * kRowBytes);
   const auto srs = make_rsrc(FP8 ? k_scale + b * int64_t(K) : nullptr, FP8 ? n * 4 : 0);
   const auto xrs = make_rsrc(x, n * 4);
   for (int j0 = 64 * wave; j0 < n; j0 += 64 * int(blockDim.x / 64)) {
-    float p[4];
+    float tot;
+    if constexpr (FP8) {
+      // block blk, step s: lane (l % 32, l / 32) takes bytes [64s + 32(l/32), +32) of key j0 + 32 blk + l % 32
+      float p[2];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      Frag bf[M::kSteps];
-      const int base = (j0 + 16 * st + r) * kRowBytes;
+      for (int blk = 0; blk < 2; ++blk) {
+        i32x8 bf[2];
 #pragma unroll
-      for (int s = 0; s < M::kSteps; ++s) {
-        const int off = base + M::dofs(s, g) * M::kElemBytes;
-        if constexpr (FP8) {
+        for (int s = 0; s < 2; ++s) {
+          const int off = (j0 + 32 * blk + (lane & 31)) * kRowBytes + 64 * s + 32 * (lane >> 5);
           const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
           const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 16, 0, 0);
-          bf[s] = Frag{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]),
-                       int(hi[3])};
-        } else {
-          bf[s] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+          bf[s] = i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
         }
+        p[blk] = qr.partial(bf);
       }
-      p[st] = qr.partial(bf);
+      tot = tile_total32(p[0], p[1]);
+    } else {
+      float p[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        Frag bf[M::kSteps];
+        const int base = (j0 + 16 * st + r) * kRowBytes;
+#pragma unroll
+        for (int s = 0; s < M::kSteps; ++s)
+          bf[s] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(krs, base + M::dofs(s, g) * M::kElemBytes, 0, 0));
+        p[st] = qr.partial(bf);
+      }
+      tot = subtile_total(p, lane);
     }
-    const float tot = subtile_total(p, lane);
     const float sk =
         FP8 ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, (j0 + lane) * 4, 0, 0)) : 1.f;
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, FP8 ? tot * sk : tot), xrs, (j0 + lane) * 4,
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, qr.finish(tot, sk)), xrs, (j0 + lane) * 4,
                                           0, 0);
   }
 }
