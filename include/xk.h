@@ -6,6 +6,7 @@
  *   xk_indexer_logits_paged  the same score with keys in a paged mxfp4 / fp8 cache
  *   xk_indexer_topk          deterministic per-query top-k of those scores
  *   xk_indexer_logits_topk   both at once, without the score matrix for prefill shapes
+ *   xk_indexer_logits_topk_noalloc  the same with built-in scratch, for callers that cannot allocate
  *   xk_mxfp4_paged_gather    mxfp4 paged KV rows of the selected keys, decoded to bf16
  *   xk_sparse_attention_mxfp4  attention of each query over its selected rows (the consumer)
  * and the producers of their quantized inputs:
@@ -16,8 +17,9 @@
  *   - Pointers are DEVICE pointers (hipMalloc / torch CUDA tensors) unless
  *     stated otherwise; every buffer is dense row-major with the shape given.
  *     The caller owns all memory; the library allocates nothing and keeps no
- *     state between calls (apart from a per-device "is this gfx950" cache),
- *     so calls on different streams or threads are independent.
+ *     state between calls (apart from a per-device "is this gfx950" cache
+ *     and the built-in scratch of xk_indexer_logits_topk_noalloc), so calls
+ *     on different streams or threads are independent (except that one).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). A
  *     call only enqueues kernels: outputs are valid once the stream reaches
  *     them, and inputs must stay untouched until then. Nothing synchronises.
@@ -224,6 +226,30 @@ xk_status xk_indexer_logits_topk(const void* q, const float* q_scale,
                                  const float* w, const int32_t* limit, int32_t* idx,
                                  int B, int T, int K, int H, int D, int topk, int dtype,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused indexer logits -> top-k that allocates nothing, for callers that
+ * cannot allocate device memory or cannot pass a workspace (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments and result as xk_indexer_logits_topk, without the workspace:
+ * idx is bit-for-bit what xk_indexer_logits_topk writes. Its scratch is a
+ * 64 MiB array built into the library (held on every GPU the library runs
+ * on until the process ends). Calls needing more are split into slices of
+ * whole sequences, or, when one sequence needs more, into ranges of at
+ * least 8 of its queries; sizes for which even such a slice needs more
+ * than 64 MiB (a sequence of more than ~2M keys) return XK_ERR_UNSUPPORTED
+ * before anything is enqueued. The call makes no hipMalloc, hipFree or other
+ * allocating call. Every call on one GPU uses that GPU's one array: calls
+ * that can overlap on one GPU (different streams, or threads without
+ * ordering) race and must not be issued; calls ordered on one stream are
+ * safe (nothing in the array needs to start at zero).
+ */
+xk_status xk_indexer_logits_topk_noalloc(const void* q, const float* q_scale,
+                                         const void* k, const float* k_scale,
+                                         const float* w, const int32_t* limit, int32_t* idx,
+                                         int B, int T, int K, int H, int D, int topk, int dtype,
+                                         void* stream);
 
 /*
  * mxfp4 paged KV gather.

@@ -23,6 +23,7 @@ XK_IN_FP32, XK_IN_BF16 = 0, 1
 
 EXPORTED = ("xk_indexer_logits", "xk_indexer_logits_paged", "xk_indexer_topk_workspace_size",
             "xk_indexer_topk", "xk_indexer_logits_topk_workspace_size", "xk_indexer_logits_topk",
+            "xk_indexer_logits_topk_noalloc",
             "xk_mxfp4_paged_gather", "xk_sparse_attention_mxfp4", "xk_quant_fp8_rows", "xk_mxfp4_cache_write",
             "xk_status_string", "xk_last_error")
 
@@ -51,6 +52,8 @@ def _load() -> ctypes.CDLL:
     lib.xk_indexer_logits_topk_workspace_size.restype = Z
     lib.xk_indexer_logits_topk.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P]
     lib.xk_indexer_logits_topk.restype = I
+    lib.xk_indexer_logits_topk_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.xk_indexer_logits_topk_noalloc.restype = I
     lib.xk_sparse_attention_mxfp4.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, I, I, I, I, I,
                                               I, I, I, P]
     lib.xk_sparse_attention_mxfp4.restype = I
@@ -280,6 +283,23 @@ def xk_indexer_logits_topk(q, k, w, topk: int, limit=None, q_scale=None, k_scale
     xk_indexer_logits."""
     args, out, _ = logits_topk_args(q, k, w, topk, limit, q_scale, k_scale, out, workspace)
     _check(_lib.xk_indexer_logits_topk(*args, _stream(stream)))
+    return out
+
+
+def xk_indexer_logits_topk_noalloc(q, k, w, topk: int, limit=None, q_scale=None, k_scale=None, out=None,
+                                   stream=None):
+    """xk_indexer_logits_topk without a workspace: the library's built-in
+    scratch (see include/xk.h). Same result; `out` is the only buffer."""
+    B, T, K, H, D, fp8 = _logits_inputs(q, k, w, limit, q_scale, k_scale)
+    if out is None:
+        out = torch.empty((B * T, topk), dtype=torch.int32, device=q.device)
+    _need(out, "out", (torch.int32,), 2)
+    if tuple(out.shape) != (B * T, topk):
+        raise ValueError("out must be [B*T,topk]")
+    dtype = XK_FP8_E4M3_OCP if fp8 else XK_BF16
+    _check(_lib.xk_indexer_logits_topk_noalloc(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w),
+                                               _ptr(limit), _ptr(out), B, T, K, H, D, topk, dtype,
+                                               _stream(stream)))
     return out
 
 

@@ -215,6 +215,105 @@ XK_EXPORT xk_status xk_indexer_logits_topk(const void* q, const float* q_scale, 
                   "xk_indexer_logits_topk launch");
 }
 
+// ---------------------------------------------------------------------------
+// Fused logits -> top-k for callers that cannot allocate: the workspace is
+// this file-scope device array (one per GPU, alive until the process ends).
+// Host code never passes the array's name to a kernel: its host-side symbol
+// is not a device address. The device address comes from
+// hipGetSymbolAddress, once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`.
+xk_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(XK_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(XK_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(XK_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return XK_OK;
+}
+
+// Fewest near-equal parts (sizes n / parts and its ceiling) of n items with
+// every part at least min_size and fits(size) true; 0 if there is none.
+template <class F>
+int64_t split_parts(int64_t n, int64_t min_size, F fits) {
+  for (int64_t parts = 1; parts <= n;) {
+    const int64_t lo = n / parts, hi = (n + parts - 1) / parts;
+    if (lo < min_size) return 0;
+    if (fits(lo) && fits(hi)) return parts;
+    parts += parts / 8 + 1;
+  }
+  return 0;
+}
+
+}  // namespace
+
+XK_EXPORT xk_status xk_indexer_logits_topk_noalloc(const void* q, const float* q_scale, const void* k,
+                                                   const float* k_scale, const float* w, const int32_t* limit,
+                                                   int32_t* idx, int B, int T, int K, int H, int D, int topk,
+                                                   int dtype, void* stream) {
+  xk_status s = check_logits_args(q, q_scale, k, k_scale, w, idx, B, T, K, H, D, dtype);
+  if (s != XK_OK) return s;
+  if (topk < 1) return fail(XK_ERR_INVALID_ARGUMENT, "topk must be >= 1");
+  if (topk > xk::kMaxTopk) return fail(XK_ERR_UNSUPPORTED, "topk above 2048");
+  if (int64_t(B) * T * topk > (int64_t(1) << 31) - 1) return fail(XK_ERR_UNSUPPORTED, "B*T*topk above 2^31-1");
+  const bool fp8 = dtype == XK_FP8_E4M3_OCP;
+  auto fits = [&](int64_t b, int64_t t) {
+    return xk::plan_fused(int(b), int(t), K, topk, fp8).bytes <= kNoAllocScratchBytes;
+  };
+  // Slices: groups of whole sequences when one sequence fits, else one
+  // sequence's queries in ranges of at least 8 (queries of a call with T >= 8
+  // are always scored by the prefill kernels, so every slice gives each row
+  // the bits the whole call would).
+  int64_t b_parts = split_parts(B, 1, [&](int64_t bc) { return fits(bc, T); });
+  int64_t t_parts = 1;
+  if (b_parts == 0) {
+    if (T >= 8) t_parts = split_parts(T, 8, [&](int64_t tc) { return fits(1, tc); });
+    if (T < 8 || t_parts == 0)
+      return fail(XK_ERR_UNSUPPORTED, "a slice of these sizes needs more than the " +
+                                          std::to_string(kNoAllocScratchBytes >> 20) +
+                                          " MiB of built-in scratch; use xk_indexer_logits_topk with a workspace");
+    b_parts = B;
+  }
+  s = check_device();
+  if (s != XK_OK) return s;
+  void* ws = nullptr;
+  s = scratch_address(&ws);
+  if (s != XK_OK) return s;
+  const size_t eb = fp8 ? 1 : 2;
+  const auto* q8 = static_cast<const uint8_t*>(q);
+  const auto* k8 = static_cast<const uint8_t*>(k);
+  for (int64_t bi = 0; bi < b_parts; ++bi) {
+    const int64_t b0 = B * bi / b_parts, b1 = B * (bi + 1) / b_parts;
+    for (int64_t ti = 0; ti < t_parts; ++ti) {
+      const int64_t t0 = T * ti / t_parts, t1 = T * (ti + 1) / t_parts;
+      const int64_t Bs = b1 - b0, Ts = t_parts == 1 ? T : t1 - t0;
+      const int64_t row0 = b0 * T + t0;  // first (b, t) row of the slice
+      const hipError_t e = xk::launch_logits_topk(
+          q8 + row0 * H * D * eb, fp8 ? q_scale + row0 * H : nullptr, k8 + b0 * int64_t(K) * D * eb,
+          fp8 ? k_scale + b0 * int64_t(K) : nullptr, w + row0 * H, limit ? limit + row0 : nullptr,
+          idx + row0 * topk, int(Bs), int(Ts), K, topk, fp8, ws, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return launched(e, "xk_indexer_logits_topk_noalloc launch");
+    }
+  }
+  return ok();
+}
+
 XK_EXPORT xk_status xk_mxfp4_paged_gather(const uint8_t* kv_fp4, const uint8_t* kv_scale,
                                           const int32_t* block_table, const int32_t* sel_pos,
                                           const int32_t* row_seq, uint16_t* out, int R, int k,

@@ -125,6 +125,22 @@ def test_logits_topk_validation(lib, args, status, needle):
 
 
 @pytest.mark.parametrize("args,status,needle", [
+    # (q, q_scale, k, k_scale, w, limit, idx, B, T, K, H, D, topk, dtype); every case is
+    # rejected on the host before any HIP call, so none of them touches the fake pointers
+    ((None, None, FAKE, None, FAKE, None, FAKE, 1, 8, 64, 64, 128, 4, 0), 1, "null"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 8, 64, 64, 128, 0, 0), 1, ">= 1"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 8, 64, 64, 128, 4096, 0), 2, "2048"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 8, 64, 32, 128, 4, 0), 2, "H=64"),
+    # a slice of 8 queries over 3M keys needs 96 MiB of scores: more than the built-in scratch
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 8, 3 << 20, 64, 128, 512, 0), 2, "built-in scratch"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 4, 1, 20 << 20, 64, 128, 512, 0), 2, "built-in scratch"),
+])
+def test_logits_topk_noalloc_validation(lib, args, status, needle):
+    assert lib.xk_indexer_logits_topk_noalloc(*args, None) == status
+    assert needle in lib.xk_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status,needle", [
     # (q, kv_fp4, kv_scale, block_table, sel_pos, row_seq, sink, scale, out,
     #  R, H, k, S, MB, NB, bs, D)
     ((None, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 1, 64, 4, 1, 1, 1, 64, 128), 1, "null"),
