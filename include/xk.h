@@ -20,7 +20,7 @@
  *     state between calls (apart from a per-device "is this gfx950" cache
  *     and the built-in scratch of xk_indexer_logits_topk_noalloc), so calls
  *     on different streams or threads are independent (except that one).
- *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). A
+ *   - `stream` is the caller's hipStream_t (NULL = the null stream). A
  *     call only enqueues kernels: outputs are valid once the stream reaches
  *     them, and inputs must stay untouched until then. Nothing synchronises.
  *   - Element offsets are computed in 64 bits (paged-MQA kernels on the pages
@@ -39,6 +39,7 @@
 #ifndef XK_H_
 #define XK_H_
 
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -92,7 +93,7 @@ xk_status xk_indexer_logits(const void* q, const float* q_scale,
                             const void* k, const float* k_scale,
                             const float* w, const int32_t* limit, float* logits,
                             int B, int T, int K, int H, int D,
-                            int dtype, void* stream);
+                            xk_qk_dtype dtype, hipStream_t stream);
 
 typedef enum {
   XK_KCACHE_MXFP4 = 0,        /* k_cache [NB,bs,D/2] E2M1 nibbles, k_scale [NB,bs,D/32] E8M0 */
@@ -119,14 +120,14 @@ typedef enum {
  *   k_cache      the pool above (16-byte aligned); k_scale its scales (4-byte aligned)
  *   block_table  [B,MB]    int32 physical page of each logical page
  *   logits       [B,T,K]   fp32 output, -inf past the limit; every element written
- *   H must be 64, D 128, bs a power of two >= 16, K <= MB*bs and NB*bs < 2^31,
- *   else XK_ERR_UNSUPPORTED / XK_ERR_INVALID_ARGUMENT. Pages holding a valid
+ *   bs must be a power of two and K <= MB*bs (else XK_ERR_INVALID_ARGUMENT);
+ *   H must be 64, D 128, bs >= 16 and NB*bs < 2^31 (else XK_ERR_UNSUPPORTED). Pages holding a valid
  *   position must lie in [0, NB) (not checked on the device).
  */
 xk_status xk_indexer_logits_paged(const void* q, const float* q_scale, const float* w,
                                   const int32_t* limit, const void* k_cache, const void* k_scale,
                                   const int32_t* block_table, float* logits, int B, int T, int K,
-                                  int H, int D, int MB, int NB, int bs, int kformat, void* stream);
+                                  int H, int D, int MB, int NB, int bs, xk_kcache_format kformat, hipStream_t stream);
 
 /*
  * Bytes of device workspace xk_indexer_topk needs for these sizes (may be 0).
@@ -157,7 +158,7 @@ size_t xk_indexer_topk_workspace_size(int R, int K, int k);
  */
 xk_status xk_indexer_topk(const float* logits, const int32_t* limit, int32_t* idx,
                           int R, int K, int k,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Sparse attention over the selected rows, read from the paged mxfp4 cache.
@@ -186,7 +187,7 @@ xk_status xk_sparse_attention_mxfp4(const void* q, const uint8_t* kv_fp4, const 
                                     const int32_t* block_table, const int32_t* sel_pos,
                                     const int32_t* row_seq, const float* sink, float scale,
                                     float* out, int R, int H, int k, int S, int MB, int NB, int bs,
-                                    int D, void* stream);
+                                    int D, hipStream_t stream);
 
 /*
  * Bytes of device workspace xk_indexer_logits_topk needs for these sizes.
@@ -194,7 +195,7 @@ xk_status xk_sparse_attention_mxfp4(const void* q, const uint8_t* kv_fp4, const 
  * reject. Prefill shapes need about 8 * min(K, 16384) bytes per query plus
  * up to 64 scratch rows of K scores; few-query shapes need the B*T*K scores.
  */
-size_t xk_indexer_logits_topk_workspace_size(int B, int T, int K, int k, int dtype);
+size_t xk_indexer_logits_topk_workspace_size(int B, int T, int K, int k, xk_qk_dtype dtype);
 
 /*
  * Fused indexer logits -> top-k.
@@ -224,8 +225,8 @@ size_t xk_indexer_logits_topk_workspace_size(int B, int T, int K, int k, int dty
 xk_status xk_indexer_logits_topk(const void* q, const float* q_scale,
                                  const void* k, const float* k_scale,
                                  const float* w, const int32_t* limit, int32_t* idx,
-                                 int B, int T, int K, int H, int D, int topk, int dtype,
-                                 void* workspace, size_t workspace_bytes, void* stream);
+                                 int B, int T, int K, int H, int D, int topk, xk_qk_dtype dtype,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Fused indexer logits -> top-k that allocates nothing, for callers that
@@ -248,8 +249,8 @@ xk_status xk_indexer_logits_topk(const void* q, const float* q_scale,
 xk_status xk_indexer_logits_topk_noalloc(const void* q, const float* q_scale,
                                          const void* k, const float* k_scale,
                                          const float* w, const int32_t* limit, int32_t* idx,
-                                         int B, int T, int K, int H, int D, int topk, int dtype,
-                                         void* stream);
+                                         int B, int T, int K, int H, int D, int topk, xk_qk_dtype dtype,
+                                         hipStream_t stream);
 
 /*
  * mxfp4 paged KV gather.
@@ -271,15 +272,15 @@ xk_status xk_indexer_logits_topk_noalloc(const void* q, const float* q_scale,
  *   row_seq     [R] int32       sequence of each row, or NULL (row r -> seq r,
  *                               requires R <= S)
  *   out         [R,k,D] bf16 bits (uint16), every element written
- *   bs must be a power of two, D must be 128, R*k and NB*bs must stay below
- *   2^31, else XK_ERR_UNSUPPORTED; kv_fp4 must be 4-byte aligned and out
- *   16-byte aligned.
+ *   bs must be a power of two (else XK_ERR_INVALID_ARGUMENT); D must be
+ *   128 and R*k and NB*bs must stay below 2^31, else XK_ERR_UNSUPPORTED;
+ *   kv_fp4 must be 4-byte aligned and out 16-byte aligned.
  */
 xk_status xk_mxfp4_paged_gather(const uint8_t* kv_fp4, const uint8_t* kv_scale,
                                 const int32_t* block_table, const int32_t* sel_pos,
                                 const int32_t* row_seq, uint16_t* out,
                                 int R, int k, int S, int MB, int NB, int bs, int D,
-                                void* stream);
+                                hipStream_t stream);
 
 typedef enum {
   XK_IN_FP32 = 0,  /* float32 rows          */
@@ -301,8 +302,8 @@ typedef enum {
  *   out    [N,D] e4m3 bytes (8-byte aligned); scale [N] fp32
  *   N >= 1, D must be 128 (XK_ERR_UNSUPPORTED otherwise).
  */
-xk_status xk_quant_fp8_rows(const void* x, int x_dtype, uint8_t* out, float* scale, int64_t N, int D,
-                            void* stream);
+xk_status xk_quant_fp8_rows(const void* x, xk_in_dtype x_dtype, uint8_t* out, float* scale, int64_t N, int D,
+                            hipStream_t stream);
 
 /*
  * mxfp4 cache writer: rows into the paged mxfp4 cache that
@@ -322,8 +323,8 @@ xk_status xk_quant_fp8_rows(const void* x, int x_dtype, uint8_t* out, float* sca
  *   kv_fp4   [NB,bs,D/2] u8 (4-byte aligned); kv_scale [NB,bs,D/32] u8 (in place)
  *   N >= 1, D must be 128.
  */
-xk_status xk_mxfp4_cache_write(const void* x, int x_dtype, const int64_t* slots, uint8_t* kv_fp4,
-                               uint8_t* kv_scale, int64_t N, int NB, int bs, int D, void* stream);
+xk_status xk_mxfp4_cache_write(const void* x, xk_in_dtype x_dtype, const int64_t* slots, uint8_t* kv_fp4,
+                               uint8_t* kv_scale, int64_t N, int NB, int bs, int D, hipStream_t stream);
 
 /* Static name of a status code. */
 const char* xk_status_string(xk_status status);

@@ -87,8 +87,8 @@ XK_EXPORT const char* xk_last_error(void) { return g_last_error.c_str(); }
 
 XK_EXPORT xk_status xk_indexer_logits(const void* q, const float* q_scale, const void* k,
                                       const float* k_scale, const float* w, const int32_t* limit,
-                                      float* logits, int B, int T, int K, int H, int D, int dtype,
-                                      void* stream) {
+                                      float* logits, int B, int T, int K, int H, int D, xk_qk_dtype dtype,
+                                      hipStream_t stream) {
   xk_status s = check_logits_args(q, q_scale, k, k_scale, w, logits, B, T, K, H, D, dtype);
   if (s != XK_OK) return s;
   const bool fp8 = dtype == XK_FP8_E4M3_OCP;
@@ -103,7 +103,7 @@ XK_EXPORT xk_status xk_indexer_logits_paged(const void* q, const float* q_scale,
                                             const int32_t* limit, const void* k_cache,
                                             const void* k_scale, const int32_t* block_table,
                                             float* logits, int B, int T, int K, int H, int D, int MB,
-                                            int NB, int bs, int kformat, void* stream) {
+                                            int NB, int bs, xk_kcache_format kformat, hipStream_t stream) {
   if (!q || !q_scale || !w || !k_cache || !k_scale || !block_table || !logits)
     return fail(XK_ERR_INVALID_ARGUMENT,
                 "null q, q_scale, w, k_cache, k_scale, block_table or logits");
@@ -113,8 +113,8 @@ XK_EXPORT xk_status xk_indexer_logits_paged(const void* q, const float* q_scale,
     return fail(XK_ERR_INVALID_ARGUMENT, "unknown key cache format");
   if (H != xk::kHeads || D != xk::kHeadDim)
     return fail(XK_ERR_UNSUPPORTED, "only H=64, D=128 (DeepSeek-V4 indexer) is implemented");
-  if ((bs & (bs - 1)) != 0 || bs < 16)
-    return fail(XK_ERR_UNSUPPORTED, "block size must be a power of two >= 16");
+  if ((bs & (bs - 1)) != 0) return fail(XK_ERR_INVALID_ARGUMENT, "block size must be a power of two");
+  if (bs < 16) return fail(XK_ERR_UNSUPPORTED, "block size must be >= 16 (a 16-key tile within one page)");
   if (int64_t(K) > int64_t(MB) * bs)
     return fail(XK_ERR_INVALID_ARGUMENT, "K exceeds the positions the block table maps (MB*bs)");
   if (int64_t(NB) * bs > (int64_t(1) << 31) - 1)
@@ -130,8 +130,8 @@ XK_EXPORT xk_status xk_indexer_logits_paged(const void* q, const float* q_scale,
                   "xk_indexer_logits_paged launch");
 }
 
-XK_EXPORT xk_status xk_quant_fp8_rows(const void* x, int x_dtype, uint8_t* out, float* scale,
-                                      int64_t N, int D, void* stream) {
+XK_EXPORT xk_status xk_quant_fp8_rows(const void* x, xk_in_dtype x_dtype, uint8_t* out, float* scale,
+                                      int64_t N, int D, hipStream_t stream) {
   if (!x || !out || !scale) return fail(XK_ERR_INVALID_ARGUMENT, "null x, out or scale");
   if (N < 1 || D < 1) return fail(XK_ERR_INVALID_ARGUMENT, "N, D must be >= 1");
   if (x_dtype != XK_IN_FP32 && x_dtype != XK_IN_BF16)
@@ -147,9 +147,9 @@ XK_EXPORT xk_status xk_quant_fp8_rows(const void* x, int x_dtype, uint8_t* out, 
                   "xk_quant_fp8_rows launch");
 }
 
-XK_EXPORT xk_status xk_mxfp4_cache_write(const void* x, int x_dtype, const int64_t* slots,
+XK_EXPORT xk_status xk_mxfp4_cache_write(const void* x, xk_in_dtype x_dtype, const int64_t* slots,
                                          uint8_t* kv_fp4, uint8_t* kv_scale, int64_t N, int NB,
-                                         int bs, int D, void* stream) {
+                                         int bs, int D, hipStream_t stream) {
   if (!x || !slots || !kv_fp4 || !kv_scale)
     return fail(XK_ERR_INVALID_ARGUMENT, "null x, slots, kv_fp4 or kv_scale");
   if (N < 1 || NB < 1 || bs < 1 || D < 1)
@@ -176,7 +176,7 @@ XK_EXPORT size_t xk_indexer_topk_workspace_size(int R, int K, int k) {
 
 XK_EXPORT xk_status xk_indexer_topk(const float* logits, const int32_t* limit, int32_t* idx, int R,
                                     int K, int k, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
+                                    hipStream_t stream) {
   if (!logits || !idx) return fail(XK_ERR_INVALID_ARGUMENT, "null logits or idx");
   if (R < 1 || K < 1 || k < 1) return fail(XK_ERR_INVALID_ARGUMENT, "R, K, k must be >= 1");
   if (k > xk::kMaxTopk) return fail(XK_ERR_UNSUPPORTED, "k above 2048");
@@ -189,7 +189,7 @@ XK_EXPORT xk_status xk_indexer_topk(const float* logits, const int32_t* limit, i
                   "xk_indexer_topk launch");
 }
 
-XK_EXPORT size_t xk_indexer_logits_topk_workspace_size(int B, int T, int K, int k, int dtype) {
+XK_EXPORT size_t xk_indexer_logits_topk_workspace_size(int B, int T, int K, int k, xk_qk_dtype dtype) {
   if (B < 1 || T < 1 || K < 1 || k < 1 || k > xk::kMaxTopk) return 0;
   if (dtype != XK_BF16 && dtype != XK_FP8_E4M3_OCP) return 0;
   if (int64_t(B) * T > (int64_t(1) << 30)) return 0;
@@ -198,8 +198,8 @@ XK_EXPORT size_t xk_indexer_logits_topk_workspace_size(int B, int T, int K, int 
 
 XK_EXPORT xk_status xk_indexer_logits_topk(const void* q, const float* q_scale, const void* k,
                                            const float* k_scale, const float* w, const int32_t* limit,
-                                           int32_t* idx, int B, int T, int K, int H, int D, int topk, int dtype,
-                                           void* workspace, size_t workspace_bytes, void* stream) {
+                                           int32_t* idx, int B, int T, int K, int H, int D, int topk, xk_qk_dtype dtype,
+                                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   xk_status s = check_logits_args(q, q_scale, k, k_scale, w, idx, B, T, K, H, D, dtype);
   if (s != XK_OK) return s;
   if (topk < 1) return fail(XK_ERR_INVALID_ARGUMENT, "topk must be >= 1");
@@ -266,7 +266,7 @@ int64_t split_parts(int64_t n, int64_t min_size, F fits) {
 XK_EXPORT xk_status xk_indexer_logits_topk_noalloc(const void* q, const float* q_scale, const void* k,
                                                    const float* k_scale, const float* w, const int32_t* limit,
                                                    int32_t* idx, int B, int T, int K, int H, int D, int topk,
-                                                   int dtype, void* stream) {
+                                                   xk_qk_dtype dtype, hipStream_t stream) {
   xk_status s = check_logits_args(q, q_scale, k, k_scale, w, idx, B, T, K, H, D, dtype);
   if (s != XK_OK) return s;
   if (topk < 1) return fail(XK_ERR_INVALID_ARGUMENT, "topk must be >= 1");
@@ -317,13 +317,13 @@ XK_EXPORT xk_status xk_indexer_logits_topk_noalloc(const void* q, const float* q
 XK_EXPORT xk_status xk_mxfp4_paged_gather(const uint8_t* kv_fp4, const uint8_t* kv_scale,
                                           const int32_t* block_table, const int32_t* sel_pos,
                                           const int32_t* row_seq, uint16_t* out, int R, int k,
-                                          int S, int MB, int NB, int bs, int D, void* stream) {
+                                          int S, int MB, int NB, int bs, int D, hipStream_t stream) {
   if (!kv_fp4 || !kv_scale || !block_table || !sel_pos || !out)
     return fail(XK_ERR_INVALID_ARGUMENT, "null kv_fp4, kv_scale, block_table, sel_pos or out");
   if (R < 1 || k < 1 || S < 1 || MB < 1 || NB < 1 || bs < 1 || D < 1)
     return fail(XK_ERR_INVALID_ARGUMENT, "R, k, S, MB, NB, bs, D must be >= 1");
   if (D != xk::kHeadDim) return fail(XK_ERR_UNSUPPORTED, "only D=128 is implemented");
-  if ((bs & (bs - 1)) != 0) return fail(XK_ERR_UNSUPPORTED, "block size must be a power of two");
+  if ((bs & (bs - 1)) != 0) return fail(XK_ERR_INVALID_ARGUMENT, "block size must be a power of two");
   if (!row_seq && R > S) return fail(XK_ERR_INVALID_ARGUMENT, "row_seq NULL needs R <= S");
   if (!aligned(kv_fp4, 4) || !aligned(out, 16))
     return fail(XK_ERR_INVALID_ARGUMENT, "kv_fp4 must be 4-byte and out 16-byte aligned");
@@ -342,7 +342,7 @@ XK_EXPORT xk_status xk_sparse_attention_mxfp4(const void* q, const uint8_t* kv_f
                                               const int32_t* block_table, const int32_t* sel_pos,
                                               const int32_t* row_seq, const float* sink, float scale, float* out,
                                               int R, int H, int k, int S, int MB, int NB, int bs, int D,
-                                              void* stream) {
+                                              hipStream_t stream) {
   if (!q || !kv_fp4 || !kv_scale || !block_table || !sel_pos || !out)
     return fail(XK_ERR_INVALID_ARGUMENT, "null q, kv_fp4, kv_scale, block_table, sel_pos or out");
   if (R < 1 || H < 1 || k < 1 || S < 1 || MB < 1 || NB < 1 || bs < 1 || D < 1)
@@ -352,7 +352,7 @@ XK_EXPORT xk_status xk_sparse_attention_mxfp4(const void* q, const uint8_t* kv_f
   if (D != xk::kHeadDim) return fail(XK_ERR_UNSUPPORTED, "only D=128 is implemented");
   if (H % 64 != 0) return fail(XK_ERR_UNSUPPORTED, "H must be a multiple of 64");
   if (k > 2048) return fail(XK_ERR_UNSUPPORTED, "k above 2048");
-  if ((bs & (bs - 1)) != 0) return fail(XK_ERR_UNSUPPORTED, "block size must be a power of two");
+  if ((bs & (bs - 1)) != 0) return fail(XK_ERR_INVALID_ARGUMENT, "block size must be a power of two");
   if (!row_seq && R > S) return fail(XK_ERR_INVALID_ARGUMENT, "row_seq NULL needs R <= S");
   if (int64_t(NB) * bs > (int64_t(1) << 31) - 1)
     return fail(XK_ERR_UNSUPPORTED, "NB*bs (cache tokens) above 2^31-1");

@@ -78,7 +78,7 @@ def test_logits_validation(lib, args, status, needle):
     ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 128, 1, 1, 64, 5), 1, "format"),
     ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 32, 128, 1, 1, 64, 0), 2, "H=64"),
     ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 128, 8, 1, 8, 0), 2, ">= 16"),
-    ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 48, 64, 128, 1, 1, 48, 1), 2, "power of two"),
+    ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 48, 64, 128, 1, 1, 48, 1), 1, "power of two"),
     ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 200, 64, 128, 3, 4, 64, 0), 1, "MB*bs"),
     ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 128, 1, 1 << 26, 64, 0), 2, "NB*bs"),
     ((FAKE, FAKE, FAKE, None, FAKE + 8, FAKE, FAKE, FAKE, 1, 1, 64, 64, 128, 1, 1, 64, 0), 1, "aligned"),
@@ -150,7 +150,7 @@ def test_logits_topk_noalloc_validation(lib, args, status, needle):
     ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 1, 64, 4, 1, 1, 1, 64, 64), 2, "D=128"),
     ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 1, 32, 4, 1, 1, 1, 64, 128), 2, "multiple of 64"),
     ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 1, 64, 4096, 1, 1, 1, 64, 128), 2, "2048"),
-    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 1, 64, 4, 1, 1, 1, 48, 128), 2, "power of two"),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 1, 64, 4, 1, 1, 1, 48, 128), 1, "power of two"),
     ((FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 3, 64, 4, 2, 1, 1, 64, 128), 1, "R <= S"),
     ((FAKE, FAKE + 4, FAKE, FAKE, FAKE, None, None, 1.0, FAKE, 1, 64, 4, 1, 1, 1, 64, 128), 1, "aligned"),
 ])
@@ -180,7 +180,7 @@ def test_logits_topk_workspace_sizes(lib):
     ((None, FAKE, FAKE, FAKE, None, FAKE, 1, 4, 1, 1, 1, 64, 128), 1, "null"),
     ((FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 0, 1, 1, 1, 64, 128), 1, ">= 1"),
     ((FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 4, 1, 1, 1, 64, 64), 2, "D=128"),
-    ((FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 4, 1, 1, 1, 48, 128), 2, "power of two"),
+    ((FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 4, 1, 1, 1, 48, 128), 1, "power of two"),
     ((FAKE, FAKE, FAKE, FAKE, None, FAKE, 3, 4, 2, 1, 1, 64, 128), 1, "R <= S"),
     ((FAKE + 1, FAKE, FAKE, FAKE, None, FAKE, 1, 4, 1, 1, 1, 64, 128), 1, "aligned"),
     ((FAKE, FAKE, FAKE, FAKE, None, FAKE + 4, 1, 4, 1, 1, 1, 64, 128), 1, "aligned"),
