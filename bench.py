@@ -85,30 +85,43 @@ def algorithmic_work(x, sel_pos=None):
             "topk_bytes": topk_bytes, "gather_bytes": gather_bytes, "distinct_rows": distinct}
 
 
-def source_hash():
+# the sources each stage's kernel is built from (a byte-counter summary is
+# valid only for the sources it was taken on)
+STAGE_SOURCES = {
+    "logits": ("logits.hip", "tile16.h", "xk_internal.h"),
+    "topk": ("topk.hip", "tile16.h", "xk_internal.h"),
+    "gather": ("gather.hip", "mxfp4.h", "xk_internal.h"),
+}
+
+
+def source_hash(stage=None):
+    """sha256 prefix of one stage's kernel sources (all of csrc/ without a stage)."""
+    csrc = os.path.join(ROOT, "sparse_attention_indexer_logits_amd", "csrc")
+    files = ([os.path.join(csrc, f) for f in STAGE_SOURCES[stage]] if stage
+             else sorted(glob.glob(os.path.join(csrc, "*"))))
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "sparse_attention_indexer_logits_amd", "csrc", "*"))):
+    for f in files:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(config, kernel_stage):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it
-    was taken on the current kernel sources; else None."""
+    """HBM bytes per launch of a stage's kernel from a committed rocprofv3
+    --pmc summary (profiles/traffic_<config>.txt), if it was taken on the
+    stage's current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{config}.txt")
     if not os.path.exists(path):
         return None
-    src, vals = None, {}
+    src, vals = {}, {}
     for line in open(path):
-        line = line.strip()
-        if line.startswith("kernel_source_sha:"):
-            src = line.split(":", 1)[1].strip()
-        elif line.startswith("traffic_bytes_per_launch"):
-            _, stage, v = line.split()
-            vals[stage] = float(v)
-    if src != source_hash():
+        parts = line.split()
+        if len(parts) == 3 and parts[0] == "kernel_source_sha":
+            src[parts[1]] = parts[2]
+        elif len(parts) == 3 and parts[0] == "traffic_bytes_per_launch":
+            vals[parts[1]] = float(parts[2])
+    if kernel_stage not in vals or src.get(kernel_stage) != source_hash(kernel_stage):
         return None
-    return vals.get(kernel_stage)
+    return vals[kernel_stage]
 
 
 def host_cores():
@@ -556,8 +569,8 @@ def measure(args, config, full):
 
 
 def kernel_only(args):
-    """One stage launched --steps times back to back (eagerly), after the
-    checked step: a short program for counter runs of one kernel."""
+    """One stage (or the step's three) launched --steps times back to back
+    (eagerly), after the checked step: a short program for counter runs."""
     import torch
     x, d, steps, work = setup(args.config, 1)
     s = steps[0]
@@ -567,9 +580,10 @@ def kernel_only(args):
         consumer_timing(args, x, d, steps, 1)
         torch.cuda.synchronize()
     else:
-        f = getattr(s, "run_" + args.kernel)
+        names = ("logits", "topk", "gather") if args.kernel == "step" else (args.kernel,)
         for _ in range(args.steps):
-            f()
+            for name in names:
+                getattr(s, "run_" + name)()
         torch.cuda.synchronize()
     print(json.dumps({"kernel": args.kernel, "config": args.config, "launches": args.steps}), flush=True)
 
@@ -591,8 +605,9 @@ def main():
     ap.add_argument("--producers", action="store_true",
                     help="time the input producers (fp8 row quantizer for q and k, mxfp4 cache "
                          "writer for k) on the config's shapes instead of the step")
-    ap.add_argument("--kernel", choices=("logits", "topk", "gather", "logits_topk", "consumer"),
-                    help="only launch this stage --steps times (for profiler counter runs)")
+    ap.add_argument("--kernel", choices=("logits", "topk", "gather", "step", "logits_topk", "consumer"),
+                    help="only launch this stage (step: the three stages in order) --steps times, "
+                         "for profiler counter runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the indexer path here "

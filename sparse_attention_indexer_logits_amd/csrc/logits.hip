@@ -520,15 +520,13 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 4 : 3) void logits_prefill_kernel(
   const int valid_bytes = (c_end - j_begin) * kRowBytes;
   const uint8_t* kchunk = k + (b * int64_t(K) + j_begin) * kRowBytes;
   const auto srs = make_rsrc(FP8 ? k_scale + b * int64_t(K) + j_begin : nullptr, FP8 ? (c_end - j_begin) * 4 : 0);
-  // piece p of LDS row `row` holds the row's 16-byte piece p ^ swz(row).
-  // A 16-byte LDS read is served 32 lanes at a time over 128 four-byte
-  // banks (512 B), so the 32 (row, piece) pairs one half-wave reads must
-  // fall in distinct 16-byte slots modulo 512 B:
-  //  bf16 rows (16 pieces, 256 B; 16 rows x one piece per read): XOR with
-  //  row % 16;
-  //  fp8 rows (8 pieces, 128 B; 32 consecutive rows x one piece per read,
-  //  rows r, r+4, ..., r+28 sharing a slot set): XOR with (row / 4) % 8.
-  auto swz = [](int row) { return FP8 ? (row >> 2) & 7 : row & 15; };
+  // piece p of LDS row `row` holds the row's 16-byte piece p ^ swz(row),
+  // so a fragment read (one piece of 16 or 32 consecutive rows per lane
+  // group) spreads over the banks. Measured with SQ_LDS_BANK_CONFLICT on
+  // gfx950: bf16 16x16 reads with row % 16 and fp8 32x32 reads with
+  // (row / 2) % 8 take no conflict cycles ((row / 4) % 8 takes one per read,
+  // no swizzle about six).
+  auto swz = [](int row) { return FP8 ? (row >> 1) & 7 : row & 15; };
   constexpr int kPieces = kRowBytes / 16;
   // this lane's source offset (within a tile) for each of its LDS loads;
   // load i of wave w fills LDS bytes [(w*kDma + i)*1024, +1024), lane l
