@@ -185,6 +185,58 @@ def cpu_baseline(x, work, budget_s):
             "ms_per_step": step_s * 1e3}
 
 
+def cpu_table(args):
+    """The CPU oracle per stage on the host's cores and on one thread, for the
+    tiny, Flash decode and Flash prefill workloads: whole steps where they
+    take seconds, else a bounded sample of query rows scaled by its share of
+    the step's valid pairs. One JSON line."""
+    import oracle
+    import workloads
+    from threadpoolctl import threadpool_limits
+
+    cores = host_cores()
+    table = {}
+    for name in ("tiny", "flash_decode", "flash_prefill"):
+        x = workloads.inputs(name)
+        cfg = x["cfg"]
+        R = cfg.rows
+        lim = x["limit"].reshape(-1)
+        n_valid = np.clip(lim.astype(np.int64) + 1, 0, cfg.K)
+        order = np.random.default_rng(0).permutation(R)
+        row = {}
+        n = None  # sample size, fixed by the all-cores run and reused on one thread
+        for threads in (cores["threads_used"], 1):
+            with threadpool_limits(limits=threads):
+                def run(n):
+                    rows = np.sort(order[:n])
+                    pairs = [(int(r) // cfg.T, int(r) % cfg.T) for r in rows]
+                    t = {}
+                    t0 = time.perf_counter()
+                    L = oracle.indexer_logits(x["q"], x["k"], x["w"], x["limit"], x["q_scale"], x["k_scale"],
+                                              cfg.dtype, rows=pairs).reshape(R, cfg.K)
+                    t["logits"] = time.perf_counter() - t0
+                    t0 = time.perf_counter()
+                    idx = oracle.indexer_topk(L, lim, cfg.topk, rows=rows)
+                    t["topk"] = time.perf_counter() - t0
+                    t0 = time.perf_counter()
+                    oracle.mxfp4_paged_gather(x["kv_fp4"], x["kv_scale"], x["block_table"], idx, x["row_seq"],
+                                              x["block_size"], rows=rows)
+                    t["gather"] = time.perf_counter() - t0
+                    return t, rows
+                if n is None:
+                    t1, _ = run(1)
+                    n = int(min(R, max(1, args.cpu_budget / 3 / max(sum(t1.values()), 1e-6))))
+                t, rows = run(n)
+                share = float(n_valid[rows].sum()) / max(float(n_valid.sum()), 1.0)
+                row[f"threads_{threads}"] = {
+                    "ms_per_step": {k: v / share * 1e3 for k, v in t.items()},
+                    "sample": f"{n} of {R} query rows" + ("" if n == R else ", scaled by their share of the valid pairs")}
+        table[name] = row
+    print(json.dumps({"cpu_oracle_per_stage": table, "host_cores": cores["affinity"],
+                      "host_cpu_count": cores["cpu_count"], "blas_threads": cores["blas_threads"],
+                      "kind": "oracle (float64 numpy)"}), flush=True)
+
+
 def producers(args):
     """The producers of the path's quantized inputs on a config's shapes: q
     (B*T*64 rows) and k (the valid keys) quantized per row to OCP fp8, and k
@@ -605,6 +657,9 @@ def main():
     ap.add_argument("--producers", action="store_true",
                     help="time the input producers (fp8 row quantizer for q and k, mxfp4 cache "
                          "writer for k) on the config's shapes instead of the step")
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="only time the CPU oracle per stage on all host cores and on one thread "
+                         "(tiny, Flash decode and Flash prefill workloads)")
     ap.add_argument("--kernel", choices=("logits", "topk", "gather", "step", "logits_topk", "consumer"),
                     help="only launch this stage (step: the three stages in order) --steps times, "
                          "for profiler counter runs")
@@ -615,6 +670,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.cpu_table:
+        cpu_table(args)
         return
     if args.producers:
         producers(args)
