@@ -163,10 +163,15 @@ def cpu_baseline(x, work, budget_s):
                                   x["row_seq"], x["block_size"], rows=rows)
         return time.perf_counter() - t0, rows
 
+    # the first row also pays one-time costs (dequantizing the sequence's
+    # keys), so the sample grows until it fills about the budget
     t1, _ = run(1)
     n = int(min(R, max(1, budget_s / max(t1, 1e-6))))
-    if n < R:
+    tn, rows = run(n)
+    while tn < 0.5 * budget_s and n < R:
+        n = int(min(R, max(n + 1, n * 0.8 * budget_s / max(tn, 1e-6))))
         tn, rows = run(n)
+    if n < R:
         frac = float(np.clip(x["limit"].reshape(-1)[rows] + 1, 0, cfg.K).sum()) / max(work["pairs"], 1)
         step_s = tn / max(frac, 1e-12)          # scale by the share of the step's pairs done
         sample = (f"{n} of {R} query rows (logits + top-k + gather, float64 numpy), {tn:.1f} s, "
