@@ -17,8 +17,8 @@
 // sq*sk*relu(x): sq folds into the head weight and sk multiplies the
 // finished score. fp8 operands use the f8f6f4 MFMAs with OCP e4m3 on both
 // sides; the A block scale 2^-25 brings every e4m3 score into (-1, 1), so the
-// ReLU, the rounding to f16 and the weighted head sum take one clamped
-// packed convert and one v_dot2_f32_f16 per two heads (tile16.h).
+// ReLU and the rounding to f16 take one clamped packed convert per two
+// heads, and the weighted head sum one v_fma_mix_f32 per head (tile16.h).
 //
 // Two kernels:
 //  * decode  (few queries, long rows; HBM bound; 16x16 tiles). A workgroup

@@ -67,16 +67,28 @@ __device__ __forceinline__ f16x2 relu_pk_f16(float x0, float x1) {
   return __builtin_elementwise_min(__builtin_elementwise_max(h, f16x2{0, 0}), f16x2{1, 1});
 }
 
+// acc + x * w on both f16 halves, one rounding each (v_pk_fma_f16).
+// Measured on gfx950: packed f16 FMAs issue alongside the 32x32x64 fp8
+// MFMAs, while v_dot2_f32_f16 / v_dot2c_f32_f16 do not overlap them at all
+// (even when independent of them), so the epilogue avoids the dot
+// instructions.
+__device__ __forceinline__ f16x2 pk_fma(f16x2 x, f16x2 w, f16x2 acc) { return __builtin_elementwise_fma(x, w, acc); }
+// the fp32 sum of two packed f16 partial sums
+__device__ __forceinline__ float sum4(f16x2 a, f16x2 b) { return (float(a[0]) + float(a[1])) + (float(b[0]) + float(b[1])); }
+
 // The head weights in the form the epilogue takes.
 //  bf16: fp32 weights; per head one v_max (ReLU) and one fma.
 //  fp8:  the scores arrive scaled into (-1, 1) (Mma16<true>), so one clamped
-//        f16 convert takes the ReLU of two heads and one v_dot2_f32_f16
-//        multiplies both by their weights and adds them to an fp32 sum: one
-//        VALU op per head instead of two. The weights are w * sq * 2^e rounded
-//        to nearest f16, with e putting the query's largest |w * sq| in
-//        [2^14, 2^15); `post` = 2^(25 - e) undoes both scalings exactly on the
-//        finished score. The two f16 roundings bound each head's term to a
-//        relative error of about 2^-10 (the fp8 inputs themselves carry 2^-4).
+//        f16 convert takes the ReLU of two heads, and one v_pk_fma_f16
+//        multiplies both by their f16 weights and adds them to two f16
+//        partial sums: one VALU op per head instead of two. Each partial sum
+//        takes 8 heads (4 on 16x16 tiles), and the partial sums are added in
+//        fp32. The weights are w * sq * 2^e rounded to nearest f16, with e
+//        putting the query's largest |w * sq| in [2^11, 2^12): every term is
+//        then below 2^12 and every partial sum below 2^15, inside the f16
+//        range. `post` = 2^(25 - e) undoes both scalings exactly on the
+//        finished score. Each f16 rounding is a relative error of at most
+//        2^-11 (the fp8 inputs themselves carry 2^-4).
 template <bool FP8>
 struct Query16 {
   using M = Mma16<FP8>;
@@ -97,8 +109,8 @@ struct Query16 {
       // lanes l, l^16, l^32, l^48 hold the four head groups
       m = fmaxf(m, __shfl_xor(m, 16));
       m = fmaxf(m, __shfl_xor(m, 32));
-      // m = f * 2^x with f in [0.5, 1): m * 2^(15 - x) lies in [2^14, 2^15)
-      const int e = m > 0.f ? min(max(15 - __builtin_amdgcn_frexp_expf(m), -100), 140) : 0;
+      // m = f * 2^x with f in [0.5, 1): m * 2^(12 - x) lies in [2^11, 2^12)
+      const int e = m > 0.f ? min(max(12 - __builtin_amdgcn_frexp_expf(m), -100), 140) : 0;
       post = __builtin_ldexpf(1.f, M::kScaleShift - e);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -158,11 +170,13 @@ struct Query16 {
   __device__ float epilogue(const f32x4 (&acc)[4]) const {
     float p0 = 0.f, p1 = 0.f;
     if constexpr (FP8) {
+      f16x2 h0 = {0, 0}, h1 = {0, 0};
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        p0 = __builtin_amdgcn_fdot2(relu_pk_f16(acc[mt][0], acc[mt][1]), wh[mt][0], p0, false);
-        p1 = __builtin_amdgcn_fdot2(relu_pk_f16(acc[mt][2], acc[mt][3]), wh[mt][1], p1, false);
+        h0 = pk_fma(relu_pk_f16(acc[mt][0], acc[mt][1]), wh[mt][0], h0);
+        h1 = pk_fma(relu_pk_f16(acc[mt][2], acc[mt][3]), wh[mt][1], h1);
       }
+      return sum4(h0, h1);
     } else {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -219,7 +233,7 @@ struct Query32 {
 #pragma unroll
       for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(wf[mt][e]));
     m = fmaxf(m, __shfl_xor(m, 32));  // lanes l and l^32 hold the two halves of the heads
-    const int e2 = m > 0.f ? min(max(15 - __builtin_amdgcn_frexp_expf(m), -100), 140) : 0;
+    const int e2 = m > 0.f ? min(max(12 - __builtin_amdgcn_frexp_expf(m), -100), 140) : 0;
     post = __builtin_ldexpf(1.f, M::kScaleShift - e2);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -267,12 +281,12 @@ struct Query32 {
     // keep all four MFMAs ahead of the epilogue (left alone, the scheduler
     // runs the two M-tiles one after the other through one accumulator)
     __builtin_amdgcn_sched_barrier(0);
-    float q0 = 0.f, q1 = 0.f;
+    f16x2 h0 = {0, 0}, h1 = {0, 0};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q0 = __builtin_amdgcn_fdot2(relu_pk_f16(acc0[2 * i], acc0[2 * i + 1]), wh[0][i], q0, false);
+    for (int i = 0; i < 8; ++i) h0 = pk_fma(relu_pk_f16(acc0[2 * i], acc0[2 * i + 1]), wh[0][i], h0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q1 = __builtin_amdgcn_fdot2(relu_pk_f16(acc1[2 * i], acc1[2 * i + 1]), wh[1][i], q1, false);
-    return q0 + q1;
+    for (int i = 0; i < 8; ++i) h1 = pk_fma(relu_pk_f16(acc1[2 * i], acc1[2 * i + 1]), wh[1][i], h1);
+    return sum4(h0, h1);
   }
   __device__ float finish(float tot, float sk) const { return tot * post * sk; }
 };
