@@ -53,6 +53,7 @@ namespace xk {
 namespace {
 
 constexpr int kBins = 2048;  // 11-bit digits
+constexpr int kRefreshRoom = 2048;  // list entries kept free for the chunks after a refresh check
 
 __device__ __forceinline__ int lane_id() { return int(threadIdx.x & 63); }
 
@@ -1197,6 +1198,39 @@ __device__ __forceinline__ void append_list(TopkShared<BLOCK, CAP>& sh, KeyAt ke
   }
 }
 
+// Raise a long row's bound and shrink its candidate list in place. The
+// list holds every key >= tau_f seen so far (raw score bits), at least k of
+// them; a count search over the list finds t with k <= C(t) <= k + k/8 + 64
+// list entries >= t, so the row's k-th largest key is >= t and every winner
+// seen so far stays in the list, and later keys below t can be dropped.
+// Called by the whole block with the list complete (after a barrier), when
+// it has filled past its refresh mark. Returns false (list untouched) when
+// the search finds no such t (non-finite or crowded scores).
+template <int BLOCK, int CAP>
+__device__ __forceinline__ bool refresh_list(TopkShared<BLOCK, CAP>& sh, int k, float& tau_f) {
+  constexpr int LR = CAP / BLOCK;
+  const int tid = threadIdx.x;
+  const int nc = sh.ccount;  // uniform: read after a barrier
+  float lx[LR];
+  uint32_t lj[LR];
+#pragma unroll
+  for (int u = 0; u < LR; ++u) {
+    const int i = tid + BLOCK * u;
+    lx[u] = i < nc ? __uint_as_float(sh.ckey[i]) : 0.f;
+    lj[u] = i < nc ? sh.cj[i] : 0u;
+  }
+  auto valid = [&](int u) { return tid + BLOCK * u < nc; };
+  float t = 0.f;
+  // every thread's list reads above come before the search's first barrier
+  if (!count_threshold<BLOCK, CAP, LR>(sh, lx, valid, nc, k, k + (k >> 3) + 64, t)) return false;
+  if (tid == 0) sh.ccount = 0;
+  __syncthreads();
+  append_list<BLOCK, CAP, LR>(sh, [&](int u) { return __float_as_uint(lx[u]); }, [&](int u) { return lj[u]; },
+                              [&](int u) { return valid(u) && lx[u] >= t; });
+  tau_f = fmaxf(tau_f, t);
+  return true;
+}
+
 // Longer rows. The first BLOCK*V keys are held in registers; their
 // histogram gives the bin b* that holds the prefix's k-th largest key, and
 // tau, the smallest prefix key in a bin >= b*, is at most that key. The
@@ -1205,7 +1239,11 @@ __device__ __forceinline__ void append_list(TopkShared<BLOCK, CAP>& sh, KeyAt ke
 // >= b* and the keys >= tau of the rest of the row (streamed once) form an
 // LDS candidate list, from which the winners are selected exactly. If the list runs out of room (scores
 // crowded into b*), the row falls back to multi-pass streaming selection.
-template <int BLOCK, int V, int CAP, int NBUF, bool Q4 = false>
+// REFRESH: a list that fills past CAP - kRefreshRoom entries during the
+// stream is shrunk by refresh_list, which also raises the bound; this lets
+// a list of CAP entries serve rows whose first bound admits more keys than
+// that.
+template <int BLOCK, int V, int CAP, int NBUF, bool Q4 = false, bool REFRESH = false>
 __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const float* __restrict__ x, int n,
                                               int k, int32_t* __restrict__ orow) {
   constexpr int U = 16;           // streamed entries per thread per chunk
@@ -1222,10 +1260,17 @@ __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const 
   float first[U], second[U];  // the streamed part's first chunks, in flight during the prefix's threshold
   load_chunk<BLOCK, U, Q4>(rs, prefix, first);
   if constexpr (NBUF == 3) load_chunk<BLOCK, U, Q4>(rs, prefix + BLOCK * U, second);
-  uint32_t key[V];
+  // order keys of the prefix (0 = past the row's end); held in registers
+  // unless the prefix is wide (REFRESH kernels), where they are recomputed
+  uint32_t key[REFRESH ? 1 : V];
+  if constexpr (!REFRESH) {
 #pragma unroll
-  for (int v = 0; v < V; ++v) key[v] = chunk_j<BLOCK, Q4>(0, v) < prefix ? order_key(raw[v]) : 0u;
-  auto key_at = [&](int v) { return key[v]; };
+    for (int v = 0; v < V; ++v) key[v] = chunk_j<BLOCK, Q4>(0, v) < prefix ? order_key(raw[v]) : 0u;
+  }
+  auto key_at = [&](int v) -> uint32_t {
+    if constexpr (REFRESH) return chunk_j<BLOCK, Q4>(0, v) < prefix ? order_key(raw[v]) : 0u;
+    else return key[v];
+  };
   auto j_at = [&](int v) { return uint32_t(chunk_j<BLOCK, Q4>(0, v)); };
   if (n <= prefix) {
     // entries u >= nu lie past n for every thread
@@ -1239,10 +1284,11 @@ __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const 
     sh.overflow = 0;
     sh.tau = 0xFFFFFFFFu;
   }
-  // The bound tau. Rows of at least four prefixes: a count search over the
-  // prefix (compares and block sums only) for C(tau) between k and
-  // k + k/8 + 64. Otherwise, or if it finds none, the prefix's histogram
-  // gives b* and tau is the smallest prefix key in a bin >= b*. Either way
+  // The bound tau. Rows of at least four prefixes (every row past the
+  // prefix with REFRESH): a count search over the prefix (compares and
+  // block sums only) for C(tau) between k and k + k/8 + 64. Otherwise, or
+  // if it finds none, the prefix's histogram gives b* and tau is the
+  // smallest prefix key in a bin >= b* (REFRESH: the radix path instead). Either way
   // tau is at most the prefix's k-th largest key. (Measured on the long fp8
   // rows, ~96K keys: 187.5 -> 183.2 us; on 16K-64K rows the search's looser
   // bound lets through more candidates than its cheaper start saves, and a
@@ -1251,24 +1297,33 @@ __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const 
   // them into order keys), so the stream's masked writes carry no
   // conversion.
   float tau_f = 0.f;
+  bool can_refresh = true;  // uniform: cleared when a refresh finds no bound
   const bool counted =
-      n >= 4 * prefix &&
-      count_threshold<BLOCK, CAP, V>(sh, raw, [&](int v) { return key[v] != 0u; }, prefix, min(k, prefix),
+      (REFRESH || n >= 4 * prefix) &&
+      count_threshold<BLOCK, CAP, V>(sh, raw, [&](int v) { return key_at(v) != 0u; }, prefix, min(k, prefix),
                                      min(k, prefix) + (min(k, prefix) >> 3) + 64, tau_f);
   if (counted) {
     append_list<BLOCK, CAP, V>(sh, [&](int v) { return __float_as_uint(raw[v]); }, j_at,
-                               [&](int v) { return key[v] != 0u && raw[v] >= tau_f; });
+                               [&](int v) { return key_at(v) != 0u && raw[v] >= tau_f; });
+  } else if constexpr (REFRESH) {
+    // no bound from the search (non-finite or crowded scores): the radix
+    // path (the prefix histogram's registers would not fit beside a wide
+    // prefix)
+    __syncthreads();  // the search's last LDS reads come before the radix path's writes
+    radix_topk<BLOCK, CAP>(sh, x, n, k, orow);
+    return;
   } else {
     __syncthreads();  // the search may return right after reading wlo / whi, which the histogram rewrites
     int bin[V];
     bucket_threshold<BLOCK, CAP, V>(sh, key_at, k, V, bin);
+    auto bin_at = [&](int v) { return bin[v]; };
     const int bstar = sh.digit;
     // prefix keys in bins >= b* join the list; tau, the smallest of them, is
     // at most the prefix's k-th largest key
     uint32_t mn = 0xFFFFFFFFu, unused = 0u;
-    append_list<BLOCK, CAP, V>(sh, [&](int v) { return __float_as_uint(key_value(key[v])); }, j_at, [&](int v) {
-      const bool t = bin[v] >= bstar;
-      if (t) mn = min(mn, key[v]);
+    append_list<BLOCK, CAP, V>(sh, [&](int v) { return __float_as_uint(key_value(key_at(v))); }, j_at, [&](int v) {
+      const bool t = bin_at(v) >= bstar;
+      if (t) mn = min(mn, key_at(v));
       return t;
     });
     wave_min_max(mn, unused);
@@ -1289,6 +1344,13 @@ __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const 
     else
       append_list<BLOCK, CAP, U>(sh, key_of, j_of,
                                  [&](int u) { return chunk_j<BLOCK, Q4>(base, u) < n && c[u] >= tau_f; });
+    if constexpr (REFRESH) {
+      __syncthreads();  // the chunk's appends are in: the count is uniform
+      if (can_refresh && !sh.overflow && sh.ccount > CAP - kRefreshRoom) {
+        can_refresh = refresh_list<BLOCK, CAP>(sh, k, tau_f);
+        __syncthreads();  // the shrunk list is complete before the next chunk appends
+      }
+    }
   });
   __syncthreads();
   if (!sh.overflow) {
@@ -1313,14 +1375,16 @@ __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const 
   radix_topk<BLOCK, CAP>(sh, x, n, k, orow);
 }
 
-template <int BLOCK, int V, int CAP, int NBUF = 2, bool Q4 = false>
-__global__ __launch_bounds__(BLOCK) void topk_long_kernel(const float* __restrict__ logits,
+// The second bound keeps 4 waves per SIMD (128 VGPRs): two 512-thread
+// workgroups per CU, or one of 1024.
+template <int BLOCK, int V, int CAP, int NBUF = 2, bool Q4 = false, bool REFRESH = false>
+__global__ __launch_bounds__(BLOCK, 4) void topk_long_kernel(const float* __restrict__ logits,
                                                           const int32_t* __restrict__ limit,
                                                           int32_t* __restrict__ idx, int K, int k) {
   __shared__ TopkShared<BLOCK, CAP> sh;
   const int64_t row = blockIdx.x;
   const int n = limit ? max(0, min(limit[row], K - 1) + 1) : K;
-  long_row_topk<BLOCK, V, CAP, NBUF, Q4>(sh, logits + row * K, n, k, idx + row * k);
+  long_row_topk<BLOCK, V, CAP, NBUF, Q4, REFRESH>(sh, logits + row * K, n, k, idx + row * k);
 }
 
 // ---------------------------------------------------------------------------
@@ -1470,6 +1534,7 @@ hipError_t launch_wave(const float* logits, const int32_t* limit, int32_t* idx, 
 }
 
 constexpr int kWaveMinRows = 1024;  // fewer rows leave most SIMDs idle: a workgroup per row instead
+constexpr int kLongPairRows = 512;  // rows for two long-row workgroups per CU
 
 }  // namespace
 
@@ -1484,8 +1549,15 @@ hipError_t launch_topk(const float* logits, const int32_t* limit, int32_t* idx, 
   if (K <= 256 * 16) return launch_one<256, 16, 256>(logits, limit, idx, R, K, k, stream);
   if (K <= 1024 * 8) return launch_one<1024, 8, 1024>(logits, limit, idx, R, K, k, stream);
   if (K <= 1024 * 16) return launch_one<1024, 16, 1024>(logits, limit, idx, R, K, k, stream);
-  // 16-byte loads when every row starts 16-byte aligned
-  if (K % 4 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0)
+  // 16-byte loads when every row starts 16-byte aligned. With enough rows
+  // for two workgroups per CU, 512-thread workgroups (same 16K-key prefix,
+  // 6K-entry list refreshed when it fills): one row's selection phases then
+  // overlap the other's streaming.
+  const bool q4 = K % 4 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0;
+  if (q4 && R >= kLongPairRows)
+    hipLaunchKernelGGL((topk_long_kernel<512, 32, 6144, 2, true, true>), dim3(unsigned(R)), dim3(512), 0, stream,
+                       logits, limit, idx, K, k);
+  else if (q4)
     hipLaunchKernelGGL((topk_long_kernel<1024, 16, 8192, 2, true>), dim3(unsigned(R)), dim3(1024), 0, stream,
                        logits, limit, idx, K, k);
   else

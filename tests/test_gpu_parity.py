@@ -252,6 +252,40 @@ def test_topk_heavy_ties_and_signed_zero(xk, K):
         _topk_case(xk, L, np.array([K - 1, 10, K // 3, K - 2, K // 2 + 3], np.int32), k)
 
 
+@pytest.mark.parametrize("K,k", [(98304, 1024), (98304, 2048), (40000, 512)])
+def test_topk_long_rows_paired(xk, K, k):
+    """Batches of >= 512 long rows run two 512-thread workgroups per CU with a
+    6K-entry candidate list that is shrunk (and the bound raised) when it
+    fills. Rows: plain normal, upward trends that fill the list (refresh),
+    a steep trend and an increasing row that overflow it (radix path),
+    heavy ties, all-equal, half -inf, decreasing; mixed limits."""
+    print(f"[parity] top-k long paired K={K} k={k}", flush=True)
+    rng = np.random.default_rng(K + k)
+    R = 512
+    L = rng.standard_normal((R, K)).astype(np.float32)
+    ramp = np.arange(K, dtype=np.float32) / K
+    for r in range(R):
+        kind = r % 8
+        if kind == 1:
+            L[r] += 0.5 * ramp
+        elif kind == 2:
+            L[r] += 1.0 * ramp
+        elif kind == 3:
+            L[r] += 4.0 * ramp
+        elif kind == 4:
+            L[r] = rng.choice(np.float32([0.0, -0.0, 1.0, 2.0, -1.0]), size=K)
+        elif kind == 5:
+            L[r] = np.arange(K, dtype=np.float32) if r % 16 == 5 else 3.0
+        elif kind == 6:
+            L[r, : K // 2] = -np.inf
+        elif kind == 7 and r % 16 == 7:
+            L[r] = -np.arange(K, dtype=np.float32)
+    lim = np.full(R, K - 1, np.int32)
+    lim[::5] = rng.integers(0, K, size=len(lim[::5]))
+    lim[3::11] = K + 7
+    _topk_case(xk, L, lim, k)
+
+
 def test_topk_deterministic(xk):
     rng = np.random.default_rng(3)
     L = torch.from_numpy(rng.choice(np.float32([0, 1, 2]), size=(64, 9000))).cuda()
