@@ -419,7 +419,7 @@ __device__ __forceinline__ float wave_min(float v) {
 // keeps the compiler from moving memory accesses across it
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
+  static_assert(N >= 0 && N < 64, "vmcnt field (6 bits)");
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
@@ -456,16 +456,22 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 4 : 3) void logits_prefill_kernel(
   constexpr int kTileBytes = kTile * kRowBytes;
   constexpr int kDma = kTileBytes / (NW * 64 * 16);           // 16-byte LDS loads per lane per tile
   static_assert(kDma >= 1 && kTileBytes % (NW * 64 * 16) == 0, "tile split");
-  // vector-memory operations a wave issues in a step after the next tile's
-  // loads: the following tile's loads, the score stores and (fp8) the key
-  // scales
-  constexpr int kAfter = kDma + kGroups + (FP8 ? kGroups : 0);
+  // Tile buffers in rotation: while tile t is scored, tiles t+1 .. t+kBufs-1
+  // are landing. fp8 (two workgroups per CU, 16 KB tiles) takes four, bf16
+  // (three workgroups per CU) three.
+  constexpr int kBufs = FP8 ? 4 : 3;
+  // vector-memory operations a wave may still have outstanding at the end
+  // of step t once tile t+1 has landed: those issued after tile t+1's
+  // loads, i.e. the score stores of the step that issued them and, in each
+  // later step, the key scales (fp8), the next tile's loads and the stores
+  constexpr int kAfter = kGroups + (kBufs - 2) * (kDma + kGroups + (FP8 ? kGroups : 0));
   constexpr int kTauEvery = 512 / kTile;  // candidates: tiles between bound updates
-  // three tile buffers as separate arrays, so the compiler can tell the
-  // buffer being read from the ones being written
+  // tile buffers as separate arrays, so the compiler can tell the buffer
+  // being read from the ones being written
   __shared__ __attribute__((aligned(16))) uint8_t tile0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t tile1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t tile2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tile3[kBufs == 4 ? kTileBytes : 16];
 
   // the wave index in a scalar register: per-wave values derived from it
   // (rows, buffer descriptors) then stay scalar
@@ -589,10 +595,12 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 4 : 3) void logits_prefill_kernel(
     qr.zero();
   dma(tile0, 0);
   dma(tile1, 1);
-  wait_vm_barrier<kDma>();  // tile 0 has landed (this wave's part), then all waves' parts
+  if constexpr (kBufs == 4) dma(tile2, 2);
+  // tile 0 has landed (this wave's part), then all waves' parts
+  wait_vm_barrier<(kBufs - 2) * kDma>();
 
-  // score tile tix (in `cur`) after starting tile tix + 2 (into `nxt`,
-  // the buffer every wave finished reading before the last barrier)
+  // score tile tix (in `cur`) after starting tile tix + kBufs - 1 (into
+  // `nxt`, the buffer every wave finished reading before the last barrier)
   auto step = [&](const uint8_t* cur, uint8_t* nxt, int tix) {
     if (kCand && (tix % kTauEvery) == kTauEvery - 2) tau = fmaxf(tau, wave_min(best[kCand ? NL - 1 : 0]));
     float sk[kGroups];  // fp8: scale of key (group start + lane)
@@ -604,7 +612,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 4 : 3) void logits_prefill_kernel(
     // the scale loads stay ahead of the tile loads: waiting for them then
     // leaves the tile loads in flight
     __builtin_amdgcn_sched_barrier(0);
-    dma(nxt, tix + 2);
+    dma(nxt, tix + kBufs - 1);
 #pragma unroll
     for (int h = 0; h < kGroups; ++h) {
       const uint8_t* grp = cur + h * 64 * kRowBytes;
@@ -651,18 +659,21 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 4 : 3) void logits_prefill_kernel(
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, jo * 4, 0, 0);
       }
     }
-    // tile tix + 1 has landed: this wave's part (only tile tix + 2's loads,
-    // the store and the scale load may still be outstanding), then all waves'
+    // tile tix + 1 has landed: this wave's part, then all waves'
     wait_vm_barrier<kAfter>();
   };
   // Candidates: every eighth tile the wave raises tau to its lists' minimum.
   for (int tix = 0;;) {
-    step(tile0, tile2, tix);
+    step(tile0, kBufs == 4 ? tile3 : tile2, tix);
     if (++tix >= n_tiles) break;
     step(tile1, tile0, tix);
     if (++tix >= n_tiles) break;
     step(tile2, tile1, tix);
     if (++tix >= n_tiles) break;
+    if constexpr (kBufs == 4) {
+      step(tile3, tile2, tix);
+      if (++tix >= n_tiles) break;
+    }
   }
   // no LDS load may still be in flight when the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(0);
