@@ -14,8 +14,9 @@
 // are resolved to cache tokens once (sel_pos -> block table) into LDS.
 // Then per chunk of 64 slots:
 //  * 256 threads decode the chunk's mxfp4 rows (exact, as the gather does)
-//    into a K tile [slot][d] and a transposed V tile [d][slot] in LDS; the
-//    next chunk's nibbles are loaded into registers meanwhile;
+//    into one tile [slot][d] in LDS, read as K and, through gfx950's
+//    transposing LDS load, as V^T; the next chunk's nibbles are loaded into
+//    registers meanwhile;
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (keys as rows, this wave's 16
 //    heads as columns): lane l holds head l%16's scores of keys 4(l/16)+i of
 //    each 16-key subtile;
@@ -25,7 +26,12 @@
 //    S^T registers (rounded to bf16). The contraction over keys only needs A
 //    and B to agree on the key order, so K-slot 8g+e of a 32-key step is key
 //    4g+e of its first subtile (e < 4) or of its second (e >= 4), and the V^T
-//    fragment reads the same keys (two 8-byte LDS reads).
+//    fragment holds the same keys: two ds_read_b64_tr_b16 from the [slot][d]
+//    tile. Measured lane mapping of that load: in each 16-lane group, lane
+//    i = 4a + b receives element b of the 8-byte reads of lanes a, a + 4,
+//    a + 8 and a + 12; so when lane j reads row base + (j & 15) / 4 at
+//    columns 16 mt + 4 (j & 3), lane i gets d = 16 mt + i of rows base ..
+//    base + 3.
 // At the end the sink joins the denominator and lane l stores 4 consecutive
 // outputs of head l%16 per 16-dim tile.
 #include "mxfp4.h"
@@ -35,10 +41,20 @@ namespace {
 
 constexpr int kAttnHeads = 64;              // heads per workgroup
 constexpr int kChunk = 64;                  // slots per chunk
-constexpr int kKPitch = kHeadDim + 8;       // bf16 per K-tile row (16-byte pad)
-constexpr int kVPitch = kChunk + 4;         // bf16 per V^T-tile row: 34 dwords, so the 8-byte
-                                            // fragment reads of 16 rows hit 16 distinct bank pairs
+constexpr int kKPitch = kHeadDim + 8;       // bf16 per tile row (16-byte pad)
 constexpr int kMaxAttnSlots = 2048;         // tokens resolved in LDS
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+
+// V^T fragment half: d = 16 mt + (lane & 15) of tile rows base .. base + 3
+// (the transposing load's mapping above). `kt` points into LDS.
+__device__ __forceinline__ uint2 vt_frag4(const uint16_t* kt, int base, int mt, int lane) {
+  const uint16_t* p = kt + (base + ((lane & 15) >> 2)) * kKPitch + 16 * mt + 4 * (lane & 3);
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
 
 __device__ __forceinline__ float shfl_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 16));
@@ -57,7 +73,6 @@ __global__ __launch_bounds__(256) void sparse_attention_kernel(
     float* __restrict__ out, int H, int k, int MB, int bs_log2) {
   using Frag = bf16x8;
   __shared__ __attribute__((aligned(16))) uint16_t kt[kChunk * kKPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kHeadDim * kVPitch];
   __shared__ __attribute__((aligned(16))) float sbias[kChunk];
   __shared__ int tok[kMaxAttnSlots];
 
@@ -90,8 +105,7 @@ __global__ __launch_bounds__(256) void sparse_attention_kernel(
   for (int s = 0; s < 4; ++s) qb[s] = *reinterpret_cast<const Frag*>(qrow + 32 * s + 8 * g);
   __syncthreads();
 
-  // chunk loads: thread -> slot tid%64 of the chunk, dims [32*(tid/64), +32): a
-  // wave's transposed writes then cover 64 consecutive slots of one dim
+  // chunk loads: thread -> slot tid%64 of the chunk, dims [32*(tid/64), +32)
   const int lslot = tid & 63, quarter = tid >> 6;
   auto fetch = [&](int c0, u32x4& nib, uint32_t& sc, int& t) {
     const int j = c0 + lslot;
@@ -114,7 +128,7 @@ __global__ __launch_bounds__(256) void sparse_attention_kernel(
   float m = -INFINITY, l = 0.f;  // running max (base-2 scaled) and sum of head c
 
   for (int c0 = 0; c0 < k; c0 += kChunk) {
-    // 2. decode the chunk into the K and V^T tiles
+    // 2. decode the chunk into the tile
     {
       u32x4 d[4];
 #pragma unroll
@@ -122,14 +136,6 @@ __global__ __launch_bounds__(256) void sparse_attention_kernel(
       uint16_t* krow = kt + lslot * kKPitch + 32 * quarter;
 #pragma unroll
       for (int w = 0; w < 4; ++w) reinterpret_cast<u32x4*>(krow)[w] = d[w];
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int dim = 32 * quarter + 8 * w + 2 * e;
-          vt[dim * kVPitch + lslot] = uint16_t(d[w][e] & 0xFFFFu);
-          vt[(dim + 1) * kVPitch + lslot] = uint16_t(d[w][e] >> 16);
-        }
       if (quarter == 0) sbias[lslot] = t >= 0 ? 0.f : -INFINITY;
     }
     __syncthreads();
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(256) void sparse_attention_kernel(
       // are keys 4g..4g+3 of the wave's subtile on both operands
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        const uint2 v = *reinterpret_cast<const uint2*>(vt + (16 * mt + c) * kVPitch + 16 * wave + 4 * g);
+        const uint2 v = vt_frag4(kt, 16 * wave + 4 * g, mt, lane);
         o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v), pq, o[mt], 0, 0, 0);
       }
     } else {
@@ -195,9 +201,8 @@ __global__ __launch_bounds__(256) void sparse_attention_kernel(
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-          const uint16_t* vrow = vt + (16 * mt + c) * kVPitch + 32 * ks + 4 * g;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+          const uint2 lo = vt_frag4(kt, 32 * ks + 4 * g, mt, lane);
+          const uint2 hi = vt_frag4(kt, 32 * ks + 16 + 4 * g, mt, lane);
           const Frag a = __builtin_bit_cast(Frag, u32x4{lo.x, lo.y, hi.x, hi.y});
           o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ks], o[mt], 0, 0, 0);
         }
