@@ -33,7 +33,10 @@
 //    columns 16 mt + 4 (j & 3), lane i gets d = 16 mt + i of rows base ..
 //    base + 3.
 // At the end the sink joins the denominator and lane l stores 4 consecutive
-// outputs of head l%16 per 16-dim tile.
+// outputs of head l%16 per 16-dim tile (attention_rows_kernel). Decode
+// batches, with fewer (row, 64-head) workgroups than CUs, run
+// sparse_attention_split_kernel: 16 heads per workgroup and the chunk's keys
+// split over its four waves, merged at the end.
 #include "mxfp4.h"
 
 namespace xk {
@@ -43,6 +46,7 @@ constexpr int kAttnHeads = 64;              // heads per workgroup
 constexpr int kChunk = 64;                  // slots per chunk
 constexpr int kKPitch = kHeadDim + 8;       // bf16 per tile row (16-byte pad)
 constexpr int kMaxAttnSlots = 2048;         // tokens resolved in LDS
+constexpr int kRowsHeadTiles = 1;           // 16-head tiles per wave in attention_rows_kernel
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
@@ -65,8 +69,11 @@ __device__ __forceinline__ float shfl_sum(float v) {
   return v + __shfl_xor(v, 32);
 }
 
-template <bool SPLIT>
-__global__ __launch_bounds__(256) void sparse_attention_kernel(
+// Decode batches (fewer (row, 64-head) workgroups than CUs): the workgroup
+// takes 16 heads and its four waves split every chunk's keys (wave w keys
+// 16w..16w+15), each wave running its own online softmax; the four partial
+// states are merged at the end (its 58 KB of LDS allow two per CU).
+__global__ __launch_bounds__(256) void sparse_attention_split_kernel(
     const uint16_t* __restrict__ q, const uint32_t* __restrict__ kv_fp4, const uint8_t* __restrict__ kv_scale,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ sel_pos,
     const int32_t* __restrict__ row_seq, const float* __restrict__ sink, float scale_log2,
@@ -78,14 +85,10 @@ __global__ __launch_bounds__(256) void sparse_attention_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
-  // SPLIT: the workgroup takes 16 heads and its four waves split every chunk's
-  // keys (wave w keys 16w..16w+15), each wave running its own online softmax;
-  // the four partial states are merged at the end. Otherwise each wave takes
-  // 16 of the workgroup's 64 heads over all keys.
-  constexpr int kHeadsPerWg = SPLIT ? 16 : kAttnHeads;
+  constexpr int kHeadsPerWg = 16;
   const int groups = H / kHeadsPerWg;
   const int64_t r = blockIdx.x / groups;
-  const int head = (blockIdx.x % groups) * kHeadsPerWg + (SPLIT ? 0 : 16 * wave) + c;  // this lane's head column
+  const int head = (blockIdx.x % groups) * kHeadsPerWg + c;  // this lane's head column
 
   // 1. the row's slots -> cache tokens (-1: padded slot)
   const int seq = row_seq ? row_seq[r] : int(r);
@@ -141,28 +144,23 @@ __global__ __launch_bounds__(256) void sparse_attention_kernel(
     __syncthreads();
     if (c0 + kChunk < k) fetch(c0 + kChunk, nib, sc, t);  // in flight during the MFMAs
 
-    // 3. S^T = K Q^T for this wave's heads (SPLIT: of this wave's 16 keys)
-    constexpr int NST = SPLIT ? 1 : 4;  // 16-key subtiles per wave
-    f32x4 sacc[NST];
-#pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      const int key0 = 16 * (SPLIT ? wave : st);
-      sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* arow = kt + (key0 + c) * kKPitch + 8 * g;
+    // 3. S^T = K Q^T for this wave's 16 keys
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      const uint16_t* arow = kt + (16 * wave + c) * kKPitch + 8 * g;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const Frag*>(arow + 32 * s), qb[s],
-                                                            sacc[st], 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const Frag*>(arow + 32 * s), qb[s], sacc,
+                                                       0, 0, 0);
     }
     // 4. online softmax (base 2), head c
-    float x[NST][4], cmax = -INFINITY;
-#pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sbias[16 * (SPLIT ? wave : st) + 4 * g]);
+    float x[4], cmax = -INFINITY;
+    {
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sbias[16 * wave + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[st][i] = fmaf(sacc[st][i], scale_log2, b4[i]);
-        cmax = fmaxf(cmax, x[st][i]);
+        x[i] = fmaf(sacc[i], scale_log2, b4[i]);
+        cmax = fmaxf(cmax, x[i]);
       }
     }
     cmax = shfl_max(cmax);
@@ -170,49 +168,30 @@ __global__ __launch_bounds__(256) void sparse_attention_kernel(
     const bool any = m_new > -INFINITY;
     const float alpha = any ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
     float psum = 0.f;
-    Frag pb[2];
-    s16x4 pq;  // SPLIT: this lane's probabilities (bf16 bits) of keys 4g..4g+3 of the wave's subtile
+    s16x4 pq;  // this lane's probabilities (bf16 bits) of keys 4g..4g+3 of the wave's subtile
 #pragma unroll
-    for (int st = 0; st < NST; ++st)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = any ? __builtin_amdgcn_exp2f(x[st][i] - m_new) : 0.f;
-        psum += p;
-        if constexpr (SPLIT)
-          pq[i] = __builtin_bit_cast(short, __bf16(p));
-        else
-          pb[st >> 1][4 * (st & 1) + i] = __bf16(p);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const float p = any ? __builtin_amdgcn_exp2f(x[i] - m_new) : 0.f;
+      psum += p;
+      pq[i] = __builtin_bit_cast(short, __bf16(p));
+    }
     l = fmaf(l, alpha, shfl_sum(psum));
     m = m_new;
-    // 5. O^T = O^T * alpha + V^T P^T
+    // 5. O^T = O^T * alpha + V^T P^T: one 16-key step on
+    // v_mfma_f32_16x16x16_bf16; a lane group's K slots are keys 4g..4g+3 of
+    // the wave's subtile on both operands
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
-    if constexpr (SPLIT) {
-      // one 16-key step on v_mfma_f32_16x16x16_bf16: a lane group's K slots
-      // are keys 4g..4g+3 of the wave's subtile on both operands
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const uint2 v = vt_frag4(kt, 16 * wave + 4 * g, mt, lane);
-        o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v), pq, o[mt], 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-          const uint2 lo = vt_frag4(kt, 32 * ks + 4 * g, mt, lane);
-          const uint2 hi = vt_frag4(kt, 32 * ks + 16 + 4 * g, mt, lane);
-          const Frag a = __builtin_bit_cast(Frag, u32x4{lo.x, lo.y, hi.x, hi.y});
-          o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ks], o[mt], 0, 0, 0);
-        }
-      }
+    for (int mt = 0; mt < 8; ++mt) {
+      const uint2 v = vt_frag4(kt, 16 * wave + 4 * g, mt, lane);
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v), pq, o[mt], 0, 0, 0);
     }
     __syncthreads();  // the tiles are rewritten by the next chunk
   }
 
-  if constexpr (SPLIT) {
-    // 6'. merge the four waves' states of the 16 heads, then the sink
+  {
+    // 6. merge the four waves' states of the 16 heads, then the sink
     __shared__ float cm[4][16], cl[4][16];
     __shared__ __attribute__((aligned(16))) float co[4][16][kHeadDim];
     if (g == 0) {
@@ -248,19 +227,182 @@ __global__ __launch_bounds__(256) void sparse_attention_kernel(
     float* orow = out + (r * H + hd) * int64_t(kHeadDim) + d0;
     *reinterpret_cast<f32x4*>(orow) = f32x4{acc[0], acc[1], acc[2], acc[3]} * f;
     *reinterpret_cast<f32x4*>(orow + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]} * f;
-    return;
   }
-  // 6. the sink joins the denominator; store head c's outputs
-  const float s2 = sink ? sink[head] * 1.4426950408889634f : -INFINITY;
-  const float mf = fmaxf(m, s2);
-  float f = 0.f;
-  if (mf > -INFINITY) {
-    const float a = __builtin_amdgcn_exp2f(m - mf);
-    f = a / (l * a + __builtin_amdgcn_exp2f(s2 - mf));
+}
+
+// Rows with many (row, 64-head) workgroups: HT 16-head tiles per wave,
+// 4 / HT waves per workgroup. Each K-tile or V^T fragment read from LDS
+// feeds HT MFMAs, so two tiles per wave halve the LDS reads per row; the
+// price is registers (233 VGPRs, two waves per SIMD), and measured on the
+// long prefill rows that is slower (139 against 110 us), so one tile per
+// wave (113 VGPRs, four waves per SIMD) is the launched form.
+template <int HT>
+__global__ __launch_bounds__(64 * (4 / HT), HT == 2 ? 2 : 4) void attention_rows_kernel(
+    const uint16_t* __restrict__ q, const uint32_t* __restrict__ kv_fp4, const uint8_t* __restrict__ kv_scale,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ sel_pos,
+    const int32_t* __restrict__ row_seq, const float* __restrict__ sink, float scale_log2,
+    float* __restrict__ out, int H, int k, int MB, int bs_log2) {
+  using Frag = bf16x8;
+  constexpr int NW = 4 / HT;           // waves per workgroup (64 heads)
+  constexpr int NT = 64 * NW;          // threads
+  constexpr int NQ = HT;               // 32-dim groups each thread decodes per slot
+  __shared__ __attribute__((aligned(16))) uint16_t kt[kChunk * kKPitch];
+  __shared__ __attribute__((aligned(16))) float sbias[kChunk];
+  __shared__ int tok[kMaxAttnSlots];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int groups = H / kAttnHeads;
+  const int64_t r = blockIdx.x / groups;
+  const int hbase = (blockIdx.x % groups) * kAttnHeads + 16 * HT * wave;  // head column c of tile ht: hbase + 16 ht + c
+
+  // 1. the row's slots -> cache tokens (-1: padded slot)
+  const int seq = row_seq ? row_seq[r] : int(r);
+  for (int j = tid; j < k; j += NT) {
+    const int p = sel_pos[r * k + j];
+    int t = -1;
+    if (p >= 0) {
+      const int blk = block_table[int64_t(seq) * MB + (p >> bs_log2)];
+      t = (blk << bs_log2) + (p & ((1 << bs_log2) - 1));
+    }
+    tok[j] = t;
   }
-  float* orow = out + (r * H + head) * int64_t(kHeadDim);
+  // the wave's heads as B fragments (column = head, K = d in [32s+8g, +8))
+  Frag qb[HT][4];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(orow + 16 * mt + 4 * g) = o[mt] * f;
+  for (int ht = 0; ht < HT; ++ht) {
+    const uint16_t* qrow = q + (r * H + hbase + 16 * ht + c) * int64_t(kHeadDim);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qb[ht][s] = *reinterpret_cast<const Frag*>(qrow + 32 * s + 8 * g);
+  }
+  __syncthreads();
+
+  // chunk loads: thread -> slot tid%64 of the chunk, dims [32*NQ*part, +32*NQ)
+  const int lslot = tid & 63, part = tid >> 6;
+  u32x4 nib[NQ];
+  uint32_t sc[NQ];
+  int t;
+  auto fetch = [&](int c0) {
+    const int j = c0 + lslot;
+    t = j < k ? tok[j] : -1;
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) {
+      nib[qq] = u32x4{0u, 0u, 0u, 0u};
+      sc[qq] = 0u;
+      if (t >= 0) {
+        nib[qq] = reinterpret_cast<const u32x4*>(kv_fp4)[int64_t(t) * 4 + NQ * part + qq];
+        sc[qq] = kv_scale[int64_t(t) * 4 + NQ * part + qq];
+      }
+    }
+  };
+  fetch(0);
+
+  f32x4 o[HT][8];  // O^T tile mt of head tile ht: dims 16mt + 4g + i of head c
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[ht][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[HT], l[HT];  // running max (base-2 scaled) and sum of head c of each tile
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    m[ht] = -INFINITY;
+    l[ht] = 0.f;
+  }
+
+  for (int c0 = 0; c0 < k; c0 += kChunk) {
+    // 2. decode the chunk into the tile
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) {
+      uint16_t* krow = kt + lslot * kKPitch + 32 * (NQ * part + qq);
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        reinterpret_cast<u32x4*>(krow)[w] = t >= 0 ? decode8(nib[qq][w], sc[qq]) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (part == 0) sbias[lslot] = t >= 0 ? 0.f : -INFINITY;
+    __syncthreads();
+    if (c0 + kChunk < k) fetch(c0 + kChunk);  // in flight during the MFMAs
+
+    // 3. S^T = K Q^T: each K fragment feeds the wave's HT head tiles
+    f32x4 sacc[HT][4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) sacc[ht][st] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* arow = kt + (16 * st + c) * kKPitch + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const Frag a = *reinterpret_cast<const Frag*>(arow + 32 * s);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+          sacc[ht][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ht][s], sacc[ht][st], 0, 0, 0);
+      }
+    }
+    // 4. online softmax (base 2), head c of each tile
+    Frag pb[HT][2];
+    float alpha[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      float x[4][4], cmax = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sbias[16 * st + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[st][i] = fmaf(sacc[ht][st][i], scale_log2, b4[i]);
+          cmax = fmaxf(cmax, x[st][i]);
+        }
+      }
+      cmax = shfl_max(cmax);
+      const float m_new = fmaxf(m[ht], cmax);
+      const bool any = m_new > -INFINITY;
+      alpha[ht] = any ? __builtin_amdgcn_exp2f(m[ht] - m_new) : 1.f;
+      float psum = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = any ? __builtin_amdgcn_exp2f(x[st][i] - m_new) : 0.f;
+          psum += p;
+          pb[ht][st >> 1][4 * (st & 1) + i] = __bf16(p);
+        }
+      l[ht] = fmaf(l[ht], alpha[ht], shfl_sum(psum));
+      m[ht] = m_new;
+    }
+    // 5. O^T = O^T * alpha + V^T P^T: each V^T fragment feeds HT tiles
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) o[ht][mt] *= alpha[ht];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const uint2 lo = vt_frag4(kt, 32 * ks + 4 * g, mt, lane);
+        const uint2 hi = vt_frag4(kt, 32 * ks + 16 + 4 * g, mt, lane);
+        const Frag a = __builtin_bit_cast(Frag, u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+          o[ht][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ht][ks], o[ht][mt], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // the tile is rewritten by the next chunk
+  }
+
+  // 6. the sink joins the denominator; store head c's outputs of each tile
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int head = hbase + 16 * ht + c;
+    const float s2 = sink ? sink[head] * 1.4426950408889634f : -INFINITY;
+    const float mf = fmaxf(m[ht], s2);
+    float f = 0.f;
+    if (mf > -INFINITY) {
+      const float a = __builtin_amdgcn_exp2f(m[ht] - mf);
+      f = a / (l[ht] * a + __builtin_amdgcn_exp2f(s2 - mf));
+    }
+    float* orow = out + (r * H + head) * int64_t(kHeadDim);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(orow + 16 * mt + 4 * g) = o[ht][mt] * f;
+  }
 }
 
 }  // namespace
@@ -274,13 +416,13 @@ hipError_t launch_sparse_attention(const uint16_t* q, const uint8_t* kv_fp4, con
   // Fewer (row, 64-head) workgroups than CUs (decode): 16 heads per workgroup
   // with the keys split across its waves, four times the workgroups.
   if (int64_t(R) * (H / kAttnHeads) < 256)
-    hipLaunchKernelGGL(sparse_attention_kernel<true>, dim3(unsigned(int64_t(R) * (H / 16))), dim3(256), 0, stream,
+    hipLaunchKernelGGL(sparse_attention_split_kernel, dim3(unsigned(int64_t(R) * (H / 16))), dim3(256), 0, stream,
                        q, reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale, block_table, sel_pos, row_seq, sink,
                        scale_log2, out, H, k, MB, bs_log2);
   else
-    hipLaunchKernelGGL(sparse_attention_kernel<false>, dim3(unsigned(int64_t(R) * (H / kAttnHeads))), dim3(256), 0,
-                       stream, q, reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale, block_table, sel_pos, row_seq,
-                       sink, scale_log2, out, H, k, MB, bs_log2);
+    hipLaunchKernelGGL(attention_rows_kernel<kRowsHeadTiles>, dim3(unsigned(int64_t(R) * (H / kAttnHeads))),
+                       dim3(64 * (4 / kRowsHeadTiles)), 0, stream, q, reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale,
+                       block_table, sel_pos, row_seq, sink, scale_log2, out, H, k, MB, bs_log2);
   return hipGetLastError();
 }
 
