@@ -44,7 +44,19 @@ namespace {
 
 constexpr int kAttnHeads = 64;              // heads per workgroup
 constexpr int kChunk = 64;                  // slots per chunk
-constexpr int kKPitch = kHeadDim + 8;       // bf16 per tile row (16-byte pad)
+constexpr int kKPitch = kHeadDim + 16;      // bf16 per tile row: 72 dwords
+
+// Element offset of (row, col) in a [slot][d] tile, col a multiple of 4. The
+// 16-byte piece col/8 is stored at piece ^ (row bit 3). With the 72-dword
+// pitch (8 banks per row) the three access patterns then take no bank
+// conflicts: 16-byte reads and writes of 16 consecutive rows (rows r and
+// r + 8 land 4 banks apart) and the transposing 8-byte reads of 4
+// consecutive rows times 4 column pairs per 16-lane group (8 banks per row,
+// one swizzle bit per group). A 68-dword pitch suits the first pattern only:
+// measured, its bank-conflict cycles exceeded its LDS cycles.
+__device__ __forceinline__ int tile_at(int row, int col) {
+  return row * kKPitch + (((col >> 3) ^ ((row >> 3) & 1)) << 3) + (col & 7);
+}
 constexpr int kMaxAttnSlots = 2048;         // tokens resolved in LDS
 constexpr int kRowsHeadTiles = 1;           // 16-head tiles per wave in attention_rows_kernel
 
@@ -55,7 +67,7 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 // V^T fragment half: d = 16 mt + (lane & 15) of tile rows base .. base + 3
 // (the transposing load's mapping above). `kt` points into LDS.
 __device__ __forceinline__ uint2 vt_frag4(const uint16_t* kt, int base, int mt, int lane) {
-  const uint16_t* p = kt + (base + ((lane & 15) >> 2)) * kKPitch + 16 * mt + 4 * (lane & 3);
+  const uint16_t* p = kt + tile_at(base + ((lane & 15) >> 2), 16 * mt + 4 * (lane & 3));
   const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
   return __builtin_bit_cast(uint2, v);
 }
@@ -136,9 +148,8 @@ __global__ __launch_bounds__(256) void sparse_attention_split_kernel(
       u32x4 d[4];
 #pragma unroll
       for (int w = 0; w < 4; ++w) d[w] = t >= 0 ? decode8(nib[w], sc) : u32x4{0u, 0u, 0u, 0u};
-      uint16_t* krow = kt + lslot * kKPitch + 32 * quarter;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) reinterpret_cast<u32x4*>(krow)[w] = d[w];
+      for (int w = 0; w < 4; ++w) *reinterpret_cast<u32x4*>(kt + tile_at(lslot, 32 * quarter + 8 * w)) = d[w];
       if (quarter == 0) sbias[lslot] = t >= 0 ? 0.f : -INFINITY;
     }
     __syncthreads();
@@ -147,11 +158,10 @@ __global__ __launch_bounds__(256) void sparse_attention_split_kernel(
     // 3. S^T = K Q^T for this wave's 16 keys
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-      const uint16_t* arow = kt + (16 * wave + c) * kKPitch + 8 * g;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const Frag*>(arow + 32 * s), qb[s], sacc,
-                                                       0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            *reinterpret_cast<const Frag*>(kt + tile_at(16 * wave + c, 8 * g + 32 * s)), qb[s], sacc, 0, 0, 0);
     }
     // 4. online softmax (base 2), head c
     float x[4], cmax = -INFINITY;
@@ -313,10 +323,10 @@ __global__ __launch_bounds__(64 * (4 / HT), HT == 2 ? 2 : 4) void attention_rows
     // 2. decode the chunk into the tile
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq) {
-      uint16_t* krow = kt + lslot * kKPitch + 32 * (NQ * part + qq);
 #pragma unroll
       for (int w = 0; w < 4; ++w)
-        reinterpret_cast<u32x4*>(krow)[w] = t >= 0 ? decode8(nib[qq][w], sc[qq]) : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(kt + tile_at(lslot, 32 * (NQ * part + qq) + 8 * w)) =
+            t >= 0 ? decode8(nib[qq][w], sc[qq]) : u32x4{0u, 0u, 0u, 0u};
     }
     if (part == 0) sbias[lslot] = t >= 0 ? 0.f : -INFINITY;
     __syncthreads();
@@ -328,10 +338,9 @@ __global__ __launch_bounds__(64 * (4 / HT), HT == 2 ? 2 : 4) void attention_rows
     for (int st = 0; st < 4; ++st) {
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) sacc[ht][st] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* arow = kt + (16 * st + c) * kKPitch + 8 * g;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const Frag a = *reinterpret_cast<const Frag*>(arow + 32 * s);
+        const Frag a = *reinterpret_cast<const Frag*>(kt + tile_at(16 * st + c, 8 * g + 32 * s));
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
           sacc[ht][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ht][s], sacc[ht][st], 0, 0, 0);
