@@ -394,6 +394,7 @@ __global__ __launch_bounds__(kPagedWaves * 64, 2) void logits_paged_kernel(
 // (entries past it are dropped); the selection kernel then has the row
 // recomputed.
 constexpr int kPrefillTile = 64;     // bf16 keys per LDS tile
+constexpr int kPrefillBufsFp8 = 4;    // fp8 key-tile buffers in rotation
 constexpr int kPrefillTileFp8 = 128;  // fp8 keys per LDS tile (16 KB, one barrier per two 64-key groups)
 // keys per prefill workgroup chunk are capped so that a chunk's key bytes
 // fit a buffer descriptor's 32-bit range
@@ -459,7 +460,8 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 4 : 3) void logits_prefill_kernel(
   // Tile buffers in rotation: while tile t is scored, tiles t+1 .. t+kBufs-1
   // are landing. fp8 (two workgroups per CU, 16 KB tiles) takes four, bf16
   // (three workgroups per CU) three.
-  constexpr int kBufs = FP8 ? 4 : 3;
+  constexpr int kBufs = FP8 ? kPrefillBufsFp8 : 3;
+  static_assert(kBufs >= 2 && kBufs <= 4, "two to four tile buffers");
   // vector-memory operations a wave may still have outstanding at the end
   // of step t once tile t+1 has landed: those issued after tile t+1's
   // loads, i.e. the score stores of the step that issued them and, in each
@@ -470,7 +472,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 4 : 3) void logits_prefill_kernel(
   // being read from the ones being written
   __shared__ __attribute__((aligned(16))) uint8_t tile0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t tile1[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t tile2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tile2[kBufs >= 3 ? kTileBytes : 16];
   __shared__ __attribute__((aligned(16))) uint8_t tile3[kBufs == 4 ? kTileBytes : 16];
 
   // the wave index in a scalar register: per-wave values derived from it
@@ -594,7 +596,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 4 : 3) void logits_prefill_kernel(
   else
     qr.zero();
   dma(tile0, 0);
-  dma(tile1, 1);
+  if constexpr (kBufs >= 3) dma(tile1, 1);
   if constexpr (kBufs == 4) dma(tile2, 2);
   // tile 0 has landed (this wave's part), then all waves' parts
   wait_vm_barrier<(kBufs - 2) * kDma>();
@@ -664,15 +666,22 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 4 : 3) void logits_prefill_kernel(
   };
   // Candidates: every eighth tile the wave raises tau to its lists' minimum.
   for (int tix = 0;;) {
-    step(tile0, kBufs == 4 ? tile3 : tile2, tix);
-    if (++tix >= n_tiles) break;
-    step(tile1, tile0, tix);
-    if (++tix >= n_tiles) break;
-    step(tile2, tile1, tix);
-    if (++tix >= n_tiles) break;
-    if constexpr (kBufs == 4) {
-      step(tile3, tile2, tix);
+    if constexpr (kBufs == 2) {
+      step(tile0, tile1, tix);
       if (++tix >= n_tiles) break;
+      step(tile1, tile0, tix);
+      if (++tix >= n_tiles) break;
+    } else {
+      step(tile0, kBufs == 4 ? tile3 : tile2, tix);
+      if (++tix >= n_tiles) break;
+      step(tile1, tile0, tix);
+      if (++tix >= n_tiles) break;
+      step(tile2, tile1, tix);
+      if (++tix >= n_tiles) break;
+      if constexpr (kBufs == 4) {
+        step(tile3, tile2, tix);
+        if (++tix >= n_tiles) break;
+      }
     }
   }
   // no LDS load may still be in flight when the workgroup's LDS is released
