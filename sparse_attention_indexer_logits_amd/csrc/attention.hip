@@ -59,6 +59,7 @@ __device__ __forceinline__ int tile_at(int row, int col) {
 }
 constexpr int kMaxAttnSlots = 2048;         // tokens resolved in LDS
 constexpr int kRowsHeadTiles = 1;           // 16-head tiles per wave in attention_rows_kernel
+constexpr int kRowsChunk = 64;              // slots per chunk in attention_rows_kernel
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
@@ -246,8 +247,8 @@ __global__ __launch_bounds__(256) void sparse_attention_split_kernel(
 // price is registers (233 VGPRs, two waves per SIMD), and measured on the
 // long prefill rows that is slower (139 against 110 us), so one tile per
 // wave (113 VGPRs, four waves per SIMD) is the launched form.
-template <int HT>
-__global__ __launch_bounds__(64 * (4 / HT), HT == 2 ? 2 : 4) void attention_rows_kernel(
+template <int HT, int C>
+__global__ __launch_bounds__(64 * (4 / HT), HT == 2 && C == 64 ? 2 : (HT == 2 ? 3 : 4)) void attention_rows_kernel(
     const uint16_t* __restrict__ q, const uint32_t* __restrict__ kv_fp4, const uint8_t* __restrict__ kv_scale,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ sel_pos,
     const int32_t* __restrict__ row_seq, const float* __restrict__ sink, float scale_log2,
@@ -255,9 +256,12 @@ __global__ __launch_bounds__(64 * (4 / HT), HT == 2 ? 2 : 4) void attention_rows
   using Frag = bf16x8;
   constexpr int NW = 4 / HT;           // waves per workgroup (64 heads)
   constexpr int NT = 64 * NW;          // threads
-  constexpr int NQ = HT;               // 32-dim groups each thread decodes per slot
-  __shared__ __attribute__((aligned(16))) uint16_t kt[kChunk * kKPitch];
-  __shared__ __attribute__((aligned(16))) float sbias[kChunk];
+  constexpr int NST = C / 16;          // 16-slot subtiles per chunk
+  constexpr int SPP = NT / C;          // threads per slot in the decode
+  constexpr int NQ = 4 / SPP;          // 32-dim groups each thread decodes per slot
+  static_assert(NQ >= 1 && NQ * SPP == 4, "decode split");
+  __shared__ __attribute__((aligned(16))) uint16_t kt[C * kKPitch];
+  __shared__ __attribute__((aligned(16))) float sbias[C];
   __shared__ int tok[kMaxAttnSlots];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -287,8 +291,8 @@ __global__ __launch_bounds__(64 * (4 / HT), HT == 2 ? 2 : 4) void attention_rows
   }
   __syncthreads();
 
-  // chunk loads: thread -> slot tid%64 of the chunk, dims [32*NQ*part, +32*NQ)
-  const int lslot = tid & 63, part = tid >> 6;
+  // chunk loads: thread -> slot tid%C of the chunk, dims [32*NQ*part, +32*NQ)
+  const int lslot = tid % C, part = tid / C;
   u32x4 nib[NQ];
   uint32_t sc[NQ];
   int t;
@@ -319,7 +323,7 @@ __global__ __launch_bounds__(64 * (4 / HT), HT == 2 ? 2 : 4) void attention_rows
     l[ht] = 0.f;
   }
 
-  for (int c0 = 0; c0 < k; c0 += kChunk) {
+  for (int c0 = 0; c0 < k; c0 += C) {
     // 2. decode the chunk into the tile
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq) {
@@ -330,12 +334,12 @@ __global__ __launch_bounds__(64 * (4 / HT), HT == 2 ? 2 : 4) void attention_rows
     }
     if (part == 0) sbias[lslot] = t >= 0 ? 0.f : -INFINITY;
     __syncthreads();
-    if (c0 + kChunk < k) fetch(c0 + kChunk);  // in flight during the MFMAs
+    if (c0 + C < k) fetch(c0 + C);  // in flight during the MFMAs
 
     // 3. S^T = K Q^T: each K fragment feeds the wave's HT head tiles
-    f32x4 sacc[HT][4];
+    f32x4 sacc[HT][NST];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int st = 0; st < NST; ++st) {
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) sacc[ht][st] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -347,13 +351,13 @@ __global__ __launch_bounds__(64 * (4 / HT), HT == 2 ? 2 : 4) void attention_rows
       }
     }
     // 4. online softmax (base 2), head c of each tile
-    Frag pb[HT][2];
+    Frag pb[HT][C / 32];
     float alpha[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      float x[4][4], cmax = -INFINITY;
+      float x[NST][4], cmax = -INFINITY;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
+      for (int st = 0; st < NST; ++st) {
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sbias[16 * st + 4 * g]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(64 * (4 / HT), HT == 2 ? 2 : 4) void attention_rows
       alpha[ht] = any ? __builtin_amdgcn_exp2f(m[ht] - m_new) : 1.f;
       float psum = 0.f;
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
+      for (int st = 0; st < NST; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float p = any ? __builtin_amdgcn_exp2f(x[st][i] - m_new) : 0.f;
@@ -383,7 +387,7 @@ __global__ __launch_bounds__(64 * (4 / HT), HT == 2 ? 2 : 4) void attention_rows
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) o[ht][mt] *= alpha[ht];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < C / 32; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         const uint2 lo = vt_frag4(kt, 32 * ks + 4 * g, mt, lane);
@@ -429,7 +433,7 @@ hipError_t launch_sparse_attention(const uint16_t* q, const uint8_t* kv_fp4, con
                        q, reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale, block_table, sel_pos, row_seq, sink,
                        scale_log2, out, H, k, MB, bs_log2);
   else
-    hipLaunchKernelGGL(attention_rows_kernel<kRowsHeadTiles>, dim3(unsigned(int64_t(R) * (H / kAttnHeads))),
+    hipLaunchKernelGGL((attention_rows_kernel<kRowsHeadTiles, kRowsChunk>), dim3(unsigned(int64_t(R) * (H / kAttnHeads))),
                        dim3(64 * (4 / kRowsHeadTiles)), 0, stream, q, reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale,
                        block_table, sel_pos, row_seq, sink, scale_log2, out, H, k, MB, bs_log2);
   return hipGetLastError();
