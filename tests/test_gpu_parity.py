@@ -207,6 +207,38 @@ def test_logits_edges(xk, B, T, K, lim_mode, dtype):
     check_logits(x, out.cpu().numpy(), np.arange(B * T), f"edge {B},{T},{K}")
 
 
+@pytest.mark.parametrize("T", [3, 24])  # decode and prefill kernels (both round through f16)
+def test_logits_fp8_extremes(xk, T):
+    """fp8 inputs at the edges of the f16 epilogue: e4m3 codes over every
+    finite value (scores up to 128 * 448^2, just under the 2^25 the block
+    scale maps to 1), scales spread over 2^-8 .. 2^8, head weights spanning
+    2^-40 .. 2^10 with both signs (the smallest flush to zero in f16 against
+    the largest), one query with all weights zero (its valid logits are
+    exactly 0) and one with a single nonzero weight. The contract is 5e-2 of
+    max|logit|; the f16 roundings are checked against 1e-2."""
+    print(f"[parity] logits fp8 extremes T={T}", flush=True)
+    K = 700
+    x = workloads.custom(seed=4242 + T, B=1, T=T, K=K, topk=8, dtype="fp8", causal_offset=K - T)
+    rng = np.random.default_rng(99 + T)
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)  # every finite e4m3 code
+    x["q"] = rng.choice(codes, size=x["q"].shape).astype(np.uint8)
+    x["k"] = rng.choice(codes, size=x["k"].shape).astype(np.uint8)
+    x["k"][0, : K // 8] = 0x7E                            # +448 rows: the largest scores
+    x["q_scale"] = np.exp2(rng.uniform(-8, 8, size=x["q_scale"].shape)).astype(np.float32)
+    x["k_scale"] = np.exp2(rng.uniform(-8, 8, size=x["k_scale"].shape)).astype(np.float32)
+    w = np.exp2(rng.uniform(-40, 10, size=x["w"].shape)) * rng.choice([-1.0, 1.0], size=x["w"].shape)
+    w[0, 0] = 0.0
+    w[0, 1] = 0.0
+    w[0, 1, 5] = 3.0
+    x["w"] = w.astype(np.float32)
+    d = workloads.to_device(x)
+    g = run_logits(xk, x, d).cpu().numpy()
+    err = check_logits(x, g, np.arange(T), f"fp8 extremes T={T}")
+    assert err <= 1e-2, f"fp8 extremes: rel err {err:.3e}"
+    n0 = int(x["limit"][0, 0]) + 1
+    assert np.all(g[0, 0, :n0] == 0.0), "all-zero weights must give exact zeros"
+
+
 def test_logits_deterministic(xk):
     x = workloads.custom(seed=77, B=1, T=40, K=777, dtype="bf16", causal_offset=700)
     d = workloads.to_device(x)
