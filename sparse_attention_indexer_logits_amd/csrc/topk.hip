@@ -625,7 +625,8 @@ __device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t rs, int base, 
     static_assert(U % 4 == 0, "whole quads");
 #pragma unroll
     for (int i = 0; i < U / 4; ++i) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, chunk_j<BLOCK, true>(base, 4 * i) * 4, 0, 0);
+      // Non-temporal: each score is read once; caching it only evicts lines still in use.
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, chunk_j<BLOCK, true>(base, 4 * i) * 4, 0, 2);
 #pragma unroll
       for (int e = 0; e < 4; ++e) c[4 * i + e] = __uint_as_float(v[e]);
     }
@@ -872,7 +873,7 @@ __device__ __forceinline__ bool wave_row_topk(WaveRowShared& sh, const float* __
   float xs[V];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rs, (256 * i + 4 * lane) * 4, 0, 0);
+    const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rs, (256 * i + 4 * lane) * 4, 0, 2);  // read once: non-temporal
 #pragma unroll
     for (int c = 0; c < 4; ++c) xs[4 * i + c] = __uint_as_float(r[c]);
   }
