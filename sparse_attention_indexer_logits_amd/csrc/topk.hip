@@ -1170,6 +1170,85 @@ __device__ __forceinline__ bool count_threshold(TopkShared<BLOCK, CAP>& sh, cons
   return false;
 }
 
+// count_threshold for entries that all lie inside the row (a long row's
+// prefix): no validity test per entry, the range from float min / max
+// (v_min3 / v_max3), and the first probe's mean and variance from every
+// fourth entry. A prefix with a non-finite score (or NaN) goes through
+// count_threshold, which keeps such scores out of the range and moments.
+template <int BLOCK, int CAP, int V>
+__device__ __forceinline__ bool count_threshold_dense(TopkShared<BLOCK, CAP>& sh, const float (&x)[V], int m,
+                                                      int need, int goal, float& tau) {
+  constexpr int kSteps = 8;
+  static_assert(V % 4 == 0, "sampled moments take entries 0, 4, 8, ...");
+  float mn = INFINITY, mx = -INFINITY, s1 = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    mn = fminf(mn, x[v]);
+    mx = fmaxf(mx, x[v]);
+    if (v % 4 == 0) {
+      s1 += x[v];
+      s2 = fmaf(x[v], x[v], s2);
+    }
+  }
+  // NaN (outside the contract) or infinities: the careful search
+  const bool odd = !(fabsf(mn) < INFINITY && fabsf(mx) < INFINITY && s2 < INFINITY);
+  uint32_t kmn = order_key(mn), kmx = order_key(mx);
+  wave_min_max(kmn, kmx);
+  {
+    const int wave = int(threadIdx.x) >> 6;
+    const uint64_t any_odd = __ballot(odd);
+    if (lane_id() == 0) {
+      sh.wlo[wave] = any_odd ? 0u : kmn;  // 0 (below every finite key) flags the wave
+      sh.whi[wave] = kmx;
+    }
+  }
+  block_fsum2(sh, 0, s1, s2);  // its barrier also publishes wlo / whi
+#pragma unroll
+  for (int w = 0; w < BLOCK / 64; ++w) {
+    kmn = min(kmn, sh.wlo[w]);
+    kmx = max(kmx, sh.whi[w]);
+  }
+  if (!(finite_key(kmn) && finite_key(kmx))) {
+    __syncthreads();  // every thread has read wlo / whi before the careful search rewrites them
+    return count_threshold<BLOCK, CAP, V>(sh, x, [](int) { return true; }, m, need, goal, tau);
+  }
+  if (!(kmn < kmx)) return false;
+  float lo = key_value(kmn), hi = key_value(kmx);
+  int clo = m, chi = 1;
+  const float aim = float((need + goal) >> 1);
+  const float ms = float(m >> 2);  // entries sampled per row (m = BLOCK * V)
+  const float mean = s1 / ms;
+  const float var = fmaxf(s2 / ms - mean * mean, 0.f);
+  float t = fmaf(sqrtf(var), normal_upper_quantile(aim / float(m)), mean);
+#pragma unroll 1
+  for (int step = 0; step < kSteps; ++step) {
+    if (step > 0 || !(t > lo && t < hi)) {
+      float f = (float(clo) - aim) / float(max(clo - chi, 1));
+      f = fminf(fmaxf(f, 0.125f), 0.875f);
+      t = fmaf(f, hi, fmaf(-f, lo, lo));
+      if (!(t > lo && t < hi)) return false;  // uniform: the bracket cannot shrink
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) cnt += x[v] >= t ? 1 : 0;
+    float cl = float(cnt), unused = 0.f;
+    block_fsum2(sh, 1 - (step & 1), cl, unused);
+    const int ct = int(cl);
+    if (ct >= need) {
+      lo = t;
+      clo = ct;
+      if (ct <= goal) {
+        tau = t;
+        return true;
+      }
+    } else {
+      hi = t;
+      chi = ct;
+    }
+  }
+  return false;
+}
+
 // Append the entries u of a chunk with take(u) to the LDS list ckey / cj
 // (key_at / j_at are evaluated for taken entries only). The wave takes all
 // U ballots first and claims room for all its entries with one LDS atomic,
@@ -1307,13 +1386,27 @@ __device__ __forceinline__ void long_row_topk(TopkShared<BLOCK, CAP>& sh, const 
   // conversion.
   float tau_f = 0.f;
   bool can_refresh = true;  // uniform: cleared when a refresh finds no bound
-  const bool counted =
-      (REFRESH || n >= 4 * prefix) &&
-      count_threshold<BLOCK, CAP, V>(sh, raw, [&](int v) { return key_at(v) != 0u; }, prefix, min(k, prefix),
-                                     min(k, prefix) + (min(k, prefix) >> 3) + 64, tau_f);
+  bool counted;
+  if constexpr (REFRESH)  // n > prefix: every prefix entry lies inside the row
+    counted = count_threshold_dense<BLOCK, CAP, V>(sh, raw, prefix, min(k, prefix),
+                                                   min(k, prefix) + (min(k, prefix) >> 3) + 64, tau_f);
+  else
+    counted = n >= 4 * prefix &&
+              count_threshold<BLOCK, CAP, V>(sh, raw, [&](int v) { return key_at(v) != 0u; }, prefix, min(k, prefix),
+                                             min(k, prefix) + (min(k, prefix) >> 3) + 64, tau_f);
   if (counted) {
-    append_list<BLOCK, CAP, V>(sh, [&](int v) { return __float_as_uint(raw[v]); }, j_at,
-                               [&](int v) { return key_at(v) != 0u && raw[v] >= tau_f; });
+    if constexpr (REFRESH) {
+      // in two halves: 32 lane masks would not fit the scalar registers
+      static_assert(V % 8 == 0, "halves of whole quads");
+      constexpr int H2 = V / 2;
+      append_list<BLOCK, CAP, H2>(sh, [&](int v) { return __float_as_uint(raw[v]); }, j_at,
+                                  [&](int v) { return raw[v] >= tau_f; });
+      append_list<BLOCK, CAP, H2>(sh, [&](int v) { return __float_as_uint(raw[H2 + v]); },
+                                  [&](int v) { return j_at(H2 + v); }, [&](int v) { return raw[H2 + v] >= tau_f; });
+    } else {
+      append_list<BLOCK, CAP, V>(sh, [&](int v) { return __float_as_uint(raw[v]); }, j_at,
+                                 [&](int v) { return key_at(v) != 0u && raw[v] >= tau_f; });
+    }
   } else if constexpr (REFRESH) {
     // no bound from the search (non-finite or crowded scores): the radix
     // path (the prefix histogram's registers would not fit beside a wide
