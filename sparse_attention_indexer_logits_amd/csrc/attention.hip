@@ -60,8 +60,10 @@ __device__ __forceinline__ int tile_at(int row, int col) {
 constexpr int kMaxAttnSlots = 2048;         // tokens resolved in LDS
 constexpr int kRowsHeadTiles = 1;           // 16-head tiles per wave in attention_rows_kernel
 constexpr int kRowsChunk = 64;              // slots per chunk in attention_rows_kernel
+constexpr int kSplitWaves = 8;              // waves (16-slot key subtiles per chunk) in sparse_attention_split_kernel
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
@@ -83,29 +85,48 @@ __device__ __forceinline__ float shfl_sum(float v) {
 }
 
 // Decode batches (fewer (row, 64-head) workgroups than CUs): the workgroup
-// takes 16 heads and its four waves split every chunk's keys (wave w keys
-// 16w..16w+15), each wave running its own online softmax; the four partial
-// states are merged at the end (its 58 KB of LDS allow two per CU).
-__global__ __launch_bounds__(256) void sparse_attention_split_kernel(
+// takes 16 heads and its NW waves split every chunk of 16*NW slots (wave w
+// keys 16w..16w+15), each wave running its own online softmax over its keys
+// of every chunk; the NW partial states are merged at the end in a fixed
+// order, so the result does not depend on timing. More waves mean fewer
+// chunks per row, i.e. fewer dependent decode -> score -> accumulate rounds
+// for the few workgroups of a decode batch. The chunk tile and the merge
+// buffers share the LDS.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void sparse_attention_split_kernel(
     const uint16_t* __restrict__ q, const uint32_t* __restrict__ kv_fp4, const uint8_t* __restrict__ kv_scale,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ sel_pos,
     const int32_t* __restrict__ row_seq, const float* __restrict__ sink, float scale_log2,
     float* __restrict__ out, int H, int k, int MB, int bs_log2) {
   using Frag = bf16x8;
-  __shared__ __attribute__((aligned(16))) uint16_t kt[kChunk * kKPitch];
-  __shared__ __attribute__((aligned(16))) float sbias[kChunk];
+  constexpr int NT = 64 * NW;   // threads
+  constexpr int C = 16 * NW;    // slots per chunk
+  constexpr int kHeadsPerWg = 16;
+  constexpr int DPT = kHeadDim * kHeadsPerWg / NT;  // merged outputs per thread
+  static_assert(DPT >= 2 && DPT % 2 == 0, "merge split");
+  struct Loop {
+    uint16_t kt[C * kKPitch];
+    float sbias[C];
+  };
+  struct Merge {
+    float cm[NW][kHeadsPerWg], cl[NW][kHeadsPerWg];
+    float co[NW][kHeadsPerWg][kHeadDim];
+  };
+  __shared__ __attribute__((aligned(16))) uint8_t lds[sizeof(Loop) > sizeof(Merge) ? sizeof(Loop) : sizeof(Merge)];
   __shared__ int tok[kMaxAttnSlots];
+  auto& L = *reinterpret_cast<Loop*>(lds);
+  uint16_t* kt = L.kt;
+  float* sbias = L.sbias;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
-  constexpr int kHeadsPerWg = 16;
   const int groups = H / kHeadsPerWg;
   const int64_t r = blockIdx.x / groups;
   const int head = (blockIdx.x % groups) * kHeadsPerWg + c;  // this lane's head column
 
   // 1. the row's slots -> cache tokens (-1: padded slot)
   const int seq = row_seq ? row_seq[r] : int(r);
-  for (int j = tid; j < k; j += 256) {
+  for (int j = tid; j < k; j += NT) {
     const int p = sel_pos[r * k + j];
     int t = -1;
     if (p >= 0) {
@@ -121,8 +142,8 @@ __global__ __launch_bounds__(256) void sparse_attention_split_kernel(
   for (int s = 0; s < 4; ++s) qb[s] = *reinterpret_cast<const Frag*>(qrow + 32 * s + 8 * g);
   __syncthreads();
 
-  // chunk loads: thread -> slot tid%64 of the chunk, dims [32*(tid/64), +32)
-  const int lslot = tid & 63, quarter = tid >> 6;
+  // chunk loads: thread -> slot tid%C of the chunk, dims [32*(tid/C), +32)
+  const int lslot = tid % C, quarter = tid / C;
   auto fetch = [&](int c0, u32x4& nib, uint32_t& sc, int& t) {
     const int j = c0 + lslot;
     t = j < k ? tok[j] : -1;
@@ -143,7 +164,7 @@ __global__ __launch_bounds__(256) void sparse_attention_split_kernel(
   for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;  // running max (base-2 scaled) and sum of head c
 
-  for (int c0 = 0; c0 < k; c0 += kChunk) {
+  for (int c0 = 0; c0 < k; c0 += C) {
     // 2. decode the chunk into the tile
     {
       u32x4 d[4];
@@ -154,7 +175,7 @@ __global__ __launch_bounds__(256) void sparse_attention_split_kernel(
       if (quarter == 0) sbias[lslot] = t >= 0 ? 0.f : -INFINITY;
     }
     __syncthreads();
-    if (c0 + kChunk < k) fetch(c0 + kChunk, nib, sc, t);  // in flight during the MFMAs
+    if (c0 + C < k) fetch(c0 + C, nib, sc, t);  // in flight during the MFMAs
 
     // 3. S^T = K Q^T for this wave's 16 keys
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -198,34 +219,36 @@ __global__ __launch_bounds__(256) void sparse_attention_split_kernel(
       const uint2 v = vt_frag4(kt, 16 * wave + 4 * g, mt, lane);
       o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v), pq, o[mt], 0, 0, 0);
     }
-    __syncthreads();  // the tiles are rewritten by the next chunk
+    __syncthreads();  // the tiles are rewritten by the next chunk (and by the merge)
   }
 
   {
-    // 6. merge the four waves' states of the 16 heads, then the sink
-    __shared__ float cm[4][16], cl[4][16];
-    __shared__ __attribute__((aligned(16))) float co[4][16][kHeadDim];
+    // 6. merge the NW waves' states of the 16 heads, then the sink
+    auto& M = *reinterpret_cast<Merge*>(lds);
     if (g == 0) {
-      cm[wave][c] = m;
-      cl[wave][c] = l;
+      M.cm[wave][c] = m;
+      M.cl[wave][c] = l;
     }
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(&co[wave][c][16 * mt + 4 * g]) = o[mt];
+    for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(&M.co[wave][c][16 * mt + 4 * g]) = o[mt];
     __syncthreads();
-    const int hc = tid >> 4, d0 = 8 * (tid & 15);  // 16 threads per head, 8 dims each
-    float mw[4], mm = -INFINITY;
+    constexpr int TPH = NT / kHeadsPerWg;   // threads per head
+    const int hc = tid / TPH, d0 = DPT * (tid % TPH);
+    float mw[NW], mm = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      mw[w] = cm[w][hc];
+    for (int w = 0; w < NW; ++w) {
+      mw[w] = M.cm[w][hc];
       mm = fmaxf(mm, mw[w]);
     }
-    float lsum = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f, acc[DPT];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
       const float a = mw[w] > -INFINITY ? __builtin_amdgcn_exp2f(mw[w] - mm) : 0.f;
-      lsum = fmaf(cl[w][hc], a, lsum);
+      lsum = fmaf(M.cl[w][hc], a, lsum);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(co[w][hc][d0 + e], a, acc[e]);
+      for (int e = 0; e < DPT; ++e) acc[e] = fmaf(M.co[w][hc][d0 + e], a, acc[e]);
     }
     const int hd = (blockIdx.x % groups) * kHeadsPerWg + hc;
     const float s2 = sink ? sink[hd] * 1.4426950408889634f : -INFINITY;
@@ -236,8 +259,8 @@ __global__ __launch_bounds__(256) void sparse_attention_split_kernel(
       f = a / (lsum * a + __builtin_amdgcn_exp2f(s2 - mf));
     }
     float* orow = out + (r * H + hd) * int64_t(kHeadDim) + d0;
-    *reinterpret_cast<f32x4*>(orow) = f32x4{acc[0], acc[1], acc[2], acc[3]} * f;
-    *reinterpret_cast<f32x4*>(orow + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]} * f;
+#pragma unroll
+    for (int e = 0; e < DPT; e += 2) *reinterpret_cast<f32x2*>(orow + e) = f32x2{acc[e], acc[e + 1]} * f;
   }
 }
 
@@ -429,9 +452,9 @@ hipError_t launch_sparse_attention(const uint16_t* q, const uint8_t* kv_fp4, con
   // Fewer (row, 64-head) workgroups than CUs (decode): 16 heads per workgroup
   // with the keys split across its waves, four times the workgroups.
   if (int64_t(R) * (H / kAttnHeads) < 256)
-    hipLaunchKernelGGL(sparse_attention_split_kernel, dim3(unsigned(int64_t(R) * (H / 16))), dim3(256), 0, stream,
-                       q, reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale, block_table, sel_pos, row_seq, sink,
-                       scale_log2, out, H, k, MB, bs_log2);
+    hipLaunchKernelGGL((sparse_attention_split_kernel<kSplitWaves>), dim3(unsigned(int64_t(R) * (H / 16))),
+                       dim3(64 * kSplitWaves), 0, stream, q, reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale,
+                       block_table, sel_pos, row_seq, sink, scale_log2, out, H, k, MB, bs_log2);
   else
     hipLaunchKernelGGL((attention_rows_kernel<kRowsHeadTiles, kRowsChunk>), dim3(unsigned(int64_t(R) * (H / kAttnHeads))),
                        dim3(64 * (4 / kRowsHeadTiles)), 0, stream, q, reinterpret_cast<const uint32_t*>(kv_fp4), kv_scale,
