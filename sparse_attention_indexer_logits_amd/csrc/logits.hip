@@ -415,6 +415,22 @@ __device__ __forceinline__ float wave_min(float v) {
   return fminf(fminf(lane_v(0), lane_v(16)), fminf(lane_v(32), lane_v(48)));
 }
 
+// -inf over orow[j0, j1) by one wave: 16-byte non-temporal stores over the
+// 16-byte aligned body when the row starts 16-byte aligned (vec), single
+// stores at the ragged ends
+__device__ __forceinline__ void fill_neg_inf(float* orow, int j0, int j1, int lane, bool vec) {
+  if (j0 >= j1) return;  // uniform
+  if (!vec) {
+    for (int j = j0 + lane; j < j1; j += 64) orow[j] = -INFINITY;
+    return;
+  }
+  const int a0 = min(j1, (j0 + 3) & ~3), a1 = max(a0, j1 & ~3);
+  if (lane < a0 - j0) orow[j0 + lane] = -INFINITY;
+  if (lane < j1 - a1) orow[a1 + lane] = -INFINITY;
+  const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int j = a0 + 4 * lane; j < a1; j += 256) __builtin_nontemporal_store(ninf, reinterpret_cast<f32x4*>(orow + j));
+}
+
 // waits until at most N vector-memory operations of this wave are
 // outstanding, then joins the workgroup barrier; the asm's memory clobber
 // keeps the compiler from moving memory accesses across it
@@ -512,12 +528,16 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 4 : 3) void logits_prefill_kernel(
   const int64_t bt = b * T + (qvalid ? t_q : 0);
   const int lim = qvalid ? clamp_limit(limit, bt, K) : -1;
   const int q_end = min(j_end, lim + 1);
-  if (!kCand && qvalid) {
-    float* orow = out + bt * K;
-    for (int j = max(j_begin, lim + 1) + lane; j < j_end; j += 64) orow[j] = -INFINITY;
-  }
+  // this query's keys of the chunk past its limit are -inf; a workgroup with
+  // keys to score issues these stores once tile 0 has landed, so no early
+  // wait (vector-memory counts complete in issue order) waits for them
+  const bool vec = (K & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+  auto fill = [&]() {
+    if (!kCand && qvalid) fill_neg_inf(out + bt * K, max(j_begin, lim + 1), j_end, lane, vec);
+  };
   if (kCand && blockIdx.x == 0 && threadIdx.x < 2) co.ctrl[threadIdx.x] = 0;  // queue counters
   if (c_end <= j_begin) {  // uniform over the workgroup
+    fill();
     if (kCand && qvalid && lane == 0) co.count[bt * n_chunks + chunk] = 0;
     return;
   }
@@ -600,6 +620,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 4 : 3) void logits_prefill_kernel(
   if constexpr (kBufs == 4) dma(tile2, 2);
   // tile 0 has landed (this wave's part), then all waves' parts
   wait_vm_barrier<(kBufs - 2) * kDma>();
+  fill();
 
   // score tile tix (in `cur`) after starting tile tix + kBufs - 1 (into
   // `nxt`, the buffer every wave finished reading before the last barrier)
