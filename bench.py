@@ -477,6 +477,71 @@ def copy_calibration(nbytes=1 << 30, reps=4):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def device_peaks(torch):
+    """The GPU's CU count and peak clocks (HIP device attributes) and the
+    rates reached on it, next to the spec peaks the fractions use: dense MFMA
+    issue on the two prefill tile shapes (fp8 32x32x64, bf16 16x16x32; 4
+    waves per SIMD, 4 independent accumulator chains each), a non-temporal
+    2 GiB read stream, and torch's 1 GiB fill and copy (bytes moved / time)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_indexer_logits_amd", "libxk_peaks.so"))
+    cus, clk, mclk = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    if lib.xkp_device_info(0, ctypes.byref(cus), ctypes.byref(clk), ctypes.byref(mclk)) != 0:
+        raise RuntimeError("hipDeviceGetAttribute failed")
+    props = torch.cuda.get_device_properties(0)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best_ms(launch, reps=3):
+        launch()   # warm-up
+        ms = []
+        for _ in range(reps):
+            e0.record()
+            launch()
+            e1.record()
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return min(ms)
+
+    lib.xkp_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p]
+    lib.xkp_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    blocks = 4 * cus.value          # 4 waves per workgroup: 4 waves per SIMD
+    ops = torch.arange(64, dtype=torch.int32, device="cuda") * 0x01010101 % 0x3F3F3F3F
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    out = {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""), "compute_units": cus.value,
+           "peak_clock_MHz": clk.value / 1e3, "memory_clock_MHz": mclk.value / 1e3, "measured": {}}
+    meas = out["measured"]
+    for kind, name, iters, flop in ((0, "mfma_fp8_32x32x64_TFLOPs", 2048, 2 * 32 * 32 * 64),
+                                    (1, "mfma_bf16_16x16x32_TFLOPs", 8192, 2 * 16 * 16 * 32)):
+        def launch(kind=kind, iters=iters):
+            if lib.xkp_mfma_loop(kind, ops.data_ptr(), sink.data_ptr(), blocks, iters, stream) != 0:
+                raise RuntimeError("MFMA probe launch failed")
+        ms = best_ms(launch)
+        meas[name] = blocks * 4 * 4 * iters * flop / (ms / 1e3) / 1e12
+    nbytes = 2 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(7)
+    rblocks = 8 * cus.value
+    rsink = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda")
+
+    def read():
+        if lib.xkp_read_stream(src.data_ptr(), nbytes // 16, rsink.data_ptr(), rblocks, stream) != 0:
+            raise RuntimeError("read probe launch failed")
+    meas["hbm_read_GBps"] = nbytes / (best_ms(read) / 1e3) / 1e9
+    del src, rsink
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    meas["hbm_fill_GBps"] = buf.numel() / (best_ms(lambda: buf.fill_(3)) / 1e3) / 1e9
+    dst = torch.empty_like(buf)
+    meas["hbm_copy_GBps"] = 2 * buf.numel() / (best_ms(lambda: dst.copy_(buf)) / 1e3) / 1e9
+    del buf, dst
+    meas["frac_of_spec"] = {
+        "mfma_fp8": meas["mfma_fp8_32x32x64_TFLOPs"] / PEAK["mfma_fp8"],
+        "mfma_bf16": meas["mfma_bf16_16x16x32_TFLOPs"] / PEAK["mfma_bf16"],
+        "hbm_read": meas["hbm_read_GBps"] / PEAK["hbm"]}
+    torch.cuda.synchronize()
+    return out
+
+
 def dispatch_us(torch, launches, flush=None):
     """Duration of each launch, timed alone with an event pair on the launch
     stream: p10/p50/p90 and mean in microseconds. With `flush` (a device
@@ -688,6 +753,7 @@ def main():
 
     import torch
 
+    device = device_peaks(torch)
     x, res = measure(args, args.config, full=True)
     cfg = x["cfg"]
     stages = res["stages"]
@@ -714,7 +780,7 @@ def main():
                    "input_copies_rotated": res["input_copies_rotated"]},
         "topk_gather_GBps": res["topk_gather_GBps"], "topk_gather_frac_hbm": res["topk_gather_frac_hbm"],
         "logits_kernel_TFLOPs": res["logits_kernel_TFLOPs"],
-        "stages": stages, "roofline": roof, "work": res["work"],
+        "stages": stages, "roofline": roof, "work": res["work"], "device": device,
     }
     for k in ("fused", "consumer"):
         if k in res:

@@ -66,6 +66,10 @@ def build(verbose: bool = False) -> str:
     _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [j[0] for j in jobs],
          verbose)
     os.replace(tmp, LIB)
+    # the benchmark's achievable-rate probes: a library of their own
+    peaks = os.path.join(PKG, "libxk_peaks.so")
+    _run([hipcc()] + COMMON + ["-shared", "-o", peaks + ".tmp", os.path.join(PKG, "probes", "peaks.hip")], verbose)
+    os.replace(peaks + ".tmp", peaks)
     return LIB
 
 
