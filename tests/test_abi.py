@@ -224,3 +224,20 @@ def test_python_binding_rejects_host_tensors():
     with pytest.raises(ValueError, match="device tensor"):
         xk.xk_indexer_logits(q, torch.zeros((1, 8, 128), dtype=torch.bfloat16),
                              torch.zeros((1, 1, 64)))
+
+
+def test_bench_probe_library_exports_and_checks_arguments():
+    """The benchmark's achievable-rate probes (a library of their own, not the
+    indexer ABI): exported, and bad arguments are refused before any launch."""
+    path = os.path.join(ROOT, "sparse_attention_indexer_logits_amd", "libxk_peaks.so")
+    if not os.path.exists(path):
+        pytest.skip("libxk_peaks.so not built")
+    raw = ctypes.CDLL(path)
+    for n in ("xkp_device_info", "xkp_mfma_loop", "xkp_read_stream"):
+        assert hasattr(raw, n), n
+    raw.xkp_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p]
+    raw.xkp_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert raw.xkp_mfma_loop(0, None, None, 16, 1, None) == 1          # no operand buffers
+    assert raw.xkp_mfma_loop(0, 16, 16, 0, 1, None) == 1               # no workgroups
+    assert raw.xkp_read_stream(8, 4, 16, 16, None) == 1                # source not 16-byte aligned
