@@ -753,7 +753,10 @@ def main():
 
     import torch
 
-    device = device_peaks(torch)
+    try:   # auxiliary: a failure here is reported in the line, not fatal to it
+        device = device_peaks(torch)
+    except (OSError, RuntimeError) as e:
+        device = {"error": f"{type(e).__name__}: {e}"}
     x, res = measure(args, args.config, full=True)
     cfg = x["cfg"]
     stages = res["stages"]
