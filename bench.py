@@ -528,6 +528,16 @@ def device_peaks(torch):
         if lib.xkp_read_stream(src.data_ptr(), nbytes // 16, rsink.data_ptr(), rblocks, stream) != 0:
             raise RuntimeError("read probe launch failed")
     meas["hbm_read_GBps"] = nbytes / (best_ms(read) / 1e3) / 1e9
+    # the same stream at decode-sized transfers (one launch of that many
+    # bytes, timed back to back): the rate a launch of the decode stages'
+    # size can reach at all
+    for mib in (16, 64, 256):
+        nb = mib << 20
+
+        def read_n(nb=nb):
+            if lib.xkp_read_stream(src.data_ptr(), nb // 16, rsink.data_ptr(), rblocks, stream) != 0:
+                raise RuntimeError("read probe launch failed")
+        meas[f"hbm_read_{mib}MiB_GBps"] = nb / (best_ms(read_n, reps=5) / 1e3) / 1e9
     del src, rsink
     buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     meas["hbm_fill_GBps"] = buf.numel() / (best_ms(lambda: buf.fill_(3)) / 1e3) / 1e9
