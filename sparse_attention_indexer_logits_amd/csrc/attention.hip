@@ -43,7 +43,6 @@ namespace xk {
 namespace {
 
 constexpr int kAttnHeads = 64;              // heads per workgroup
-constexpr int kChunk = 64;                  // slots per chunk
 constexpr int kKPitch = kHeadDim + 16;      // bf16 per tile row: 72 dwords
 
 // Element offset of (row, col) in a [slot][d] tile, col a multiple of 4. The
