@@ -879,8 +879,9 @@ __device__ __forceinline__ bool wave_row_topk(WaveRowShared& sh, const float* __
   }
   // Every loop below runs over all G groups with a uniform test, so xs stays
   // in registers: groups >= ng hold no entry and are skipped, and the one
-  // group straddling the row's end gets NaN past it (every comparison with
-  // it is false).
+  // group straddling the row's end tests each entry's index. (Writing NaN
+  // into that group instead made the compiler copy row registers across the
+  // uniform branches and spill four of them, reloaded in every search probe.)
   // The mean and variance only seed the search's first probe, so they come
   // from every fourth key (j % 4 == 0): half the VALU of the full sums
   // (measured 25.4 -> 24.2 us on the causal 4096-key rows, same indices).
@@ -904,7 +905,6 @@ __device__ __forceinline__ bool wave_row_topk(WaveRowShared& sh, const float* __
       for (int c = 0; c < 4; ++c) {
         const bool in = 256 * i + 4 * lane + c < n;
         const float v = in ? xs[4 * i + c] : 0.f;
-        xs[4 * i + c] = in ? v : __builtin_nanf("");
         if (in) {
           mn = fminf(mn, v);
           mx = fmaxf(mx, v);
@@ -920,11 +920,15 @@ __device__ __forceinline__ bool wave_row_topk(WaveRowShared& sh, const float* __
   auto count_lane = [&](float t) {
     int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < G; ++i)
-      if (i < ng) {
+    for (int i = 0; i < G; ++i) {
+      if (i < nfull) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) cnt += xs[4 * i + c] >= t ? 1 : 0;
+      } else if (i < ng) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) cnt += xs[4 * i + c] >= t && 256 * i + 4 * lane + c < n ? 1 : 0;
       }
+    }
     return cnt;
   };
   // 1. the bound tau (c = C(tau), mine = this lane's part of it)
@@ -975,7 +979,7 @@ __device__ __forceinline__ bool wave_row_topk(WaveRowShared& sh, const float* __
       if (i < ng) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (xs[4 * i + e] >= tau)
+          if (xs[4 * i + e] >= tau && (i < nfull || 256 * i + 4 * lane + e < n))
             sh.cand[at++] = (uint64_t(__float_as_uint(xs[4 * i + e])) << 32) |
                             uint64_t(~uint32_t(256 * i + 4 * lane + e));
       }
