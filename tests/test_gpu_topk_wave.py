@@ -3,7 +3,7 @@ keys, k <= 512, K a multiple of 4) with the oracle, through the C ABI.
 
 The batches have at least 1024 rows, so the launcher takes that path; each
 mixes rows the wave finishes itself with rows it hands to the workgroup's
-radix path (bins at or above the threshold holding more than 768 entries:
+radix path (more than 896 candidates above the bound, the wave's list size:
 heavy ties, infinities), and the row count is not a multiple of the rows per
 workgroup. Every row is compared with the oracle, bit for bit."""
 import numpy as np
