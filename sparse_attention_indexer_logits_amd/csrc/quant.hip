@@ -18,9 +18,10 @@
 // lanes one 32-element group, and a lane's eight nibbles one 32-bit word
 // of the cache row. A wave takes 4 rows per pass and issues the loads of
 // its passes before any arithmetic, to keep enough bytes in flight.
-// Integer codes are decided from float32 values exactly as the definitions
-// state them (IEEE division, power-of-two scaling, rint = round to nearest
-// even).
+// Integer codes are decided from the same float32 values the definitions
+// give (the correctly rounded quotient x / scale, power-of-two scaling), and
+// the rounding to e4m3 or E2M1 is the hardware conversion, which rounds to
+// nearest even as both formats specify.
 #include <math.h>
 
 #include <type_traits>
@@ -31,10 +32,11 @@ namespace xk {
 namespace {
 
 constexpr int kQuantWaves = 4;  // waves per workgroup; a wave takes 4 rows per pass
-// Passes per wave (rows 4 * P): one below kManyRows rows, four above.
-// Measured on the long-prefill shapes (0.1 M rows: one pass 10-15% faster)
-// and the Pro decode keys (2.6 M rows: four passes 9% faster for the mxfp4
-// writer, equal for the fp8 rows).
+// Passes per wave (rows 4 * P) of the fp8 rows: one below kManyRows rows, two
+// above. Measured on the Pro decode keys (2.5 M rows): two passes 6% faster
+// than one or four; on the long-prefill shapes (0.1 M rows) one to eight
+// passes time alike. The mxfp4 writer takes one pass at every size (8%
+// faster than two or four on the Pro decode keys).
 constexpr int64_t kManyRows = int64_t(1) << 20;
 
 template <int CTRL>
@@ -47,33 +49,34 @@ __device__ __forceinline__ float dpp_max(float v) {
 __device__ __forceinline__ float quad_max(float v) { return dpp_max<0x4E>(dpp_max<0xB1>(v)); }
 __device__ __forceinline__ float row16_max(float v) { return dpp_max<0x140>(dpp_max<0x141>(quad_max(v))); }
 
-// OCP e4m3 code of v: round to nearest even, saturated to +-448.
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t sign = __float_as_uint(v) >> 31 << 7;
-  const float a = fminf(fabsf(v), 448.f);
-  uint32_t code;
-  if (a < 0.015625f) {  // below 2^-6: subnormal, quantum 2^-9 (8 rounds up to the least normal)
-    code = uint32_t(rintf(a * 512.f));
-  } else {
-    int e = int((__float_as_uint(a) >> 23) & 0xFF) - 127;  // a is a normal float here
-    float m = rintf(ldexpf(a, 3 - e));                       // 3 mantissa bits: m in [8, 16]
-    if (m == 16.f) {
-      m = 8.f;
-      ++e;
-    }
-    code = (uint32_t(e + 7) << 3) | (uint32_t(m) - 8u);
-  }
-  return sign | code;
+// Four OCP e4m3 codes (element i in byte i) of values already clamped to
+// [-448, 448]; the conversion rounds to nearest even.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
 }
 
-// E2M1 code of v: round to nearest even (ties to the code with mantissa 0),
-// saturated to +-6. Magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 are codes 0..7.
-__device__ __forceinline__ uint32_t e2m1_rne(float v) {
-  const uint32_t sign = __float_as_uint(v) >> 31 << 3;
-  const float a = fabsf(v);
-  uint32_t m = a > 5.f ? 7u : a >= 3.5f ? 6u : a > 2.5f ? 5u : a >= 1.75f ? 4u
-             : a > 1.25f ? 3u : a >= 0.75f ? 2u : a > 0.25f ? 1u : 0u;
-  return sign | m;
+// The float32 quotient x / s rounded to nearest even, as an IEEE division
+// gives it, wherever |x / s| >= 2^-10 (below that the e4m3 code is a zero of
+// x's sign, and the sign is kept). rs is the double reciprocal of s (relative
+// error 2^-53), so x * rs is within 2^-52 (relative) of the exact quotient.
+// A quotient of two float32 numbers lies more than 2^-49 (relative) from any
+// float32 rounding midpoint: a midpoint has 25 significant bits with the last
+// one set, so x - midpoint * s is a nonzero multiple of the product of the
+// midpoint's and s's last-bit weights. One rounding of x * rs to float32
+// therefore lands where the exact quotient's does.
+__device__ __forceinline__ float quotient(float x, double rs) { return float(double(x) * rs); }
+
+// Four E2M1 nibbles (element 2i in the low nibble of byte i) of four values in
+// (-8, 8) into the bytes sel, sel + 1 of old: round to nearest even, values
+// beyond 6 saturate.
+__device__ __forceinline__ uint32_t e2m1x2(uint32_t old, float a, float b, int sel) {
+  switch (sel) {  // the byte select is an immediate of the instruction
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.f, 3);
+  }
 }
 
 // Eight consecutive elements of a row: lane (row % 4 in the pass, l % 16)
@@ -124,12 +127,11 @@ __global__ __launch_bounds__(kQuantWaves * 64) void quant_fp8_rows_kernel(
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(elem<BF16>(v[p], i)));
     amax = row16_max(amax);
     const float s = amax > 0.f ? amax / 448.f : 1.f;
-    uint32_t lo = 0u, hi = 0u;
+    const double rs = 1.0 / double(s);
+    float q[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= e4m3_rne(elem<BF16>(v[p], i) / s) << (8 * i);
-      hi |= e4m3_rne(elem<BF16>(v[p], 4 + i) / s) << (8 * i);
-    }
+    for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_fmed3f(quotient(elem<BF16>(v[p], i), rs), -448.f, 448.f);
+    const uint32_t lo = e4m3x4(q[0], q[1], q[2], q[3]), hi = e4m3x4(q[4], q[5], q[6], q[7]);
     if (row < N) {
       reinterpret_cast<uint2*>(out)[row * 16 + col] = make_uint2(lo, hi);
       if (col == 0) scale[row] = s;
@@ -165,7 +167,8 @@ __global__ __launch_bounds__(kQuantWaves * 64) void mxfp4_write_kernel(
     }
     uint32_t word = 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) word |= e2m1_rne(ldexpf(elem<BF16>(v[p], i), -e)) << (4 * i);
+    for (int i = 0; i < 4; ++i)  // |x * 2^-e| < 8 by the choice of e
+      word = e2m1x2(word, ldexpf(elem<BF16>(v[p], 2 * i), -e), ldexpf(elem<BF16>(v[p], 2 * i + 1), -e), i);
     const int64_t sl = slot[p];
     if (sl >= 0 && sl < n_slots) {
       reinterpret_cast<uint32_t*>(kv_fp4)[sl * 16 + col] = word;
@@ -186,7 +189,7 @@ hipError_t launch_quant_fp8_rows(const void* x, bool bf16, uint8_t* out, float* 
   };
   auto by_p = [&](auto bf16_tag) {
     if (N >= kManyRows)
-      go(bf16_tag, std::integral_constant<int, 4>{});
+      go(bf16_tag, std::integral_constant<int, 2>{});
     else
       go(bf16_tag, std::integral_constant<int, 1>{});
   };
@@ -206,16 +209,10 @@ hipError_t launch_mxfp4_write(const void* x, bool bf16, const int64_t* slots, ui
     hipLaunchKernelGGL((mxfp4_write_kernel<F, P>), grid, dim3(kQuantWaves * 64), 0, stream, x, slots, kv_fp4,
                        kv_scale, N, n_slots);
   };
-  auto by_p = [&](auto bf16_tag) {
-    if (N >= kManyRows)
-      go(bf16_tag, std::integral_constant<int, 4>{});
-    else
-      go(bf16_tag, std::integral_constant<int, 1>{});
-  };
   if (bf16)
-    by_p(std::true_type{});
+    go(std::true_type{}, std::integral_constant<int, 1>{});
   else
-    by_p(std::false_type{});
+    go(std::false_type{}, std::integral_constant<int, 1>{});
   return hipGetLastError();
 }
 

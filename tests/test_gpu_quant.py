@@ -37,7 +37,7 @@ def _rows(seed, N):
     return x
 
 
-# (1 << 20) + 3 rows: the launch shape for many rows (four passes per wave), ragged
+# (1 << 20) + 3 rows: the fp8 launch shape for many rows (two passes per wave), ragged
 @pytest.mark.parametrize("dtype,N", [(d, n) for d in ("fp32", "bf16") for n in (1, 7, 1000, 98304)]
                          + [("fp32", (1 << 20) + 3)])
 def test_quant_fp8_rows(xk, dtype, N):
