@@ -34,6 +34,14 @@ def _rows(seed, N):
         x[6] = np.resize([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -5.0, 5.5, 0.1], 128)
         x[7, :32] = 7.5
         x[7, 32:] = np.resize([1e-30, -3e-38, 2e-40], 96)  # tiny groups (subnormal range)
+    if N > 10:
+        # scale 3 (amax 1344): quotients that are exact e4m3 midpoints at a scale that is not a
+        # power of two, so ties reach the encoder through a rounded division
+        pos = np.sort(oracle.e4m3_to_f64(np.arange(0x7F, dtype=np.uint8)))
+        mids = (pos[1:] + pos[:-1]) / 2
+        x[8] = np.resize(np.r_[1344.0, 3 * mids[::-1]], 128) * np.where(np.arange(128) % 2, -1, 1)
+        # a subnormal scale (amax 1e-37): the rounded scale puts |x / scale| just above 448
+        x[9] = np.r_[1e-37, np.linspace(-1e-37, 1e-37, 127)]
     return x
 
 
