@@ -180,8 +180,9 @@ xk_status xk_indexer_topk(const float* logits, const int32_t* limit, int32_t* id
  *   scale        the softmax scale (finite)
  *   out          [R,H,D] fp32 (16-byte aligned); every element is written
  *   D must be 128, H a multiple of 64 and k <= 2048, else XK_ERR_UNSUPPORTED.
- * Scores and sums are fp32; the weights enter the value sum rounded to bf16,
- * so |out - exact| <= ~2^-9 * max_j |v_j| per row.
+ * Scores and sums are fp32; the weights enter the value sum rounded to bf16
+ * (relative error at most 2^-8) while the denominator sums them in fp32, so
+ * |out - exact| <= 2^-8 * max_j |v_j| per row, up to fp32 rounding.
  */
 xk_status xk_sparse_attention_mxfp4(const void* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
                                     const int32_t* block_table, const int32_t* sel_pos,
