@@ -301,7 +301,7 @@ typedef enum {
  *
  *   x      [N,D] fp32 or bf16 (x_dtype), 16-byte aligned
  *   out    [N,D] e4m3 bytes (8-byte aligned); scale [N] fp32
- *   N >= 1, D must be 128 (XK_ERR_UNSUPPORTED otherwise).
+ *   1 <= N <= 2^34, D must be 128 (XK_ERR_UNSUPPORTED otherwise).
  */
 xk_status xk_quant_fp8_rows(const void* x, xk_in_dtype x_dtype, uint8_t* out, float* scale, int64_t N, int D,
                             hipStream_t stream);
@@ -322,7 +322,7 @@ xk_status xk_quant_fp8_rows(const void* x, xk_in_dtype x_dtype, uint8_t* out, fl
  *
  *   x        [N,D] fp32 or bf16 rows (16-byte aligned); slots [N] int64
  *   kv_fp4   [NB,bs,D/2] u8 (4-byte aligned); kv_scale [NB,bs,D/32] u8 (in place)
- *   N >= 1, D must be 128.
+ *   1 <= N <= 2^34, D must be 128 (XK_ERR_UNSUPPORTED otherwise).
  */
 xk_status xk_mxfp4_cache_write(const void* x, xk_in_dtype x_dtype, const int64_t* slots, uint8_t* kv_fp4,
                                uint8_t* kv_scale, int64_t N, int NB, int bs, int D, hipStream_t stream);

@@ -137,7 +137,7 @@ XK_EXPORT xk_status xk_quant_fp8_rows(const void* x, xk_in_dtype x_dtype, uint8_
   if (x_dtype != XK_IN_FP32 && x_dtype != XK_IN_BF16)
     return fail(XK_ERR_INVALID_ARGUMENT, "unknown x dtype");
   if (D != xk::kHeadDim) return fail(XK_ERR_UNSUPPORTED, "only D=128 is implemented");
-  if (N > (int64_t(1) << 40)) return fail(XK_ERR_UNSUPPORTED, "N above 2^40");
+  if (N > (int64_t(1) << 34)) return fail(XK_ERR_UNSUPPORTED, "N above 2^34");  // grid: N / 16 workgroups
   if (!aligned(x, 16) || !aligned(out, 8) || !aligned(scale, 4))
     return fail(XK_ERR_INVALID_ARGUMENT, "x, out or scale misaligned (16, 8, 4 bytes)");
   xk_status s = check_device();
@@ -157,7 +157,7 @@ XK_EXPORT xk_status xk_mxfp4_cache_write(const void* x, xk_in_dtype x_dtype, con
   if (x_dtype != XK_IN_FP32 && x_dtype != XK_IN_BF16)
     return fail(XK_ERR_INVALID_ARGUMENT, "unknown x dtype");
   if (D != xk::kHeadDim) return fail(XK_ERR_UNSUPPORTED, "only D=128 is implemented");
-  if (N > (int64_t(1) << 40)) return fail(XK_ERR_UNSUPPORTED, "N above 2^40");
+  if (N > (int64_t(1) << 34)) return fail(XK_ERR_UNSUPPORTED, "N above 2^34");  // grid: N / 16 workgroups
   if (!aligned(x, 16) || !aligned(slots, 8) || !aligned(kv_fp4, 4))
     return fail(XK_ERR_INVALID_ARGUMENT, "x, slots or kv_fp4 misaligned (16, 8, 4 bytes)");
   xk_status s = check_device();

@@ -198,6 +198,7 @@ def test_gather_validation(lib, args, status, needle):
     ((FAKE, 3, FAKE, FAKE, 4, 128), 1, "dtype"),
     ((FAKE, 0, FAKE, FAKE, 4, 64), 2, "D=128"),
     ((FAKE + 4, 0, FAKE, FAKE, 4, 128), 1, "misaligned"),
+    ((FAKE, 0, FAKE, FAKE, (1 << 34) + 1, 128), 2, "2^34"),
 ])
 def test_quant_fp8_rows_validation(lib, args, status, needle):
     assert lib.xk_quant_fp8_rows(*args, None) == status
@@ -211,6 +212,7 @@ def test_quant_fp8_rows_validation(lib, args, status, needle):
     ((FAKE, 2, FAKE, FAKE, FAKE, 4, 2, 64, 128), 1, "dtype"),
     ((FAKE, 1, FAKE, FAKE, FAKE, 4, 2, 64, 256), 2, "D=128"),
     ((FAKE, 1, FAKE + 4, FAKE, FAKE, 4, 2, 64, 128), 1, "misaligned"),
+    ((FAKE, 1, FAKE, FAKE, FAKE, (1 << 34) + 1, 2, 64, 128), 2, "2^34"),
 ])
 def test_mxfp4_cache_write_validation(lib, args, status, needle):
     assert lib.xk_mxfp4_cache_write(*args, None) == status
