@@ -82,7 +82,8 @@ typedef enum {
  *                       values >= K are clamped to K-1
  *   logits   [B,T,K]    fp32 output; every element is written
  *   B, T, K >= 1; H must be 64 and D 128 (the DeepSeek-V4 indexer:
- *   index_n_heads 64, index_head_dim 128), else XK_ERR_UNSUPPORTED.
+ *   index_n_heads 64, index_head_dim 128), B*T <= 2^30 and B*T*K <= 2^38
+ *   (1 TB of logits), else XK_ERR_UNSUPPORTED.
  * Dot products accumulate in fp32 (MFMA). bf16: the ReLU, weights and head
  * sum run in fp32, so results match a float64 evaluation to ~1e-6 of
  * max|logit|. fp8: each head's ReLU'd score and weight are rounded to f16
@@ -121,7 +122,8 @@ typedef enum {
  *   block_table  [B,MB]    int32 physical page of each logical page
  *   logits       [B,T,K]   fp32 output, -inf past the limit; every element written
  *   bs must be a power of two and K <= MB*bs (else XK_ERR_INVALID_ARGUMENT);
- *   H must be 64, D 128, bs >= 16 and NB*bs < 2^31 (else XK_ERR_UNSUPPORTED). Pages holding a valid
+ *   H must be 64, D 128, bs >= 16, NB*bs < 2^31, B*T <= 2^30 and B*T*K <= 2^38 (else
+ *   XK_ERR_UNSUPPORTED). Pages holding a valid
  *   position must lie in [0, NB) (not checked on the device).
  */
 xk_status xk_indexer_logits_paged(const void* q, const float* q_scale, const float* w,

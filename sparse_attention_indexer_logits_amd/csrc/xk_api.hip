@@ -68,6 +68,8 @@ xk_status check_logits_args(const void* q, const float* q_scale, const void* k, 
     return fail(XK_ERR_UNSUPPORTED, "only H=64, D=128 (DeepSeek-V4 indexer) is implemented");
   if (!aligned(q, 16) || !aligned(k, 16)) return fail(XK_ERR_INVALID_ARGUMENT, "q and k must be 16-byte aligned");
   if (int64_t(B) * T > (int64_t(1) << 30)) return fail(XK_ERR_UNSUPPORTED, "B*T above 2^30");
+  // 1 TB of fp32 logits; keeps every launch grid (rows x key chunks) below 2^31
+  if (int64_t(B) * T * K > (int64_t(1) << 38)) return fail(XK_ERR_UNSUPPORTED, "B*T*K above 2^38");
   return XK_OK;
 }
 
@@ -120,6 +122,7 @@ XK_EXPORT xk_status xk_indexer_logits_paged(const void* q, const float* q_scale,
   if (int64_t(NB) * bs > (int64_t(1) << 31) - 1)
     return fail(XK_ERR_UNSUPPORTED, "NB*bs (cache positions) above 2^31-1");
   if (int64_t(B) * T > (int64_t(1) << 30)) return fail(XK_ERR_UNSUPPORTED, "B*T above 2^30");
+  if (int64_t(B) * T * K > (int64_t(1) << 38)) return fail(XK_ERR_UNSUPPORTED, "B*T*K above 2^38");
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(k_scale, 4))
     return fail(XK_ERR_INVALID_ARGUMENT, "q and k_cache must be 16-byte, k_scale 4-byte aligned");
   xk_status s = check_device();

@@ -64,6 +64,7 @@ FAKE = 0x10000  # aligned, never dereferenced: validation fails before any HIP c
     ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 32, 128, 0), 2, "H=64"),
     ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 64, 64, 0), 2, "H=64"),
     ((FAKE + 2, None, FAKE, None, FAKE, None, FAKE, 1, 1, 8, 64, 128, 0), 1, "aligned"),
+    ((FAKE, None, FAKE, None, FAKE, None, FAKE, 1 << 16, 1 << 10, 1 << 20, 64, 128, 0), 2, "2^38"),
 ])
 def test_logits_validation(lib, args, status, needle):
     assert lib.xk_indexer_logits(*args, None) == status
@@ -83,6 +84,8 @@ def test_logits_validation(lib, args, status, needle):
     ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 128, 1, 1 << 26, 64, 0), 2, "NB*bs"),
     ((FAKE, FAKE, FAKE, None, FAKE + 8, FAKE, FAKE, FAKE, 1, 1, 64, 64, 128, 1, 1, 64, 0), 1, "aligned"),
     ((FAKE, FAKE, FAKE, None, FAKE, FAKE + 2, FAKE, FAKE, 1, 1, 64, 64, 128, 1, 1, 64, 1), 1, "aligned"),
+    ((FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 10, 1 << 10, 1 << 20, 64, 128, 1 << 14, 1, 64, 0), 2,
+     "2^38"),
 ])
 def test_logits_paged_validation(lib, args, status, needle):
     assert lib.xk_indexer_logits_paged(*args, None) == status
