@@ -61,15 +61,16 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 // x's sign, and the sign is kept). rs is the double reciprocal of s (relative
 // error 2^-53), so x * rs is within 2^-52 (relative) of the exact quotient.
 // A quotient of two float32 numbers lies more than 2^-49 (relative) from any
-// float32 rounding midpoint: a midpoint has 25 significant bits with the last
-// one set, so x - midpoint * s is a nonzero multiple of the product of the
-// midpoint's and s's last-bit weights. One rounding of x * rs to float32
-// therefore lands where the exact quotient's does.
+// float32 rounding midpoint M: M has 25 significant bits with the last one
+// set, so x never equals M * s, and x - M * s is a nonzero multiple of the
+// smaller of x's last-bit weight and the product of M's and s's, at least
+// 2^-49 of M * s. One rounding of x * rs to float32 therefore lands where the
+// exact quotient's does.
 __device__ __forceinline__ float quotient(float x, double rs) { return float(double(x) * rs); }
 
-// Four E2M1 nibbles (element 2i in the low nibble of byte i) of four values in
-// (-8, 8) into the bytes sel, sel + 1 of old: round to nearest even, values
-// beyond 6 saturate.
+// Two E2M1 codes into byte sel of old, a in the low nibble and b in the high
+// one, of values in (-8, 8): round to nearest even, magnitudes beyond 6
+// saturate.
 __device__ __forceinline__ uint32_t e2m1x2(uint32_t old, float a, float b, int sel) {
   switch (sel) {  // the byte select is an immediate of the instruction
     case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.f, 0);
