@@ -131,7 +131,7 @@ def test_attention_config_chain(xk, name):
                                       a["scale"])
     torch.cuda.synchronize()
     assert torch.equal(o1, o2), "not deterministic"
-    rows = np.unique(np.r_[0, cfg.rows - 1, np.random.default_rng(1).choice(cfg.rows, 6)])
+    rows = np.unique(np.r_[0, cfg.rows - 1, np.random.default_rng(1).choice(cfg.rows, min(cfg.rows, 62))])
     sel = idx.cpu().numpy()[rows]
     g = o1.cpu().numpy()[rows].astype(np.float64)
     gathered = oracle.mxfp4_paged_gather(x["kv_fp4"], x["kv_scale"], x["block_table"], sel,
