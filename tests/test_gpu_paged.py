@@ -124,7 +124,7 @@ def test_paged_logits_limits(xk):
 @pytest.mark.parametrize("name", ["flash_decode_fp4", "pro_decode_fp4"])
 def test_paged_config_chain(xk, name):
     """The bench configs: paged logits (sampled rows), top-k on the GPU's
-    logits (bit-exact), gather (bit-exact)."""
+    logits and the gather, bit-exact on every row."""
     x = workloads.inputs(name)
     cfg = x["cfg"]
     print(f"[paged] config={name}", flush=True)
@@ -137,9 +137,8 @@ def test_paged_config_chain(xk, name):
     xk.xk_indexer_topk(g_t, cfg.topk, d["limit"].reshape(-1), out=idx)
     torch.cuda.synchronize()
     gi = idx.cpu().numpy()
-    ref = oracle.indexer_topk(g.reshape(cfg.rows, cfg.K), x["limit"].reshape(-1), cfg.topk, rows=rows)
-    for r in rows:
-        assert np.array_equal(gi[r], ref[r])
+    ref = oracle.indexer_topk(g.reshape(cfg.rows, cfg.K), x["limit"].reshape(-1), cfg.topk)
+    assert np.array_equal(gi, ref)
     lens = x["seq_len"][x["row_seq"]]
     assert np.all(gi >= -1) and np.all(gi < lens[:, None])
     out = torch.full((cfg.rows, cfg.topk, 128), 0x7FC1, dtype=torch.int16, device="cuda")
@@ -147,6 +146,6 @@ def test_paged_config_chain(xk, name):
     torch.cuda.synchronize()
     go = out.cpu().numpy().view(np.uint16)
     o = oracle.mxfp4_paged_gather(x["kv_fp4"], x["kv_scale"], x["block_table"], gi, x["row_seq"],
-                                  x["block_size"], rows=rows)
-    assert np.array_equal(go[rows], o[rows])
+                                  x["block_size"])
+    assert np.array_equal(go, o)
     print(f"[paged] {name}: logits rel err {err:.2e}", flush=True)
