@@ -95,6 +95,45 @@ def test_attention_small(xk, R, H, k, bs, with_sink):
     print(f"[attn] max err {err:.2e}", flush=True)
 
 
+def test_attention_rows_kernel_at_the_largest_k(xk):
+    """Enough rows for the per-row kernel (R*H/64 >= 256 workgroups) at
+    k = 2048, the most slots a row may select, with padded slots, a row with
+    none, a ragged tail of valid slots and 0xFF scale bytes; sampled rows
+    against the oracle."""
+    rng = np.random.default_rng(2048)
+    R, H, k, bs = 300, 64, 2048, 64
+    S, MB = 4, 48
+    NB = S * MB
+    kv, ks = _cache(rng, NB, bs, n_ff=9)
+    table = rng.permutation(NB).astype(np.int32).reshape(S, MB)
+    sel = rng.integers(0, MB * bs, (R, k)).astype(np.int32)
+    sel[rng.random((R, k)) < 0.05] = -1
+    sel[7] = -1                                   # a row with no valid slot
+    sel[11, 1500:] = -1                           # valid slots end inside a chunk
+    row_seq = rng.integers(0, S, R).astype(np.int32)
+    q = _bf16(rng.standard_normal((R, H, 128)) * 0.3)
+    sink = rng.standard_normal(H)
+    rows = np.unique(np.r_[0, 7, 11, R - 1, rng.choice(R, 12)])
+    print(f"[attn] rows kernel R={R} k={k}", flush=True)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    xk.xk_sparse_attention_mxfp4(dev(q.view(np.int16)).view(torch.bfloat16), dev(kv), dev(ks), dev(table),
+                                 dev(sel), dev(row_seq), dev(np.asarray(sink, np.float32)), 0.09, out=out)
+    torch.cuda.synchronize()
+    g = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(g)), "unwritten or non-finite output"
+    gathered = oracle.mxfp4_paged_gather(kv, ks, table, sel[rows], row_seq[rows], bs)
+    ref = oracle.sparse_attention(q[rows], gathered, sel[rows], sink, 0.09)
+    v = oracle.bf16_bits_to_f64(gathered)
+    for i, r in enumerate(rows):
+        ok = sel[r] >= 0
+        if not ok.any():
+            assert np.all(g[r] == 0), f"row {r}: no valid slot but nonzero output"
+            continue
+        err = np.abs(g[r] - ref[i]).max() / np.abs(v[i, ok]).max()
+        assert err <= TOL, f"row {r}: err {err:.3e}"
+
+
 @pytest.mark.parametrize("regime", ["flat", "peaked", "sink_dominant"])
 def test_attention_regimes(xk, regime):
     """Nearly uniform weights, one dominant key, and a sink that takes almost
